@@ -1,0 +1,323 @@
+"""CPU oracle for the SPRINT block step -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, fp64 NumPy.  Only the tests, the package's ``smoke()`` entry and
+the CPU-baseline leg of ``bench.py`` may import this module; the product path
+never does.  It shares no code with the HIP library.
+
+Source: "LLaDA2.0-Uni: Unifying Multimodal Understanding and Generation with
+Diffusion Large Language Model" (arXiv 2604.20796, HTML version), the SPRINT
+paragraphs:
+  * SPRINT introduction -- B blocks x T denoising steps; two components.
+  * "Sparse Prefix Retention" -- first step of a block is a full pass giving
+    logits and the full KV cache; composite score of the mean-normalised key
+    norm and the top-1 softmax confidence (alpha = 0.5); per-modality keep
+    ratios, top-floor(r*n) kept within each modality; the pruned cache is
+    built once per block and attended by every later step.
+  * "Non-uniform Token Unmasking" -- per-position confidence of the predicted
+    token; accept all masked positions above tau, at least ceil(m/(T-t)).
+  * "BDLM Loss" notation -- a block is predicted from the clean earlier blocks
+    and its own noisy block (the block's own keys are part of its context).
+
+Readings of points the page leaves open (each is also listed in the design
+notes): the score equation itself did not survive on the page, and is read as
+the linear blend alpha*I + (1-alpha)*c; a position's key is the concatenation
+of its KV heads; the mean runs over the sequence's prefix positions of both
+modalities; ties in the top-k go to the lower position; "within each modality"
+pools all runs of that modality in the sequence; GQA head h reads KV head
+floor(h*Hkv/Hq); scores are scaled by 1/sqrt(D); "exceeds tau" is strict;
+m is the current masked count and t the 0-based step.
+
+Parity status: every function below is pinned by the tests in
+``tests/test_oracle_pins.py`` (closed forms, invariants, brute force).  The
+one thing no pin can reach is the *reading* of the lost score equation
+(``composite_score``): its arithmetic is pinned, its fidelity to the page is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# Scoring (Sparse Prefix Retention)
+# --------------------------------------------------------------------------
+
+def key_norms(K) -> np.ndarray:
+    """Per prefix position, the L2 norm of its key over all KV heads and dims.
+
+    K: [total_L, Hkv, D].  Reading: the key k_i of position i is the
+    concatenation of its KV heads, so ||k_i||^2 = sum_h sum_d K[i,h,d]^2.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    flat = K.reshape(K.shape[0], -1)
+    return np.sqrt(np.einsum("ij,ij->i", flat, flat))
+
+
+def key_norm_importance(K, cu_len) -> np.ndarray:
+    """Mean-normalised key norm I_i = ||k_i|| / ((1/L) sum_j ||k_j||).
+
+    Sparse Prefix Retention, definition of the key-norm importance.  The mean
+    runs over the L prefix positions of each sequence (cu_len: [nseq+1]
+    offsets).  A sequence whose keys are all zero has no defined ratio; it
+    gets I_i = 1 (every position equally important).
+    """
+    n = key_norms(K)
+    out = np.empty_like(n)
+    cu = np.asarray(cu_len, dtype=np.int64)
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        L = b - a
+        if L == 0:
+            continue
+        mu = n[a:b].sum() / L
+        out[a:b] = n[a:b] / mu if mu > 0.0 else 1.0
+    return out
+
+
+def composite_score(ibar, conf, alpha: float = 0.5) -> np.ndarray:
+    """s_i = alpha * I_i + (1 - alpha) * c_i  (Sparse Prefix Retention).
+
+    The page names the two blended terms and alpha = 0.5 but its equation was
+    lost; the linear blend is the plain reading (at alpha = 0.5 the order of
+    the terms does not matter).
+    """
+    ibar = np.asarray(ibar, dtype=np.float64)
+    conf = np.asarray(conf, dtype=np.float64)
+    return alpha * ibar + (1.0 - alpha) * conf
+
+
+def keep_count(r: float, n: int) -> int:
+    """floor(r * n), clamped to [0, n]  (Sparse Prefix Retention, keep rule)."""
+    k = math.floor(float(r) * int(n))
+    return max(0, min(int(n), int(k)))
+
+
+def select_kept(score, modality, cu_len, keep) -> np.ndarray:
+    """Global row indices kept by per-modality top-k, ascending.
+
+    Sparse Prefix Retention: within each modality of a sequence the
+    top-floor(r*n) positions by s_i are kept.  keep: [nseq, 2] counts
+    (text, image).  Order is (s descending, position ascending), so an equal
+    score keeps the lower position.  Returned indices are rows of the packed
+    [total_L, ...] cache, ascending (sequence order, then position).
+    """
+    score = np.asarray(score, dtype=np.float64)
+    modality = np.asarray(modality)
+    cu = np.asarray(cu_len, dtype=np.int64)
+    keep = np.asarray(keep, dtype=np.int64).reshape(-1, 2)
+    kept: List[int] = []
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        chosen = []
+        for m in (0, 1):
+            pos = np.nonzero(modality[a:b] == m)[0] + a
+            k = max(0, min(int(keep[s, m]), len(pos)))
+            order = np.lexsort((pos, -score[pos]))      # primary: -s, then position
+            chosen.extend(pos[order[:k]].tolist())
+        kept.extend(sorted(chosen))
+    return np.asarray(kept, dtype=np.int64)
+
+
+def compact(K, V, kept_idx):
+    """Pruned cache K'[j] = K[kept[j]], V'[j] = V[kept[j]] (bit copies)."""
+    kept_idx = np.asarray(kept_idx, dtype=np.int64)
+    return np.asarray(K)[kept_idx], np.asarray(V)[kept_idx]
+
+
+# --------------------------------------------------------------------------
+# Block attention (the denoising step's attention over the prefix cache)
+# --------------------------------------------------------------------------
+
+def attention(Q, Kp, Vp, cu_kv, Kb=None, Vb=None, scale: Optional[float] = None):
+    """O = softmax(Q K^T * scale) V per (sequence, query head), fp64.
+
+    Q: [nseq, Lq, Hq, D]; Kp/Vp: [total_kv, Hkv, D] packed by cu_kv;
+    Kb/Vb: [nseq, Lq, Hkv, D] (the block's own keys, attended without a mask:
+    the block is predicted bidirectionally from the clean prefix and its own
+    noisy tokens) or None.  Query head h reads KV head floor(h*Hkv/Hq).
+    Keys are [prefix ; block]; a softmax over an empty key set is undefined
+    and not allowed.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    Kp = np.asarray(Kp, dtype=np.float64)
+    Vp = np.asarray(Vp, dtype=np.float64)
+    nseq, Lq, Hq, D = Q.shape
+    Hkv = Kp.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    cu = np.asarray(cu_kv, dtype=np.int64)
+    O = np.zeros_like(Q)
+    for b in range(nseq):
+        kb = Kp[cu[b]:cu[b + 1]]
+        vb = Vp[cu[b]:cu[b + 1]]
+        if Kb is not None:
+            kb = np.concatenate([kb, np.asarray(Kb[b], dtype=np.float64)], axis=0)
+            vb = np.concatenate([vb, np.asarray(Vb[b], dtype=np.float64)], axis=0)
+        if kb.shape[0] == 0:
+            raise ValueError("attention over an empty key set")
+        for h in range(Hq):
+            g = (h * Hkv) // Hq
+            logits = (Q[b, :, h, :] @ kb[:, g, :].T) * scale      # [Lq, n]
+            logits -= logits.max(axis=1, keepdims=True)
+            p = np.exp(logits)
+            p /= p.sum(axis=1, keepdims=True)
+            O[b, :, h, :] = p @ vb[:, g, :]
+    return O
+
+
+# --------------------------------------------------------------------------
+# LM-head confidence
+# --------------------------------------------------------------------------
+
+def lmhead_confidence(X, W):
+    """Top-1 softmax confidence of logits z = X W^T, fp64.
+
+    Sparse Prefix Retention defines c_i = max_v p(v | x_t); Non-uniform Token
+    Unmasking uses c_n = p(x0_hat^n | x_t), read with x0_hat = argmax (greedy),
+    which is the same number.  Returns (conf, argmax, lse): conf = 1 / sum_v
+    exp(z_v - z*), argmax = lowest index attaining z*, lse = z* + log sum.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    Z = X @ W.T
+    zmax = Z.max(axis=1)
+    amax = Z.argmax(axis=1)              # first (lowest) index of the maximum
+    S = np.exp(Z - zmax[:, None]).sum(axis=1)
+    return 1.0 / S, amax.astype(np.int64), zmax + np.log(S)
+
+
+def lmhead_top2_gap(X, W) -> np.ndarray:
+    """Gap between the largest and second-largest logit of each row (fp64)."""
+    Z = np.asarray(X, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T
+    part = np.partition(Z, Z.shape[1] - 2, axis=1)
+    return part[:, -1] - part[:, -2]
+
+
+# --------------------------------------------------------------------------
+# Non-uniform Token Unmasking
+# --------------------------------------------------------------------------
+
+def min_acceptances(m: int, steps_left: int) -> int:
+    """ceil(m / (T - t)) with steps_left = T - t; all of m when none are left."""
+    if m <= 0:
+        return 0
+    if steps_left <= 0:
+        return m
+    return min(m, -(-m // steps_left))
+
+
+def fixed_schedule_count(m0: int, T: int) -> int:
+    """The standard schedule's tokens per step, ceil(m0 / T)."""
+    return -(-m0 // T)
+
+
+def unmask_select(conf, argmax, masked, tokens, tau, steps_left: int):
+    """One confidence-adaptive unmasking step (Non-uniform Token Unmasking).
+
+    conf, argmax, masked, tokens: [nseq, Lq].  tau is compared with strict
+    '>' in the precision it is given in (pass the float32 value the kernel
+    uses).  For each sequence: m = #masked, q = min_acceptances(m, steps_left),
+    count = max(#{masked with conf > tau}, q); the first `count` masked
+    positions by (conf descending, position ascending) are accepted:
+    tokens <- argmax, masked <- 0.  Returns (masked, tokens, n_accepted) as
+    new arrays.
+    """
+    conf = np.asarray(conf, dtype=np.float64)
+    argmax = np.asarray(argmax)
+    masked = np.array(masked, dtype=np.uint8, copy=True)
+    tokens = np.array(tokens, dtype=np.int64, copy=True)
+    tau = float(tau)
+    nseq, Lq = conf.shape
+    n_acc = np.zeros(nseq, dtype=np.int64)
+    for s in range(nseq):
+        cand = np.nonzero(masked[s] == 1)[0]
+        m = len(cand)
+        if m == 0:
+            continue
+        n_hi = int(np.sum(conf[s, cand] > tau))
+        count = max(n_hi, min_acceptances(m, steps_left))
+        order = np.lexsort((cand, -conf[s, cand]))
+        acc = cand[order[:count]]
+        tokens[s, acc] = argmax[s, acc]
+        masked[s, acc] = 0
+        n_acc[s] = count
+    return masked, tokens, n_acc
+
+
+# --------------------------------------------------------------------------
+# One block: the pruning pass followed by pruned denoising steps
+# --------------------------------------------------------------------------
+
+@dataclass
+class BlockResult:
+    conf_prefix: np.ndarray
+    ibar: np.ndarray
+    score: np.ndarray
+    kept_idx: np.ndarray
+    cu_kept: np.ndarray
+    outputs: List[np.ndarray] = field(default_factory=list)    # O per step
+    confs: List[np.ndarray] = field(default_factory=list)      # block conf per step
+    argmaxes: List[np.ndarray] = field(default_factory=list)
+    masks: List[np.ndarray] = field(default_factory=list)      # mask after each step
+    tokens: List[np.ndarray] = field(default_factory=list)
+    n_accepted: List[np.ndarray] = field(default_factory=list)
+
+
+def run_block(Q, K, V, Kb, Vb, hidden, W, cu_len, modality, r_text, r_img,
+              tau, T: Optional[int], n_steps: int, alpha: float = 0.5,
+              pass_rows: Optional[np.ndarray] = None) -> BlockResult:
+    """The SPRINT block as one composition (Sparse Prefix Retention +
+    Non-uniform Token Unmasking).
+
+    t = 0 is the full pass: attention over the whole prefix, block confidence
+    and unmasking; the prefix confidences give the scores, which select and
+    compact the pruned cache.  Steps t = 1..n_steps attend to the pruned cache.
+    Q, Kb, Vb stay fixed across steps (the model that would refresh them is
+    not part of this path).  T = None means at least one acceptance per step.
+    `pass_rows` restricts the prefix LM head to those rows (others get conf 0)
+    for large sizes; None computes all of them.
+    """
+    nseq, Lq, Hq, D = np.asarray(Q).shape
+    cu = np.asarray(cu_len, dtype=np.int64)
+    if pass_rows is None:
+        conf_prefix, _, _ = lmhead_confidence(hidden, W)
+    else:
+        conf_prefix = np.zeros(cu[-1])
+        c, _, _ = lmhead_confidence(np.asarray(hidden)[pass_rows], W)
+        conf_prefix[pass_rows] = c
+    ibar = key_norm_importance(K, cu)
+    score = composite_score(ibar, conf_prefix, alpha)
+    keep = np.zeros((nseq, 2), dtype=np.int64)
+    for s in range(nseq):
+        seg = np.asarray(modality)[cu[s]:cu[s + 1]]
+        keep[s, 0] = keep_count(r_text, int(np.sum(seg == 0)))
+        keep[s, 1] = keep_count(r_img, int(np.sum(seg == 1)))
+    kept = select_kept(score, modality, cu, keep)
+    cu_kept = np.zeros(nseq + 1, dtype=np.int64)
+    cu_kept[1:] = np.cumsum(keep.sum(axis=1))
+    Kp, Vp = compact(K, V, kept)
+    res = BlockResult(conf_prefix, ibar, score, kept, cu_kept)
+    masked = np.ones((nseq, Lq), dtype=np.uint8)
+    tokens = np.full((nseq, Lq), -1, dtype=np.int64)
+    big = 1 << 30
+    for t in range(n_steps + 1):
+        if t == 0:
+            O = attention(Q, K, V, cu, Kb, Vb)
+        else:
+            O = attention(Q, Kp, Vp, cu_kept, Kb, Vb)
+        conf, amax, _ = lmhead_confidence(O.reshape(nseq * Lq, Hq * D), W)
+        conf = conf.reshape(nseq, Lq)
+        amax = amax.reshape(nseq, Lq)
+        steps_left = big if T is None else T - t
+        masked, tokens, nacc = unmask_select(conf, amax, masked, tokens, tau, steps_left)
+        res.outputs.append(O)
+        res.confs.append(conf)
+        res.argmaxes.append(amax)
+        res.masks.append(masked.copy())
+        res.tokens.append(tokens.copy())
+        res.n_accepted.append(nacc)
+    return res

@@ -1,0 +1,420 @@
+"""Pins for the CPU oracle: closed forms, invariants and brute force.
+
+Each test fixes the oracle to something other than its own formula, chosen so
+that a plausible slip (a dropped sqrt, a wrong axis, a per-head instead of a
+concatenated norm, a 1/D scale, a wrong GQA group, a highest-index tie break,
+a '>=' for '>') fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_prefix_kv_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------- key norm
+
+def test_keynorm_hand_example():
+    # position 0: head0 = (3,4) -> 5; position 1: head1 = (12,9) -> 15; mean 10
+    K = np.zeros((2, 2, 2))
+    K[0, 0] = [3, 4]
+    K[1, 1] = [12, 9]
+    ib = oracle.key_norm_importance(K, [0, 2])
+    np.testing.assert_allclose(ib, [0.5, 1.5], rtol=0, atol=1e-15)
+
+
+def test_keynorm_closed_form_unit_directions():
+    rng = np.random.default_rng(1)
+    L, Hkv, D = 50, 3, 8
+    U = rng.standard_normal((L, Hkv * D))
+    U /= np.linalg.norm(U, axis=1, keepdims=True)
+    f = rng.uniform(0.1, 5.0, size=L)
+    K = (U * f[:, None]).reshape(L, Hkv, D)
+    ib = oracle.key_norm_importance(K, [0, L])
+    np.testing.assert_allclose(ib, f / f.mean(), rtol=1e-12)
+
+
+def test_keynorm_sums_to_L_per_sequence_and_is_per_sequence():
+    rng = np.random.default_rng(2)
+    lens = [7, 13, 1, 30]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    K = rng.standard_normal((cu[-1], 2, 4))
+    K2 = K.copy()
+    K2[cu[1]:cu[2]] *= 10.0          # rescale one sequence only
+    a = oracle.key_norm_importance(K, cu)
+    b = oracle.key_norm_importance(K2, cu)
+    for s in range(len(lens)):
+        assert abs(a[cu[s]:cu[s + 1]].sum() - lens[s]) < 1e-12 * lens[s]
+    np.testing.assert_allclose(a, b, rtol=1e-12)
+
+
+def test_keynorm_rotation_and_scale_invariant():
+    rng = np.random.default_rng(3)
+    L, Hkv, D = 20, 2, 4
+    K = rng.standard_normal((L, Hkv, D))
+    Qm, _ = np.linalg.qr(rng.standard_normal((Hkv * D, Hkv * D)))
+    Kr = (K.reshape(L, -1) @ Qm).reshape(L, Hkv, D)
+    a = oracle.key_norm_importance(K, [0, L])
+    np.testing.assert_allclose(oracle.key_norm_importance(Kr, [0, L]), a, rtol=1e-12)
+    np.testing.assert_allclose(oracle.key_norm_importance(3.5 * K, [0, L]), a, rtol=1e-12)
+
+
+def test_keynorm_zero_keys_and_empty_sequence():
+    K = np.zeros((5, 2, 4))
+    np.testing.assert_array_equal(oracle.key_norm_importance(K, [0, 0, 5]), np.ones(5))
+
+
+# ------------------------------------------------------------------------ score
+
+def test_composite_score_hand_values():
+    s = oracle.composite_score([0.5, 1.5], [0.1, 0.3], 0.5)
+    np.testing.assert_allclose(s, [0.3, 0.9], atol=1e-15)
+    # alpha weights the key-norm term
+    s = oracle.composite_score([0.5], [0.1], 0.25)
+    np.testing.assert_allclose(s, [0.25 * 0.5 + 0.75 * 0.1], atol=1e-15)
+    assert _golden("sprint_settings.json")["alpha"] == 0.5
+
+
+# --------------------------------------------------------------------- keep rule
+
+def test_keep_counts_golden():
+    g = _golden("sprint_settings.json")
+    for row in g["keep_counts"]:
+        assert oracle.keep_count(row["r"], row["n"]) == row["k"], row
+    assert oracle.keep_count(1.5, 10) == 10 and oracle.keep_count(-0.5, 10) == 0
+
+
+def test_workload_total_kept_golden():
+    g = {r["workload"]: r["kept"] for r in _golden("sprint_settings.json")["total_kept"]}
+    for name, want in g.items():
+        wl = synth.WORKLOADS[name]
+        lay = synth.layout_from_runs(wl.segments)
+        got = sum(oracle.keep_count(wl.r_text, int(lay.n_text[s])) +
+                  oracle.keep_count(wl.r_img, int(lay.n_img[s])) for s in range(lay.nseq))
+        assert got == want, name
+
+
+# -------------------------------------------------------------------- selection
+
+def _dominance_ok(score, chosen, pool):
+    """Every chosen position ranks above every unchosen one of the pool."""
+    out = [j for j in pool if j not in chosen]
+    for i in chosen:
+        for j in out:
+            if not (score[i] > score[j] or (score[i] == score[j] and i < j)):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_select_matches_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 11))
+    score = synth.random_scores(n, seed, levels=int(rng.integers(0, 4)))
+    modality = rng.integers(0, 2, size=n).astype(np.uint8)
+    n_t = int(np.sum(modality == 0))
+    n_i = n - n_t
+    keep = [[int(rng.integers(0, n_t + 1)), int(rng.integers(0, n_i + 1))]]
+    got = set(oracle.select_kept(score, modality, [0, n], keep).tolist())
+    want = set()
+    for m in (0, 1):
+        pool = [i for i in range(n) if modality[i] == m]
+        k = keep[0][m]
+        sols = [set(c) for c in itertools.combinations(pool, k)
+                if _dominance_ok(score, set(c), pool)]
+        assert len(sols) == 1                  # the rule picks a unique set
+        want |= sols[0]
+    assert got == want
+
+
+def test_select_identity_zero_and_ties():
+    rng = np.random.default_rng(5)
+    lay = synth.layout_from_runs([((0, 5), (1, 7), (0, 3)), ((1, 4),)])
+    n = lay.total_L
+    score = rng.uniform(size=n)
+    full = [[int(lay.n_text[s]), int(lay.n_img[s])] for s in range(lay.nseq)]
+    np.testing.assert_array_equal(oracle.select_kept(score, lay.modality, lay.cu_len, full),
+                                  np.arange(n))
+    assert len(oracle.select_kept(score, lay.modality, lay.cu_len, [[0, 0], [0, 0]])) == 0
+    # all-equal scores keep the lowest positions of each modality
+    kept = oracle.select_kept(np.ones(n), lay.modality, lay.cu_len, [[2, 3], [0, 1]])
+    # seq 0: text at 0..4 and 12..14 -> 0,1 ; image at 5..11 -> 5,6,7 ; seq 1 image 15..18 -> 15
+    np.testing.assert_array_equal(kept, [0, 1, 5, 6, 7, 15])
+
+
+def test_select_pools_modality_runs():
+    # two image runs of 5; keep floor(0.8*10) = 8 pooled, not 4 + 4 per run
+    lay = synth.layout_from_runs([((1, 5), (0, 2), (1, 5))])
+    score = np.array([9, 8, 7, 6, 5, 0, 0, 4, 3, 2, 1, 0.5], dtype=float)
+    k = oracle.keep_count(0.8, 10)
+    kept = oracle.select_kept(score, lay.modality, lay.cu_len, [[2, k]])
+    np.testing.assert_array_equal(kept, [0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
+
+
+def test_compact_is_row_gather():
+    rng = np.random.default_rng(6)
+    K = rng.standard_normal((10, 2, 3))
+    V = rng.standard_normal((10, 2, 3))
+    Kp, Vp = oracle.compact(K, V, np.arange(10))
+    assert Kp.tobytes() == K.tobytes() and Vp.tobytes() == V.tobytes()
+    Kp, Vp = oracle.compact(K, V, [1, 4, 9])
+    assert np.array_equal(Kp[1], K[4]) and np.array_equal(Vp[2], V[9])
+
+
+# -------------------------------------------------------------------- attention
+
+def _rand_attn(rng, nseq=1, Lq=3, Hq=4, Hkv=2, D=4, L=5, block=True):
+    Q = rng.standard_normal((nseq, Lq, Hq, D))
+    K = rng.standard_normal((nseq * L, Hkv, D))
+    V = rng.standard_normal((nseq * L, Hkv, D))
+    cu = np.arange(nseq + 1) * L
+    Kb = rng.standard_normal((nseq, Lq, Hkv, D)) if block else None
+    Vb = rng.standard_normal((nseq, Lq, Hkv, D)) if block else None
+    return Q, K, V, cu, Kb, Vb
+
+
+def test_attention_single_key_returns_value():
+    rng = np.random.default_rng(7)
+    Q, K, V, cu, _, _ = _rand_attn(rng, L=1, block=False)
+    O = oracle.attention(Q, K, V, cu)
+    for h in range(4):
+        g = h * 2 // 4
+        for i in range(3):
+            np.testing.assert_allclose(O[0, i, h], V[0, g], rtol=1e-14)
+
+
+def test_attention_identical_keys_average_values():
+    rng = np.random.default_rng(8)
+    Q, K, V, cu, _, _ = _rand_attn(rng, L=6, block=False)
+    K[:] = K[0]
+    O = oracle.attention(Q, K, V, cu)
+    for h in range(4):
+        g = h * 2 // 4
+        np.testing.assert_allclose(O[0, :, h], np.broadcast_to(V[:, g].mean(0), (3, 4)),
+                                   rtol=1e-12, atol=1e-14)
+
+
+def test_attention_two_key_closed_form_scale():
+    # D = 4 so that 1/sqrt(D) = 0.5 differs from 1/D and from 1
+    q = np.array([1.0, 2.0, -1.0, 0.5])
+    k1 = np.array([0.5, 1.0, 0.0, 2.0])
+    k2 = np.array([-1.0, 0.0, 1.0, 0.0])
+    v1 = np.array([1.0, 0.0, 0.0, 3.0])
+    v2 = np.array([0.0, 1.0, 2.0, -1.0])
+    Q = q.reshape(1, 1, 1, 4)
+    K = np.stack([k1, k2]).reshape(2, 1, 4)
+    V = np.stack([v1, v2]).reshape(2, 1, 4)
+    delta = (q @ k1 - q @ k2) / 2.0            # 0.5 * (3.5 - (-2)) = 2.75
+    w1 = 1.0 / (1.0 + math.exp(-delta))
+    O = oracle.attention(Q, K, V, [0, 2])
+    np.testing.assert_allclose(O[0, 0, 0], w1 * v1 + (1 - w1) * v2, rtol=1e-14)
+
+
+def test_attention_gqa_groups_are_contiguous():
+    rng = np.random.default_rng(9)
+    Hq, Hkv = 8, 2
+    Q, K, V, cu, _, _ = _rand_attn(rng, Hq=Hq, Hkv=Hkv, L=5, block=False)
+    V[:, 0, :] = 1.0
+    V[:, 1, :] = -2.0
+    O = oracle.attention(Q, K, V, cu)
+    for h in range(Hq):
+        want = 1.0 if h < 4 else -2.0        # heads 0..3 -> KV 0, 4..7 -> KV 1
+        np.testing.assert_allclose(O[0, :, h], want, rtol=1e-13)
+
+
+def test_attention_block_keys_attended_and_prefix_optional():
+    rng = np.random.default_rng(10)
+    Q, K, V, cu, Kb, Vb = _rand_attn(rng, Hq=2, Hkv=1, L=3, Lq=2)
+    # prefix empty, one block key: every query returns that key's value
+    O = oracle.attention(Q[:, :1], np.zeros((0, 1, 4)), np.zeros((0, 1, 4)), [0, 0],
+                         Kb[:, :1], Vb[:, :1])
+    np.testing.assert_allclose(O[0, 0, 0], Vb[0, 0, 0], rtol=1e-14)
+    # with a prefix the block key still contributes: equals attention over the union
+    O2 = oracle.attention(Q, K, V, cu, Kb, Vb)
+    Ku = np.concatenate([K, Kb[0]], 0)
+    Vu = np.concatenate([V, Vb[0]], 0)
+    O3 = oracle.attention(Q, Ku, Vu, [0, 5])
+    np.testing.assert_allclose(O2, O3, rtol=1e-13)
+    with pytest.raises(ValueError):
+        oracle.attention(Q, np.zeros((0, 1, 4)), np.zeros((0, 1, 4)), [0, 0])
+
+
+def test_attention_convex_hull_permutation_and_stability():
+    rng = np.random.default_rng(11)
+    Q, K, V, cu, _, _ = _rand_attn(rng, L=40, block=False)
+    O = oracle.attention(Q, K, V, cu)
+    for h in range(4):
+        g = h * 2 // 4
+        assert np.all(O[0, :, h] <= V[:, g].max(0) + 1e-12)
+        assert np.all(O[0, :, h] >= V[:, g].min(0) - 1e-12)
+    perm = rng.permutation(40)
+    np.testing.assert_allclose(oracle.attention(Q, K[perm], V[perm], cu), O, rtol=1e-12, atol=1e-14)
+    # huge logits: softmax collapses onto the largest key without overflow
+    Q2 = np.zeros((1, 1, 1, 4)); Q2[0, 0, 0, 0] = 1e4
+    K2 = np.zeros((3, 1, 4)); K2[:, 0, 0] = [1.0, 3.0, 2.0]
+    V2 = np.arange(12, dtype=float).reshape(3, 1, 4)
+    O2 = oracle.attention(Q2, K2, V2, [0, 3])
+    np.testing.assert_allclose(O2[0, 0, 0], V2[1, 0], rtol=1e-14)
+
+
+# -------------------------------------------------------------------- LM head
+
+def test_lmhead_zero_weights_uniform():
+    X = np.random.default_rng(12).standard_normal((3, 8))
+    c, a, lse = oracle.lmhead_confidence(X, np.zeros((100, 8)))
+    np.testing.assert_allclose(c, 0.01, rtol=1e-14)
+    np.testing.assert_array_equal(a, 0)
+    np.testing.assert_allclose(lse, math.log(100), rtol=1e-14)
+
+
+def test_lmhead_hand_example():
+    # z = [0, ln 2, ln 3] -> p = [1, 2, 3] / 6
+    X = np.array([[1.0]])
+    W = np.array([[0.0], [math.log(2)], [math.log(3)]])
+    c, a, lse = oracle.lmhead_confidence(X, W)
+    np.testing.assert_allclose(c, [0.5], rtol=1e-14)
+    assert a[0] == 2
+    np.testing.assert_allclose(lse, [math.log(6)], rtol=1e-14)
+
+
+@pytest.mark.parametrize("gamma", [0.5, 4.0, 12.0, 40.0])
+def test_lmhead_planted_closed_form(gamma):
+    V, H, vstar = 1000, 16, 377
+    X = np.zeros((1, H)); X[0, 0] = 1.0
+    W = np.zeros((V, H)); W[vstar, 0] = gamma
+    c, a, lse = oracle.lmhead_confidence(X, W)
+    np.testing.assert_allclose(c, [1.0 / (1.0 + (V - 1) * math.exp(-gamma))], rtol=1e-13)
+    assert a[0] == vstar
+    np.testing.assert_allclose(lse, [gamma + math.log1p((V - 1) * math.exp(-gamma))], rtol=1e-13)
+
+
+def test_lmhead_tie_goes_to_lowest_index_and_bounds():
+    rng = np.random.default_rng(13)
+    W = rng.standard_normal((50, 6)) * 0.1
+    X = rng.standard_normal((4, 6))
+    W[7] = W[31] = 10 * X[0] / np.dot(X[0], X[0])   # equal maxima for row 0
+    c, a, _ = oracle.lmhead_confidence(X, W)
+    assert a[0] == 7
+    assert np.all(c >= 1.0 / 50 - 1e-15) and np.all(c <= 1.0)
+    c2, _, _ = oracle.lmhead_confidence(X * 1e3, W)   # stable at large logits
+    assert np.all(np.isfinite(c2))
+
+
+# -------------------------------------------------------------------- unmask
+
+def _brute_unmask(conf, masked, tau, steps_left):
+    cand = [i for i in range(len(conf)) if masked[i]]
+    m = len(cand)
+    if m == 0:
+        return set()
+    n_hi = sum(1 for i in cand if conf[i] > tau)
+    q = m if steps_left <= 0 else min(m, math.ceil(m / steps_left))
+    count = max(n_hi, q)
+    sols = [set(c) for c in itertools.combinations(cand, count)
+            if _dominance_ok(conf, set(c), cand)]
+    assert len(sols) == 1
+    return sols[0]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_unmask_matches_brute_force(seed):
+    rng = np.random.default_rng(200 + seed)
+    Lq = int(rng.integers(1, 11))
+    tau = float(np.float32(0.9))
+    conf, amax, masked, tokens = synth.random_unmask_state(2, Lq, 50, seed, tau,
+                                                           tie_levels=int(rng.integers(0, 5)))
+    steps_left = int(rng.integers(-1, 6))
+    m2, t2, n2 = oracle.unmask_select(conf, amax, masked, tokens, tau, steps_left)
+    for s in range(2):
+        acc = _brute_unmask(conf[s].astype(float), masked[s], tau, steps_left)
+        assert n2[s] == len(acc)
+        for i in range(Lq):
+            if i in acc:
+                assert m2[s, i] == 0 and t2[s, i] == amax[s, i]
+            else:
+                assert m2[s, i] == masked[s, i] and t2[s, i] == tokens[s, i]
+
+
+def test_unmask_threshold_is_strict_and_always_accepts_confident():
+    conf = np.array([[0.95, 0.96, 0.2, 0.97, 0.1]], dtype=np.float32)
+    masked = np.ones((1, 5), np.uint8)
+    tau = np.float32(0.95)
+    m2, _, n = oracle.unmask_select(conf, np.arange(5)[None], masked,
+                                    np.full((1, 5), -1), tau, 100)
+    np.testing.assert_array_equal(m2[0], [1, 0, 1, 0, 1])      # 0.95 is not > 0.95
+    assert n[0] == 2
+
+
+def test_unmask_schedules_golden():
+    g = _golden("unmask_schedules.json")
+    for case in g["cases"]:
+        m0, T = case["m0"], case["T"]
+        conf = np.linspace(0.1, 0.2, m0, dtype=np.float32)[None]
+        masked = np.ones((1, m0), np.uint8)
+        tokens = np.full((1, m0), -1)
+        got = []
+        for t in range(T):
+            masked, tokens, n = oracle.unmask_select(conf, np.arange(m0)[None], masked,
+                                                     tokens, 2.0, T - t)
+            got.append(int(n[0]))
+        assert got == case["accepted"], case
+        assert masked.sum() == 0                      # terminates within T steps
+    for f in g["fixed_schedule"]:
+        assert oracle.fixed_schedule_count(f["m0"], f["T"]) == f["per_step"]
+
+
+def test_unmask_at_least_one_per_step():
+    conf = np.full((1, 6), 0.5, dtype=np.float32)
+    masked = np.ones((1, 6), np.uint8)
+    tokens = np.full((1, 6), -1)
+    counts = []
+    for _ in range(6):
+        masked, tokens, n = oracle.unmask_select(conf, np.arange(6)[None], masked, tokens,
+                                                 0.9, 1 << 30)
+        counts.append(int(n[0]))
+    assert counts == [1] * 6
+    np.testing.assert_array_equal(tokens[0], np.arange(6))   # ties resolve lowest first
+
+
+# -------------------------------------------------------------------- block
+
+def _tiny_inputs(seed=0, L=(24, 8)):
+    wl = synth.Workload("t", "f32", Hq=4, Hkv=2, D=8, Lq=6, vocab=64,
+                        segments=(((0, L[0]), (1, L[1])),), tau=0.9, T=4)
+    return wl, synth.make_inputs(wl, seed)
+
+
+def test_block_full_retention_is_identity():
+    wl, x = _tiny_inputs()
+    lay = x.layout
+    r = oracle.run_block(x.Q, x.K, x.V, x.Kb, x.Vb, x.hidden, x.W, lay.cu_len, lay.modality,
+                         1.0, 1.0, 2.0, 4, 3)
+    np.testing.assert_array_equal(r.kept_idx, np.arange(lay.total_L))
+    for O in r.outputs[1:]:
+        assert np.array_equal(O, r.outputs[0])
+    assert [int(n[0]) for n in r.n_accepted] == [2, 2, 1, 1]
+    assert r.masks[-1].sum() == 0
+
+
+def test_block_pruned_counts_and_validity():
+    wl, x = _tiny_inputs(seed=3)
+    lay = x.layout
+    r = oracle.run_block(x.Q, x.K, x.V, x.Kb, x.Vb, x.hidden, x.W, lay.cu_len, lay.modality,
+                         1.0, 0.5, 0.9, 4, 3)
+    assert len(r.kept_idx) == 24 + 4
+    img = [i for i in range(32) if lay.modality[i] == 1]
+    assert _dominance_ok(r.score, set(r.kept_idx.tolist()) & set(img), img)
+    assert abs(r.ibar.sum() - 32) < 1e-12
+    assert r.masks[-1].sum() == 0
