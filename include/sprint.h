@@ -1,0 +1,176 @@
+/*
+ * sprint.h -- C ABI of libsprint.so: the SPRINT block-wise masked-diffusion
+ * denoising step as HIP kernels for MI355X (gfx950).
+ *
+ * Method: "LLaDA2.0-Uni: Unifying Multimodal Understanding and Generation with
+ * Diffusion Large Language Model" (arXiv 2604.20796), the SPRINT paragraphs
+ * ("Sparse Prefix Retention", "Non-uniform Token Unmasking") and the block
+ * notation of its "BDLM Loss" paragraph.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are DEVICE pointers unless a comment says "host".
+ *  - The caller owns all memory; the library never allocates or frees.
+ *    Scratch memory is a caller buffer `ws` of at least the bytes returned by
+ *    the matching *_ws() query.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *    asynchronous on it; no call synchronises the device.
+ *  - Arguments are validated on the host before any HIP call; a failure
+ *    returns its SPRINT_E* code and writes nothing.  A kernel launch failure
+ *    returns SPRINT_EHIP.  Device faults surface at the caller's next sync.
+ *  - Tensors are dense, row-major and position-major.  Large operands (K, V,
+ *    Q, O, W, hidden, K_out, V_out, ws) must be 16-byte aligned; 4-byte
+ *    arrays 4-byte aligned.
+ *  - dtype: SPRINT_F32 (float) or SPRINT_BF16 (bfloat16 bit patterns);
+ *    reductions and softmax statistics are computed in fp32.
+ *  - Results are deterministic: no floating-point atomics are used, so the
+ *    same inputs give bitwise-identical outputs.
+ *  - Non-finite inputs violate the preconditions; results are then unspecified.
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef SPRINT_H
+#define SPRINT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SPRINT_OK = 0,
+  SPRINT_EINVAL = 1,       /* bad pointer, size or shape */
+  SPRINT_EUNSUPPORTED = 2, /* valid but not implemented (e.g. head_dim not 64/128) */
+  SPRINT_EWORKSPACE = 3,   /* ws smaller than the *_ws() query */
+  SPRINT_EHIP = 4          /* a HIP launch failed */
+};
+
+enum { SPRINT_F32 = 0, SPRINT_BF16 = 1 };
+
+/* Human-readable name of a status code (static string). */
+const char* sprint_strerror(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int sprint_version(void);
+
+/* ------------------------------------------------------------------------
+ * Keep counts (host only).  Sparse Prefix Retention keeps floor(r*n) positions
+ * of a modality that has n prefix positions.  Evaluated as IEEE fp64
+ * floor(r*n), clamped to [0, n]; no minimum of one.
+ * ------------------------------------------------------------------------ */
+int64_t sprint_keep_count(double r, int64_t n);
+
+/* Per-sequence keep counts and output offsets, all HOST arrays:
+ *   n_text, n_img [nseq]   prefix positions of each modality per sequence
+ *   keep   [nseq*2]        out: (text, image) counts = sprint_keep_count(r_m, n_m)
+ *   cu_kept[nseq+1]        out: exclusive prefix sum of keep per sequence
+ *   total_kept             out: cu_kept[nseq]
+ * Returns SPRINT_EINVAL on NULL pointers, nseq < 1 or negative counts. */
+int sprint_plan_keep(const int64_t* n_text, const int64_t* n_img, int32_t nseq,
+                     double r_text, double r_img, int32_t* keep, int32_t* cu_kept,
+                     int64_t* total_kept);
+
+/* ------------------------------------------------------------------------
+ * LM-head confidence.  Sparse Prefix Retention scores position i with its
+ * top-1 softmax probability c_i = max_v p(v | x_t); Non-uniform Token
+ * Unmasking uses c_n = p(x0_hat | x_t) for the greedy prediction, the same
+ * number.  For each row x of `hidden`:
+ *     z = W x  (z_v = sum_h W[v,h] x[h], fp32 accumulation),
+ *     argmax = lowest v with z_v = max z,
+ *     conf = 1 / sum_v exp(z_v - max z),   lse = max z + log(sum_v exp(z_v - max z)).
+ * The [M, V] logits never reach memory: each vocabulary tile keeps a running
+ * (max, sum of exp, argmax) that a merge kernel combines.
+ *   hidden [M, H] dtype;  W [V, H] dtype (nn.Linear layout)
+ *   conf [M] float out;  argmax [M] int32 out;  lse [M] float out or NULL
+ * Requires M >= 1, V >= 1, H a multiple of 64 (<= 65536).
+ * ------------------------------------------------------------------------ */
+size_t lmhead_confidence_ws(int64_t M, int32_t H, int32_t V, int32_t dtype);
+int lmhead_confidence(const void* hidden, int64_t M, int32_t H, const void* W, int32_t V,
+                      int32_t dtype, float* conf, int32_t* argmax, float* lse,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Composite prefix score (Sparse Prefix Retention).
+ *   n_i   = ||K[i,:,:]||_2  over all KV heads and head dims (the position's key
+ *           is the concatenation of its KV heads),
+ *   I_i   = n_i / ((1/L) sum_{j in seq} n_j)   (1 when the sequence's keys are all 0),
+ *   s_i   = alpha * I_i + (1 - alpha) * c_i.
+ * The page's score equation is missing; the linear blend is the reading used.
+ *   K     [total_L, Hkv, D] dtype, sequences packed by cu_len [nseq+1] (int32,
+ *         cu_len[0] = 0, non-decreasing, cu_len[nseq] = total_L)
+ *   conf  [total_L] float   prefix confidences (lmhead_confidence over the prefix)
+ *   ibar  [total_L] float out;  score [total_L] float out
+ * ------------------------------------------------------------------------ */
+size_t sprint_score_ws(int64_t total_L, int32_t nseq);
+int sprint_score(const void* K, const float* conf, const int32_t* cu_len, int32_t nseq,
+                 int64_t total_L, int32_t Hkv, int32_t D, int32_t dtype, float alpha,
+                 float* ibar, float* score, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Modality-aware pruning and compaction of the prefix KV cache (Sparse Prefix
+ * Retention).  For each sequence s and modality m (0 text, 1 image) the
+ * min(keep[2s+m], n_{s,m}) positions with the largest score are kept; equal
+ * scores keep the lower position; all runs of one modality in a sequence are
+ * pooled.  The kept rows, in ascending position order, are copied into a
+ * contiguous pruned cache:
+ *   kept_idx[j] = global row of K kept at output row j (ascending),
+ *   K_out[j] = K[kept_idx[j]],  V_out[j] = V[kept_idx[j]]  (bit copies).
+ *   score    [total_L] float;  modality [total_L] uint8 (0 text, 1 image)
+ *   keep     [nseq*2] int32 device (from sprint_plan_keep)
+ *   cu_kept  [nseq+1] int32 device (from sprint_plan_keep); total_kept = cu_kept[nseq]
+ *   K, V     [total_L, Hkv, D] dtype;  K_out, V_out [total_kept, Hkv, D] dtype out
+ *   kept_idx [total_kept] int32 out
+ * Precondition: cu_kept must be the prefix sum of min(keep, n) per sequence;
+ * the kernels never write outside [cu_kept[s], cu_kept[s+1]) or total_kept.
+ * ------------------------------------------------------------------------ */
+size_t sprint_prune_kv_ws(int64_t total_L, int32_t nseq);
+int sprint_prune_kv(const float* score, const uint8_t* modality, const int32_t* cu_len,
+                    const int32_t* keep, const int32_t* cu_kept, int32_t nseq, int64_t total_L,
+                    int64_t total_kept, const void* K, const void* V, int32_t Hkv, int32_t D,
+                    int32_t dtype, void* K_out, void* V_out, int32_t* kept_idx, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Block attention of a denoising step: the block's queries attend, without a
+ * mask, to [prefix cache ; the block's own keys] (the block is predicted from
+ * the clean prefix and its own noisy tokens).  With GQA, query head h reads
+ * KV head floor(h*Hkv/Hq).  O = softmax(Q K^T * scale) V per (sequence, head).
+ *   Q      [nseq, Lq, Hq, D] dtype
+ *   Kp, Vp [total_kv, Hkv, D] dtype, sequences packed by cu_kv [nseq+1]
+ *          (full cache, or the pruned cache of sprint_prune_kv)
+ *   max_kv host upper bound on any sequence's cache length (sizes the KV split)
+ *   Kb, Vb [nseq, Lq, Hkv, D] dtype, or both NULL for prefix-only attention
+ *   scale  usually 1/sqrt(D)
+ *   O      [nseq, Lq, Hq, D] dtype out (bf16 rounded to nearest even)
+ * Supports D in {64, 128}, Hq % Hkv == 0, (Hq/Hkv)*Lq <= 256, Lq <= 64.
+ * Every (sequence) must have at least one key (cache length + block >= 1).
+ * ------------------------------------------------------------------------ */
+size_t block_attend_ws(int32_t nseq, int32_t Lq, int32_t Hq, int32_t Hkv, int32_t D,
+                       int32_t max_kv, int32_t has_block);
+int block_attend(const void* Q, int32_t nseq, int32_t Lq, int32_t Hq, const void* Kp,
+                 const void* Vp, const int32_t* cu_kv, int64_t total_kv, int32_t max_kv,
+                 const void* Kb, const void* Vb, int32_t Hkv, int32_t D, float scale,
+                 int32_t dtype, void* O, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Confidence-adaptive unmasking, one step (Non-uniform Token Unmasking).
+ * For each sequence: m = number of masked positions; q = min(m, ceil(m /
+ * steps_left)) where steps_left = T - t (steps_left <= 0 accepts all m);
+ * count = max(#{masked i : conf[i] > tau}, q).  The `count` masked positions
+ * first in (conf descending, position ascending) order are accepted:
+ * tokens[i] = argmax[i], masked[i] = 0.  With tau > 1 only the minimum acts.
+ * A huge steps_left gives "at least one per step".
+ *   conf [nseq, Lq] float;  argmax [nseq, Lq] int32
+ *   masked [nseq, Lq] uint8 in/out (1 = masked);  tokens [nseq, Lq] int32 in/out
+ *   n_accepted [nseq] int32 out
+ * Requires 1 <= Lq <= 64.
+ * ------------------------------------------------------------------------ */
+int unmask_select(const float* conf, const int32_t* argmax, int32_t nseq, int32_t Lq, float tau,
+                  int32_t steps_left, uint8_t* masked, int32_t* tokens, int32_t* n_accepted,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPRINT_H */

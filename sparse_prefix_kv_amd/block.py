@@ -1,0 +1,155 @@
+"""One SPRINT block on the GPU: the pruning pass plus the pruned denoising steps.
+
+The driver only sequences calls into libsprint.so over device buffers that it
+allocates once (so a timed loop allocates nothing).  The order follows the
+SPRINT paragraphs of LLaDA2.0-Uni: the block's first step is the full pass
+(attention over the whole prefix, block confidences and unmasking) whose
+prefix confidences, with the key norms, score the prefix; the per-modality
+top-k is compacted into the pruned cache; every later step attends to that
+cache and unmasks by confidence.  Q and the block's own K/V stay fixed across
+steps because the model that would refresh them is not part of this path.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import sprint, synth
+
+BIG_STEPS = 1 << 30   # steps_left for "at least one acceptance per step"
+
+
+def _to_dev(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    if dtype == "bf16":
+        bits = synth.bf16_bits(a)
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+class SprintBlock:
+    """Device state for one block of one workload."""
+
+    def __init__(self, x: synth.Inputs, device="cuda", r_text: Optional[float] = None,
+                 r_img: Optional[float] = None, tau: Optional[float] = None,
+                 T: Optional[int] = "wl", alpha: Optional[float] = None):
+        wl = x.wl
+        lay = x.layout
+        self.wl, self.layout = wl, lay
+        self.r_text = wl.r_text if r_text is None else r_text
+        self.r_img = wl.r_img if r_img is None else r_img
+        self.tau = wl.tau if tau is None else tau
+        self.T = wl.T if T == "wl" else T
+        self.alpha = wl.alpha if alpha is None else alpha
+        dev = torch.device(device)
+        self.device = dev
+        dt = wl.dtype
+        self.nseq, self.Lq, self.Hq, self.Hkv, self.D = lay.nseq, wl.Lq, wl.Hq, wl.Hkv, wl.D
+        self.total_L = lay.total_L
+        self.Q = _to_dev(x.Q, dt, dev)
+        self.K = _to_dev(x.K, dt, dev)
+        self.V = _to_dev(x.V, dt, dev)
+        self.Kb = _to_dev(x.Kb, dt, dev)
+        self.Vb = _to_dev(x.Vb, dt, dev)
+        self.hidden = _to_dev(x.hidden, dt, dev) if x.hidden is not None else None
+        self.W = _to_dev(x.W, dt, dev)
+        self.cu_len = torch.from_numpy(lay.cu_len.astype(np.int32)).to(dev)
+        self.modality = torch.from_numpy(lay.modality).to(dev)
+        self.max_len = int(lay.lens.max())
+        keep, cu_kept, total_kept = sprint.sprint_plan_keep(lay.n_text, lay.n_img, self.r_text,
+                                                            self.r_img)
+        self.keep_host, self.cu_kept_host, self.total_kept = keep, cu_kept, total_kept
+        self.keep = torch.tensor(keep, dtype=torch.int32, device=dev)
+        self.cu_kept = torch.tensor(cu_kept, dtype=torch.int32, device=dev)
+        self.max_kept = int(np.max(np.diff(cu_kept)))
+        tl, tk = self.total_L, max(total_kept, 1)
+        f32, i32 = torch.float32, torch.int32
+        self.conf_prefix = torch.empty(tl, dtype=f32, device=dev)
+        self.argmax_prefix = torch.empty(tl, dtype=i32, device=dev)
+        self.ibar = torch.empty(tl, dtype=f32, device=dev)
+        self.score = torch.empty(tl, dtype=f32, device=dev)
+        self.K_pr = torch.empty((tk, self.Hkv, self.D), dtype=self.K.dtype, device=dev)[:total_kept]
+        self.V_pr = torch.empty((tk, self.Hkv, self.D), dtype=self.K.dtype, device=dev)[:total_kept]
+        self.kept_idx = torch.empty(tk, dtype=i32, device=dev)[:total_kept]
+        self.O = torch.empty_like(self.Q)
+        M = self.nseq * self.Lq
+        self.conf_blk = torch.empty(M, dtype=f32, device=dev)
+        self.argmax_blk = torch.empty(M, dtype=i32, device=dev)
+        self.masked = torch.ones((self.nseq, self.Lq), dtype=torch.uint8, device=dev)
+        self.tokens = torch.full((self.nseq, self.Lq), -1, dtype=i32, device=dev)
+        self.n_acc = torch.empty(self.nseq, dtype=i32, device=dev)
+        dti = sprint.BF16 if dt == "bf16" else sprint.F32
+        H, Vv = wl.H, wl.vocab
+        u8 = torch.uint8
+
+        def ws(n):
+            return torch.empty(max(int(n), 256), dtype=u8, device=dev)
+        self.ws_lm_prefix = ws(sprint.lmhead_confidence_ws(tl, H, Vv, dti)) if tl else None
+        self.ws_lm_blk = ws(sprint.lmhead_confidence_ws(M, H, Vv, dti))
+        self.ws_score = ws(sprint.sprint_score_ws(tl, self.nseq))
+        self.ws_prune = ws(sprint.sprint_prune_kv_ws(tl, self.nseq))
+        self.ws_att_full = ws(sprint.block_attend_ws(self.nseq, self.Lq, self.Hq, self.Hkv, self.D,
+                                                     self.max_len, True))
+        self.ws_att_pr = ws(sprint.block_attend_ws(self.nseq, self.Lq, self.Hq, self.Hkv, self.D,
+                                                   self.max_kept, True))
+
+    # ------------------------------------------------------------------ pieces
+    def steps_left(self, t: int) -> int:
+        return BIG_STEPS if self.T is None else self.T - t
+
+    def reset(self):
+        self.masked.fill_(1)
+        self.tokens.fill_(-1)
+
+    def prefix_confidence(self):
+        sprint.lmhead_confidence(self.hidden, self.W, conf=self.conf_prefix,
+                                 argmax=self.argmax_prefix, ws=self.ws_lm_prefix)
+
+    def score_and_prune(self):
+        sprint.sprint_score(self.K, self.conf_prefix, self.cu_len, self.alpha, ibar=self.ibar,
+                            score=self.score, ws=self.ws_score)
+        sprint.sprint_prune_kv(self.score, self.modality, self.cu_len, self.keep, self.cu_kept,
+                               self.total_kept, self.K, self.V, K_out=self.K_pr, V_out=self.V_pr,
+                               kept_idx=self.kept_idx, ws=self.ws_prune)
+
+    def attend(self, pruned: bool):
+        if pruned:
+            sprint.block_attend(self.Q, self.K_pr, self.V_pr, self.cu_kept, self.max_kept,
+                                self.Kb, self.Vb, O=self.O, ws=self.ws_att_pr)
+        else:
+            sprint.block_attend(self.Q, self.K, self.V, self.cu_len, self.max_len, self.Kb,
+                                self.Vb, O=self.O, ws=self.ws_att_full)
+
+    def confidence_and_unmask(self, t: int):
+        M = self.nseq * self.Lq
+        sprint.lmhead_confidence(self.O.view(M, self.Hq * self.D), self.W, conf=self.conf_blk,
+                                 argmax=self.argmax_blk, ws=self.ws_lm_blk)
+        sprint.unmask_select(self.conf_blk.view(self.nseq, self.Lq),
+                             self.argmax_blk.view(self.nseq, self.Lq), self.masked, self.tokens,
+                             self.tau, self.steps_left(t), n_accepted=self.n_acc)
+
+    # ------------------------------------------------------------------ block
+    def pruning_pass(self):
+        """t = 0: full pass over the prefix, scoring and pruning, first unmask."""
+        self.prefix_confidence()
+        self.score_and_prune()
+        self.attend(pruned=False)
+        self.confidence_and_unmask(0)
+
+    def pruned_step(self, t: int):
+        self.attend(pruned=True)
+        self.confidence_and_unmask(t)
+
+    def run_block(self, n_steps: int):
+        self.reset()
+        self.pruning_pass()
+        for t in range(1, n_steps + 1):
+            self.pruned_step(t)
+
+    def run_full_block(self, n_steps: int):
+        """Baseline without SPRINT pruning: every step attends to the full prefix."""
+        self.reset()
+        for t in range(0, n_steps + 1):
+            self.attend(pruned=False)
+            self.confidence_and_unmask(t)

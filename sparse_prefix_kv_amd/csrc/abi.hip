@@ -1,0 +1,191 @@
+// C ABI of libsprint.so (declared in include/sprint.h): host-side argument
+// validation, workspace queries and dispatch to the kernel launchers.
+// Every check runs before the first HIP call, so a rejected call touches no
+// device state.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/sprint.h"
+#include "sprint_internal.hpp"
+
+using namespace sprint;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool dev16(const void* p) { return p != nullptr && aligned(p, 16); }
+bool dev4(const void* p) { return p != nullptr && aligned(p, 4); }
+bool dtype_ok(int32_t dt) { return dt == SPRINT_F32 || dt == SPRINT_BF16; }
+bool head_dim_ok(int32_t D) { return D == 64 || D == 128; }
+int status_of(hipError_t e) { return e == hipSuccess ? SPRINT_OK : SPRINT_EHIP; }
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return SPRINT_OK;
+  if (ws_bytes < need) return SPRINT_EWORKSPACE;
+  if (!dev16(ws)) return SPRINT_EINVAL;
+  return SPRINT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sprint_strerror(int status) {
+  switch (status) {
+    case SPRINT_OK: return "ok";
+    case SPRINT_EINVAL: return "invalid argument";
+    case SPRINT_EUNSUPPORTED: return "unsupported shape or dtype";
+    case SPRINT_EWORKSPACE: return "workspace too small";
+    case SPRINT_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int sprint_version(void) { return 100; }
+
+int64_t sprint_keep_count(double r, int64_t n) {
+  if (n <= 0 || !(r == r)) return 0;
+  const double k = floor(r * static_cast<double>(n));
+  if (k <= 0.0) return 0;
+  if (k >= static_cast<double>(n)) return n;
+  return static_cast<int64_t>(k);
+}
+
+int sprint_plan_keep(const int64_t* n_text, const int64_t* n_img, int32_t nseq, double r_text,
+                     double r_img, int32_t* keep, int32_t* cu_kept, int64_t* total_kept) {
+  if (!n_text || !n_img || !keep || !cu_kept || !total_kept || nseq < 1) return SPRINT_EINVAL;
+  int64_t acc = 0;
+  for (int32_t s = 0; s < nseq; ++s) {
+    if (n_text[s] < 0 || n_img[s] < 0) return SPRINT_EINVAL;
+    if (n_text[s] + n_img[s] > INT32_MAX) return SPRINT_EINVAL;
+  }
+  cu_kept[0] = 0;
+  for (int32_t s = 0; s < nseq; ++s) {
+    const int64_t kt = sprint_keep_count(r_text, n_text[s]);
+    const int64_t ki = sprint_keep_count(r_img, n_img[s]);
+    keep[2 * s] = static_cast<int32_t>(kt);
+    keep[2 * s + 1] = static_cast<int32_t>(ki);
+    acc += kt + ki;
+    if (acc > INT32_MAX) return SPRINT_EINVAL;
+    cu_kept[s + 1] = static_cast<int32_t>(acc);
+  }
+  *total_kept = acc;
+  return SPRINT_OK;
+}
+
+// ---------------------------------------------------------------- LM head
+size_t lmhead_confidence_ws(int64_t M, int32_t H, int32_t V, int32_t dtype) {
+  if (M < 1 || V < 1) return 0;
+  return lmhead_ws_bytes(M, H, V, dtype);
+}
+
+int lmhead_confidence(const void* hidden, int64_t M, int32_t H, const void* W, int32_t V,
+                      int32_t dtype, float* conf, int32_t* argmax, float* lse, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return SPRINT_EINVAL;
+  if (M < 1 || V < 1 || H < 1 || M > INT32_MAX) return SPRINT_EINVAL;
+  if (!dev16(hidden) || !dev16(W) || !dev4(conf) || !dev4(argmax)) return SPRINT_EINVAL;
+  if (lse != nullptr && !aligned(lse, 4)) return SPRINT_EINVAL;
+  if (H % 64 != 0 || H > 65536) return SPRINT_EUNSUPPORTED;
+  const int st = check_ws(ws, ws_bytes, lmhead_ws_bytes(M, H, V, dtype));
+  if (st != SPRINT_OK) return st;
+  return status_of(launch_lmhead(hidden, M, H, W, V, dtype, conf, argmax, lse, ws,
+                                 as_stream(stream)));
+}
+
+// ---------------------------------------------------------------- score
+size_t sprint_score_ws(int64_t total_L, int32_t nseq) {
+  if (total_L < 0 || nseq < 1) return 0;
+  return score_ws_bytes(total_L, nseq);
+}
+
+int sprint_score(const void* K, const float* conf, const int32_t* cu_len, int32_t nseq,
+                 int64_t total_L, int32_t Hkv, int32_t D, int32_t dtype, float alpha, float* ibar,
+                 float* score, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || nseq < 1 || total_L < 0 || total_L > INT32_MAX || Hkv < 1)
+    return SPRINT_EINVAL;
+  if (!dev4(cu_len) || !isfinite(alpha)) return SPRINT_EINVAL;
+  if (!head_dim_ok(D)) return SPRINT_EUNSUPPORTED;
+  if (total_L > 0 && (!dev16(K) || !dev4(conf) || !dev4(ibar) || !dev4(score)))
+    return SPRINT_EINVAL;
+  const int st = check_ws(ws, ws_bytes, score_ws_bytes(total_L, nseq));
+  if (st != SPRINT_OK) return st;
+  return status_of(launch_score(K, conf, cu_len, nseq, total_L, Hkv, D, dtype, alpha, ibar, score,
+                                ws, as_stream(stream)));
+}
+
+// ---------------------------------------------------------------- prune
+size_t sprint_prune_kv_ws(int64_t total_L, int32_t nseq) {
+  if (total_L < 0 || nseq < 1) return 0;
+  return prune_ws_bytes(total_L, nseq);
+}
+
+int sprint_prune_kv(const float* score, const uint8_t* modality, const int32_t* cu_len,
+                    const int32_t* keep, const int32_t* cu_kept, int32_t nseq, int64_t total_L,
+                    int64_t total_kept, const void* K, const void* V, int32_t Hkv, int32_t D,
+                    int32_t dtype, void* K_out, void* V_out, int32_t* kept_idx, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || nseq < 1 || total_L < 0 || total_L > INT32_MAX || Hkv < 1)
+    return SPRINT_EINVAL;
+  if (total_kept < 0 || total_kept > total_L) return SPRINT_EINVAL;
+  if (!dev4(cu_len) || !dev4(keep) || !dev4(cu_kept)) return SPRINT_EINVAL;
+  if (!head_dim_ok(D)) return SPRINT_EUNSUPPORTED;
+  if (total_L > 0 && (!dev4(score) || modality == nullptr || !dev16(K) || !dev16(V)))
+    return SPRINT_EINVAL;
+  if (total_kept > 0 && (!dev16(K_out) || !dev16(V_out) || !dev4(kept_idx))) return SPRINT_EINVAL;
+  const int st = check_ws(ws, ws_bytes, prune_ws_bytes(total_L, nseq));
+  if (st != SPRINT_OK) return st;
+  return status_of(launch_prune(score, modality, cu_len, keep, cu_kept, nseq, total_L, total_kept,
+                                K, V, Hkv, D, dtype, K_out, V_out, kept_idx, ws,
+                                as_stream(stream)));
+}
+
+// ---------------------------------------------------------------- attention
+static int attend_shape_status(int32_t nseq, int32_t Lq, int32_t Hq, int32_t Hkv, int32_t D,
+                               int32_t max_kv) {
+  if (nseq < 1 || Lq < 1 || Hq < 1 || Hkv < 1 || max_kv < 0) return SPRINT_EINVAL;
+  if (Hq % Hkv != 0) return SPRINT_EINVAL;
+  if (!head_dim_ok(D) || Lq > 64 || (Hq / Hkv) * Lq > 256) return SPRINT_EUNSUPPORTED;
+  return SPRINT_OK;
+}
+
+size_t block_attend_ws(int32_t nseq, int32_t Lq, int32_t Hq, int32_t Hkv, int32_t D,
+                       int32_t max_kv, int32_t has_block) {
+  if (attend_shape_status(nseq, Lq, Hq, Hkv, D, max_kv) != SPRINT_OK) return 0;
+  return attend_plan(nseq, Lq, Hq, Hkv, D, max_kv, has_block, SPRINT_BF16).ws_bytes;
+}
+
+int block_attend(const void* Q, int32_t nseq, int32_t Lq, int32_t Hq, const void* Kp,
+                 const void* Vp, const int32_t* cu_kv, int64_t total_kv, int32_t max_kv,
+                 const void* Kb, const void* Vb, int32_t Hkv, int32_t D, float scale,
+                 int32_t dtype, void* O, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return SPRINT_EINVAL;
+  const int ss = attend_shape_status(nseq, Lq, Hq, Hkv, D, max_kv);
+  if (ss != SPRINT_OK) return ss;
+  if (total_kv < 0 || total_kv > INT32_MAX || !isfinite(scale)) return SPRINT_EINVAL;
+  if (!dev16(Q) || !dev16(O) || !dev4(cu_kv)) return SPRINT_EINVAL;
+  if ((Kb == nullptr) != (Vb == nullptr)) return SPRINT_EINVAL;
+  if (Kb != nullptr && (!dev16(Kb) || !dev16(Vb))) return SPRINT_EINVAL;
+  if (Kb == nullptr && max_kv < 1) return SPRINT_EINVAL;  // no keys at all
+  if (total_kv > 0 && (!dev16(Kp) || !dev16(Vp))) return SPRINT_EINVAL;
+  const AttnPlan plan = attend_plan(nseq, Lq, Hq, Hkv, D, max_kv, Kb != nullptr, dtype);
+  const int st = check_ws(ws, ws_bytes, plan.ws_bytes);
+  if (st != SPRINT_OK) return st;
+  return status_of(launch_attend(Q, nseq, Lq, Hq, Kp, Vp, cu_kv, Kb, Vb, Hkv, D, scale, dtype, O,
+                                 plan, ws, as_stream(stream)));
+}
+
+// ---------------------------------------------------------------- unmask
+int unmask_select(const float* conf, const int32_t* argmax, int32_t nseq, int32_t Lq, float tau,
+                  int32_t steps_left, uint8_t* masked, int32_t* tokens, int32_t* n_accepted,
+                  void* stream) {
+  if (nseq < 1 || Lq < 1 || tau != tau) return SPRINT_EINVAL;
+  if (Lq > 64) return SPRINT_EUNSUPPORTED;
+  if (!dev4(conf) || !dev4(argmax) || masked == nullptr || !dev4(tokens) || !dev4(n_accepted))
+    return SPRINT_EINVAL;
+  return status_of(launch_unmask(conf, argmax, nseq, Lq, tau, steps_left, masked, tokens,
+                                 n_accepted, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Host-side launchers behind the C ABI.  Arguments reaching these functions
+// have already been validated by abi.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sprint {
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- key norm + composite score
+size_t score_ws_bytes(int64_t total_L, int nseq);
+hipError_t launch_score(const void* K, const float* conf, const int32_t* cu_len, int nseq,
+                        int64_t total_L, int Hkv, int D, int dtype, float alpha, float* ibar,
+                        float* score, void* ws, hipStream_t st);
+
+// ---- per-modality top-k + compaction
+size_t prune_ws_bytes(int64_t total_L, int nseq);
+hipError_t launch_prune(const float* score, const uint8_t* modality, const int32_t* cu_len,
+                        const int32_t* keep, const int32_t* cu_kept, int nseq, int64_t total_L,
+                        int64_t total_kept, const void* K, const void* V, int Hkv, int D,
+                        int dtype, void* K_out, void* V_out, int32_t* kept_idx, void* ws,
+                        hipStream_t st);
+
+// ---- block attention (split-KV + combine)
+struct AttnPlan {
+  int kps;         // keys per split (multiple of the key tile)
+  int n_splits;    // splits per (sequence, KV head)
+  int rows;        // query rows per KV head = (Hq/Hkv) * Lq
+  size_t ws_bytes;
+};
+AttnPlan attend_plan(int nseq, int Lq, int Hq, int Hkv, int D, int max_kv, int has_block,
+                     int dtype);
+hipError_t launch_attend(const void* Q, int nseq, int Lq, int Hq, const void* Kp, const void* Vp,
+                         const int32_t* cu_kv, const void* Kb, const void* Vb, int Hkv, int D,
+                         float scale, int dtype, void* O, const AttnPlan& plan, void* ws,
+                         hipStream_t st);
+
+// ---- LM-head confidence (fused GEMM + streaming max / log-sum-exp, then merge)
+size_t lmhead_ws_bytes(int64_t M, int H, int V, int dtype);
+hipError_t launch_lmhead(const void* X, int64_t M, int H, const void* W, int V, int dtype,
+                         float* conf, int32_t* argmax, float* lse, void* ws, hipStream_t st);
+
+// ---- unmask selection
+hipError_t launch_unmask(const float* conf, const int32_t* argmax, int nseq, int Lq, float tau,
+                         int steps_left, uint8_t* masked, int32_t* tokens, int32_t* n_accepted,
+                         hipStream_t st);
+
+}  // namespace sprint

@@ -1,0 +1,60 @@
+// Confidence-adaptive unmasking, one step (LLaDA2.0-Uni, SPRINT "Non-uniform
+// Token Unmasking"): accept every masked position whose confidence exceeds
+// tau, and at least ceil(m / (T - t)) of them, ranked by (confidence
+// descending, position ascending).
+//
+// One wave per sequence, one lane per block position (Lq <= 64).  The rank of
+// a masked position is the number of masked positions ahead of it in that
+// order, computed by broadcasting every lane's confidence in turn.
+#include "sprint_device.hpp"
+#include "sprint_internal.hpp"
+
+namespace sprint {
+namespace {
+
+__global__ __launch_bounds__(64) void unmask_kernel(const float* __restrict__ conf,
+                                                    const int32_t* __restrict__ argmax, int Lq,
+                                                    float tau, int steps_left,
+                                                    uint8_t* __restrict__ masked,
+                                                    int32_t* __restrict__ tokens,
+                                                    int32_t* __restrict__ n_accepted) {
+  const int s = blockIdx.x;
+  const int i = threadIdx.x;
+  const int64_t base = static_cast<int64_t>(s) * Lq;
+  const bool valid = i < Lq;
+  const float c = valid ? conf[base + i] : 0.f;
+  const bool msk = valid && masked[base + i] != 0;
+  const uint64_t bal_m = __ballot(msk);
+  const uint64_t bal_hi = __ballot(msk && c > tau);
+  const int m = __popcll(bal_m);
+  const int n_hi = __popcll(bal_hi);
+  int q = m;
+  if (steps_left > 0) {
+    const int64_t ceil_q = (static_cast<int64_t>(m) + steps_left - 1) / steps_left;
+    q = ceil_q < m ? static_cast<int>(ceil_q) : m;
+  }
+  const int count = n_hi > q ? n_hi : q;
+  int rank = 0;
+  for (int j = 0; j < Lq; ++j) {
+    const float cj = __shfl(c, j, 64);
+    const bool mj = (bal_m >> j) & 1ull;
+    if (mj && (cj > c || (cj == c && j < i))) ++rank;
+  }
+  if (msk && rank < count) {
+    tokens[base + i] = argmax[base + i];
+    masked[base + i] = 0;
+  }
+  if (i == 0) n_accepted[s] = count;
+}
+
+}  // namespace
+
+hipError_t launch_unmask(const float* conf, const int32_t* argmax, int nseq, int Lq, float tau,
+                         int steps_left, uint8_t* masked, int32_t* tokens, int32_t* n_accepted,
+                         hipStream_t st) {
+  unmask_kernel<<<dim3(nseq), dim3(64), 0, st>>>(conf, argmax, Lq, tau, steps_left, masked, tokens,
+                                                 n_accepted);
+  return hipGetLastError();
+}
+
+}  // namespace sprint

@@ -1,0 +1,248 @@
+"""ctypes binding of libsprint.so (C ABI in include/sprint.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs and workspaces are allocated with torch when the caller
+does not pass them, and the call runs on torch's current HIP stream.  Every
+computation happens in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch  # imported before the library so that both share one HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsprint.so")
+
+F32 = 0
+BF16 = 1
+
+_c_void_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_f64 = ctypes.c_double
+_size = ctypes.c_size_t
+
+_SIGS = {
+    "sprint_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "sprint_version": (ctypes.c_int, []),
+    "sprint_keep_count": (_i64, [_f64, _i64]),
+    "sprint_plan_keep": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _f64, _f64, _c_void_p,
+                                        _c_void_p, _c_void_p]),
+    "lmhead_confidence_ws": (_size, [_i64, _i32, _i32, _i32]),
+    "lmhead_confidence": (ctypes.c_int, [_c_void_p, _i64, _i32, _c_void_p, _i32, _i32, _c_void_p,
+                                         _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "sprint_score_ws": (_size, [_i64, _i32]),
+    "sprint_score": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _i32,
+                                    _f32, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "sprint_prune_kv_ws": (_size, [_i64, _i32]),
+    "sprint_prune_kv": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
+                                       _i64, _i64, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                       _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size,
+                                       _c_void_p]),
+    "block_attend_ws": (_size, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "block_attend": (ctypes.c_int, [_c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
+                                    _i64, _i32, _c_void_p, _c_void_p, _i32, _i32, _f32, _i32,
+                                    _c_void_p, _c_void_p, _size, _c_void_p]),
+    "unmask_select": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _f32, _i32, _c_void_p,
+                                     _c_void_p, _c_void_p, _c_void_p]),
+}
+
+EXPORTS = tuple(_SIGS)
+
+_lib = None
+
+
+class SprintError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {strerror(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsprint.so once; raise loudly if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               f"`python -m sparse_prefix_kv_amd.build` (hipcc, gfx950)")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = h
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().sprint_strerror(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise SprintError(fn, status)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ws(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if ws is not None:
+        return ws
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------------- host helpers
+
+def sprint_keep_count(r: float, n: int) -> int:
+    return int(lib().sprint_keep_count(float(r), int(n)))
+
+
+def sprint_plan_keep(n_text: Sequence[int], n_img: Sequence[int], r_text: float, r_img: float):
+    """Host keep counts -> (keep [nseq*2] int32 list, cu_kept [nseq+1], total_kept)."""
+    nseq = len(n_text)
+    nt = (ctypes.c_int64 * nseq)(*[int(x) for x in n_text])
+    ni = (ctypes.c_int64 * nseq)(*[int(x) for x in n_img])
+    keep = (ctypes.c_int32 * (2 * nseq))()
+    cu = (ctypes.c_int32 * (nseq + 1))()
+    tot = ctypes.c_int64()
+    _check("sprint_plan_keep", lib().sprint_plan_keep(
+        ctypes.addressof(nt), ctypes.addressof(ni), nseq, float(r_text), float(r_img),
+        ctypes.addressof(keep), ctypes.addressof(cu), ctypes.addressof(tot)))
+    return list(keep), list(cu), int(tot.value)
+
+
+# --------------------------------------------------------------------------- workspace queries
+
+def lmhead_confidence_ws(M: int, H: int, V: int, dtype: int) -> int:
+    return int(lib().lmhead_confidence_ws(M, H, V, dtype))
+
+
+def sprint_score_ws(total_L: int, nseq: int) -> int:
+    return int(lib().sprint_score_ws(total_L, nseq))
+
+
+def sprint_prune_kv_ws(total_L: int, nseq: int) -> int:
+    return int(lib().sprint_prune_kv_ws(total_L, nseq))
+
+
+def block_attend_ws(nseq, Lq, Hq, Hkv, D, max_kv, has_block) -> int:
+    return int(lib().block_attend_ws(nseq, Lq, Hq, Hkv, D, max_kv, int(bool(has_block))))
+
+
+# --------------------------------------------------------------------------- device calls
+
+def lmhead_confidence(hidden: torch.Tensor, W: torch.Tensor, conf=None, argmax=None, lse=None,
+                      want_lse: bool = False, ws=None, stream=None):
+    """Top-1 softmax confidence and argmax of hidden @ W^T.  hidden [M, H], W [V, H]."""
+    _dev(hidden, "hidden")
+    _dev(W, "W")
+    M, H = hidden.shape
+    V = W.shape[0]
+    if W.shape[1] != H or W.dtype != hidden.dtype:
+        raise ValueError("hidden/W shape or dtype mismatch")
+    dt = _dt(hidden)
+    dev = hidden.device
+    conf = torch.empty(M, dtype=torch.float32, device=dev) if conf is None else conf
+    argmax = torch.empty(M, dtype=torch.int32, device=dev) if argmax is None else argmax
+    if want_lse and lse is None:
+        lse = torch.empty(M, dtype=torch.float32, device=dev)
+    ws = _ws(lmhead_confidence_ws(M, H, V, dt), dev, ws)
+    _check("lmhead_confidence", lib().lmhead_confidence(
+        _ptr(hidden), M, H, _ptr(W), V, dt, _ptr(conf), _ptr(argmax), _ptr(lse), _ptr(ws),
+        ws.numel(), _stream(stream)))
+    return (conf, argmax, lse) if want_lse else (conf, argmax)
+
+
+def sprint_score(K: torch.Tensor, conf: torch.Tensor, cu_len: torch.Tensor, alpha: float = 0.5,
+                 ibar=None, score=None, ws=None, stream=None):
+    """Mean-normalised key norm and composite score.  K [total_L, Hkv, D]."""
+    _dev(K, "K")
+    total_L, Hkv, D = K.shape
+    nseq = cu_len.numel() - 1
+    dev = K.device
+    ibar = torch.empty(total_L, dtype=torch.float32, device=dev) if ibar is None else ibar
+    score = torch.empty(total_L, dtype=torch.float32, device=dev) if score is None else score
+    ws = _ws(sprint_score_ws(total_L, nseq), dev, ws)
+    _check("sprint_score", lib().sprint_score(
+        _ptr(K), _ptr(conf), _ptr(cu_len), nseq, total_L, Hkv, D, _dt(K), float(alpha),
+        _ptr(ibar), _ptr(score), _ptr(ws), ws.numel(), _stream(stream)))
+    return ibar, score
+
+
+def sprint_prune_kv(score, modality, cu_len, keep, cu_kept, total_kept: int, K, V,
+                    K_out=None, V_out=None, kept_idx=None, ws=None, stream=None):
+    """Per-modality top-k selection and compaction into a contiguous pruned cache."""
+    _dev(K, "K")
+    _dev(V, "V")
+    total_L, Hkv, D = K.shape
+    nseq = cu_len.numel() - 1
+    dev = K.device
+    if K_out is None:
+        K_out = torch.empty((max(total_kept, 1), Hkv, D), dtype=K.dtype, device=dev)[:total_kept]
+    if V_out is None:
+        V_out = torch.empty((max(total_kept, 1), Hkv, D), dtype=V.dtype, device=dev)[:total_kept]
+    if kept_idx is None:
+        kept_idx = torch.empty(max(total_kept, 1), dtype=torch.int32, device=dev)[:total_kept]
+    ws = _ws(sprint_prune_kv_ws(total_L, nseq), dev, ws)
+    _check("sprint_prune_kv", lib().sprint_prune_kv(
+        _ptr(score), _ptr(modality), _ptr(cu_len), _ptr(keep), _ptr(cu_kept), nseq, total_L,
+        int(total_kept), _ptr(K), _ptr(V), Hkv, D, _dt(K), _ptr(K_out), _ptr(V_out),
+        _ptr(kept_idx), _ptr(ws), ws.numel(), _stream(stream)))
+    return K_out, V_out, kept_idx
+
+
+def block_attend(Q, Kp, Vp, cu_kv, max_kv: int, Kb=None, Vb=None, scale: Optional[float] = None,
+                 O=None, ws=None, stream=None):
+    """softmax(Q K^T * scale) V over [prefix ; block] with GQA.  Q [nseq, Lq, Hq, D]."""
+    _dev(Q, "Q")
+    nseq, Lq, Hq, D = Q.shape
+    Hkv = Kp.shape[1]
+    total_kv = Kp.shape[0]
+    if scale is None:
+        scale = D ** -0.5
+    dev = Q.device
+    O = torch.empty_like(Q) if O is None else O
+    ws = _ws(block_attend_ws(nseq, Lq, Hq, Hkv, D, max_kv, Kb is not None), dev, ws)
+    _check("block_attend", lib().block_attend(
+        _ptr(Q), nseq, Lq, Hq, _ptr(Kp) if total_kv else None, _ptr(Vp) if total_kv else None,
+        _ptr(cu_kv), total_kv, int(max_kv), _ptr(Kb), _ptr(Vb), Hkv, D, float(scale), _dt(Q),
+        _ptr(O), _ptr(ws), ws.numel(), _stream(stream)))
+    return O
+
+
+def unmask_select(conf, argmax, masked, tokens, tau: float, steps_left: int, n_accepted=None,
+                  stream=None):
+    """One confidence-adaptive unmasking step; updates masked and tokens in place."""
+    nseq, Lq = conf.shape
+    if n_accepted is None:
+        n_accepted = torch.empty(nseq, dtype=torch.int32, device=conf.device)
+    _check("unmask_select", lib().unmask_select(
+        _ptr(conf), _ptr(argmax), nseq, Lq, float(tau), int(steps_left), _ptr(masked),
+        _ptr(tokens), _ptr(n_accepted), _stream(stream)))
+    return n_accepted

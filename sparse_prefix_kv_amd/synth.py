@@ -232,3 +232,26 @@ def random_unmask_state(nseq: int, Lq: int, vocab: int, seed: int, tau: float,
     masked = (rng.uniform(0, 1, size=(nseq, Lq)) < frac_masked).astype(np.uint8)
     tokens = np.where(masked == 1, -1, rng.integers(0, vocab, size=(nseq, Lq))).astype(np.int32)
     return conf, argmax, masked, tokens
+
+
+def normal_array(shape, seed: int, std: float = 1.0, dtype: str = "f32") -> np.ndarray:
+    """N(0, std^2) float32 draws, rounded to bf16 values when dtype is "bf16"."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
+    return bf16_round(a) if dtype == "bf16" else a
+
+
+def lognormal_rows(a: np.ndarray, seed: int, sigma: float = 0.5) -> np.ndarray:
+    """Scale each leading-axis row of `a` by its own lognormal(0, sigma) draw."""
+    rng = np.random.default_rng(seed)
+    f = rng.lognormal(0.0, sigma, size=a.shape[0]).astype(np.float32)
+    return a * f.reshape((-1,) + (1,) * (a.ndim - 1))
+
+
+def plant_rows(W: np.ndarray, X: np.ndarray, pairs, gain: float, dtype: str = "f32") -> np.ndarray:
+    """Copy gain * X[r] into W[v] for each (r, v) pair, so that row r's logit
+    for token v is large (a planted confident prediction)."""
+    W = W.copy()
+    for r, v in pairs:
+        W[v] = np.float32(gain) * X[r]
+    return bf16_round(W) if dtype == "bf16" else W

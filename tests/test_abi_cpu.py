@@ -1,0 +1,127 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, computes its host-side keep counts, and rejects bad arguments
+before any HIP call."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from sparse_prefix_kv_amd import sprint
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sprint.h")
+FAKE = 0x10000          # a 16-byte-aligned address that is never dereferenced
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    return sorted({n for n in names if n not in ("if", "sizeof")})
+
+
+def test_library_exports_every_declared_function():
+    lib = sprint.lib()
+    declared = _header_functions()
+    assert len(declared) >= 13
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(sprint.EXPORTS)
+
+
+def test_strerror_and_version():
+    assert sprint.strerror(0) == "ok"
+    assert "workspace" in sprint.strerror(3)
+    assert sprint.lib().sprint_version() >= 100
+
+
+def test_keep_count_matches_page_rule_golden():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "sprint_settings.json")))
+    for row in g["keep_counts"]:
+        assert sprint.sprint_keep_count(row["r"], row["n"]) == row["k"]
+    assert sprint.sprint_keep_count(float("nan"), 10) == 0
+    assert sprint.sprint_keep_count(2.0, 10) == 10
+    assert sprint.sprint_keep_count(0.8, 0) == 0
+
+
+def test_plan_keep():
+    keep, cu, tot = sprint.sprint_plan_keep([1024, 512, 0], [3072, 15872, 64], 1.0, 0.8)
+    assert keep == [1024, 2457, 512, 12697, 0, 51]
+    assert cu == [0, 3481, 3481 + 13209, 3481 + 13209 + 51]
+    assert tot == cu[-1]
+    with pytest.raises(sprint.SprintError):
+        sprint.sprint_plan_keep([-1], [3], 1.0, 1.0)
+
+
+def test_workspace_queries_are_host_only():
+    assert sprint.lmhead_confidence_ws(4096, 2048, 32768, sprint.BF16) >= 4096 * 256 * 16
+    assert sprint.sprint_score_ws(4096, 1) > 0
+    assert sprint.sprint_prune_kv_ws(4096, 1) > 0
+    assert sprint.block_attend_ws(1, 32, 16, 4, 128, 4096, 1) > 0
+    assert sprint.block_attend_ws(1, 32, 16, 5, 128, 4096, 1) == 0       # Hq % Hkv != 0
+
+
+def _call(name, *args):
+    return getattr(sprint.lib(), name)(*args)
+
+
+def test_lmhead_rejects_before_hip():
+    ok = (FAKE, 32, 2048, FAKE, 32768, sprint.BF16, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    a = list(ok); a[0] = None
+    assert _call("lmhead_confidence", *a) == 1                      # NULL hidden
+    a = list(ok); a[0] = FAKE + 2
+    assert _call("lmhead_confidence", *a) == 1                      # misaligned
+    a = list(ok); a[2] = 100
+    assert _call("lmhead_confidence", *a) == 2                      # H not a multiple of 64
+    a = list(ok); a[5] = 7
+    assert _call("lmhead_confidence", *a) == 1                      # bad dtype
+    a = list(ok); a[10] = 16
+    assert _call("lmhead_confidence", *a) == 3                      # workspace too small
+    a = list(ok); a[1] = 0
+    assert _call("lmhead_confidence", *a) == 1                      # M = 0
+
+
+def test_score_and_prune_reject_before_hip():
+    sc = [FAKE, FAKE, FAKE, 1, 4096, 4, 128, sprint.BF16, 0.5, FAKE, FAKE, FAKE, 1 << 30, None]
+    a = list(sc); a[6] = 96
+    assert _call("sprint_score", *a) == 2
+    a = list(sc); a[3] = 0
+    assert _call("sprint_score", *a) == 1
+    a = list(sc); a[8] = float("inf")
+    assert _call("sprint_score", *a) == 1
+    a = list(sc); a[12] = 4
+    assert _call("sprint_score", *a) == 3
+    pr = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 3481, FAKE, FAKE, 4, 128, sprint.BF16,
+          FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+    a = list(pr); a[7] = 5000
+    assert _call("sprint_prune_kv", *a) == 1                        # kept > total
+    a = list(pr); a[13] = None
+    assert _call("sprint_prune_kv", *a) == 1                        # NULL K_out
+    a = list(pr); a[17] = 1
+    assert _call("sprint_prune_kv", *a) == 3
+
+
+def test_attend_and_unmask_reject_before_hip():
+    at = [FAKE, 1, 32, 16, FAKE, FAKE, FAKE, 4096, 4096, FAKE, FAKE, 4, 128, 0.088, sprint.BF16,
+          FAKE, FAKE, 1 << 30, None]
+    a = list(at); a[11] = 5
+    assert _call("block_attend", *a) == 1                           # Hq % Hkv
+    a = list(at); a[12] = 80
+    assert _call("block_attend", *a) == 2                           # head dim
+    a = list(at); a[2] = 65
+    assert _call("block_attend", *a) == 2                           # Lq > 64
+    a = list(at); a[10] = None
+    assert _call("block_attend", *a) == 1                           # Kb without Vb
+    a = list(at); a[9] = None; a[10] = None; a[8] = 0
+    assert _call("block_attend", *a) == 1                           # no keys at all
+    a = list(at); a[17] = 8
+    assert _call("block_attend", *a) == 3
+    um = [FAKE, FAKE, 1, 32, 0.9, 9, FAKE, FAKE, FAKE, None]
+    a = list(um); a[3] = 65
+    assert _call("unmask_select", *a) == 2
+    a = list(um); a[4] = float("nan")
+    assert _call("unmask_select", *a) == 1
+    a = list(um); a[6] = None
+    assert _call("unmask_select", *a) == 1
