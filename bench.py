@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""SPRINT block-step benchmark on one MI355X.
+
+One benchmark step is one whole SPRINT block over one batch of synthetic
+input: the pruning pass (prefix LM-head confidence, key-norm score,
+per-modality top-k, compaction, full-prefix attention, block confidence,
+unmasking) followed by the pruned denoising steps (attention over the pruned
+cache, block confidence, unmasking).  The default workload is the bf16
+single-sequence prefix of 4096 positions (1024 text + 3072 image), 16/4
+heads of dim 128, vocabulary 32768, pass + 8 steps.
+
+Printed: one JSON line.  `value` is denoising block-steps per second
+(1 pass + 8 pruned steps = 9 block-steps per block and sequence), from the
+eager timed region in which HIP events bracket every library call on the
+stream it runs on.  The same line carries the full-retention baseline, the
+HIP-graph replay rate, per-call timings (warm and cache-flushed), the
+roofline of the dominant call and the CPU oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector / fp32 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50, help="timed blocks")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed blocks")
+    ap.add_argument("--workload", default="single4k")
+    ap.add_argument("--cold-iters", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-blocks", type=int, default=2)
+    ap.add_argument("--no-graph", action="store_true")
+    return ap.parse_args()
+
+
+class EventTimer:
+    """Records a start/end HIP event pair around named regions on torch's
+    current stream (the stream every library call is launched on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.records = []
+
+    def __call__(self, name):
+        timer = self
+
+        class Ctx:
+            def __enter__(self_):
+                s = timer.torch.cuda.Event(enable_timing=True)
+                s.record()
+                self_.s = s
+
+            def __exit__(self_, *a):
+                e = timer.torch.cuda.Event(enable_timing=True)
+                e.record()
+                timer.records.append((name, self_.s, e))
+                return False
+        return Ctx()
+
+    def summary(self):
+        out = {}
+        for name, s, e in self.records:
+            out.setdefault(name, []).append(s.elapsed_time(e) * 1e3)   # us
+        return {k: {"n": len(v), "mean_us": sum(v) / len(v), "min_us": min(v),
+                    "median_us": sorted(v)[len(v) // 2]} for k, v in out.items()}
+
+
+def work_model(blk):
+    """Algorithmic bytes / flops per library call (counted once per launch)."""
+    wl, lay = blk.wl, blk.layout
+    es, H, V, D, Hq, Hkv, Lq = wl.es, wl.H, wl.vocab, wl.D, wl.Hq, wl.Hkv, wl.Lq
+    nseq, L, Lk = lay.nseq, lay.total_L, blk.total_kept
+    M = nseq * Lq
+    row = Hkv * D * es
+
+    def attn(kv):
+        return {"bytes": (kv + nseq * Lq) * row * 2 + 2 * nseq * Lq * Hq * D * es,
+                "flops": 4 * Lq * Hq * D * (kv + nseq * Lq)}
+    return {
+        "lmhead_prefix": {"bytes": V * H * es + L * H * es + L * 8,
+                          "flops": 2 * L * H * V, "bound": "mfma"},
+        "lmhead_block": {"bytes": V * H * es + M * H * es + M * 8,
+                         "flops": 2 * M * H * V, "bound": "hbm"},
+        "attend_full": dict(attn(L), bound="hbm"),
+        "attend_pruned": dict(attn(Lk), bound="hbm"),
+        "score": {"bytes": L * row + 12 * L, "flops": 2 * L * Hkv * D, "bound": "hbm"},
+        "prune": {"bytes": 4 * Lk * row + 4 * Lk + 5 * L, "flops": 0, "bound": "hbm"},
+        "unmask": {"bytes": M * 14, "flops": 0, "bound": "hbm"},
+    }
+
+
+def src_sha(relpath):
+    with open(os.path.join(ROOT, relpath), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(call):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    ent = t.get(call)
+    if not ent or ent.get("source_sha") != src_sha(ent["source"]):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, wl, n_blocks):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i["num_threads"] for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    lay = x.layout
+    t0 = time.perf_counter()
+    for _ in range(n_blocks):
+        oracle.run_block(x.Q, x.K, x.V, x.Kb, x.Vb, x.hidden, x.W, lay.cu_len, lay.modality,
+                         wl.r_text, wl.r_img, np.float32(wl.tau), wl.T, wl.T - 1)
+    dt = time.perf_counter() - t0
+    steps = n_blocks * wl.T * lay.nseq
+    return {"value": steps / dt, "unit": "block-steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_blocks} whole block(s) of the same workload (pass + {wl.T - 1} steps), "
+                      f"fp64 NumPy, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the SPRINT block step runs on a single MI355X here).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from sparse_prefix_kv_amd import synth
+    from sparse_prefix_kv_amd.block import SprintBlock
+
+    wl = synth.WORKLOADS[args.workload]
+    n_steps = (wl.T - 1) if wl.T is not None else wl.Lq - 1
+    log(f"[bench] workload {wl.name}: {wl.desc}")
+    x = synth.make_inputs(wl, 0)
+    blk = SprintBlock(x, "cuda")
+    lay = blk.layout
+    steps_per_block = (n_steps + 1) * lay.nseq
+    props = torch.cuda.get_device_properties(0)
+    log(f"[bench] device {props.name}, {props.multi_processor_count} CUs; kept "
+        f"{blk.total_kept} of {lay.total_L} prefix positions")
+
+    # ---------------------------------------------------------------- warmup
+    for _ in range(args.warmup):
+        blk.run_block(n_steps)
+        blk.run_full_block(n_steps)
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+
+    # ---------------------------------------------------------------- timed: SPRINT
+    timer = EventTimer(torch)
+    blk.timer = timer
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        blk.run_block(n_steps)
+    torch.cuda.synchronize()
+    t_sprint = (time.perf_counter() - t0) / args.steps
+    calls = timer.summary()
+    log(f"[bench] SPRINT block {t_sprint * 1e3:.3f} ms")
+
+    # ---------------------------------------------------------------- timed: full retention
+    timer_full = EventTimer(torch)
+    blk.timer = timer_full
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        blk.run_full_block(n_steps)
+    torch.cuda.synchronize()
+    t_full = (time.perf_counter() - t0) / args.steps
+    calls_full = timer_full.summary()
+    blk.timer = None
+    log(f"[bench] full-retention block {t_full * 1e3:.3f} ms")
+
+    # ---------------------------------------------------------------- graph replay
+    graph = None
+    if not args.no_graph:
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                blk.run_block(n_steps)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                blk.run_block(n_steps)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                g.replay()
+            torch.cuda.synchronize()
+            t_graph = (time.perf_counter() - t0) / args.steps
+            graph = {"block_ms": t_graph * 1e3, "block_steps_per_s": steps_per_block / t_graph}
+            log(f"[bench] graph-replayed SPRINT block {t_graph * 1e3:.3f} ms")
+        except Exception as e:  # graph capture is an extra, never the headline
+            graph = {"error": repr(e)[:200]}
+
+    # ---------------------------------------------------------------- cold per-call timings
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    cold = EventTimer(torch)
+
+    def cold_run(name, fn):
+        for i in range(args.cold_iters):
+            flush.fill_(float(i))
+            with cold(name):
+                fn()
+    blk.reset()
+    cold_run("lmhead_prefix", blk.prefix_confidence)
+    cold_run("score", blk.score_prefix)
+    cold_run("prune", blk.prune_prefix)
+    cold_run("attend_full", lambda: blk.attend(False))
+    cold_run("attend_pruned", lambda: blk.attend(True))
+    cold_run("lmhead_block", blk.block_confidence)
+    torch.cuda.synchronize()
+    calls_cold = cold.summary()
+    del flush
+
+    # ---------------------------------------------------------------- roofline
+    work = work_model(blk)
+    per_block = {k: v["mean_us"] * v["n"] / args.steps for k, v in calls.items()}
+    dominant = max(per_block, key=per_block.get)
+    kernels = {}
+    for name, st in calls.items():
+        w = work[name]
+        us = st["mean_us"]
+        ent = {"mean_us": round(us, 3), "launches_per_block": st["n"] // args.steps,
+               "alg_bytes": w["bytes"], "alg_flops": w["flops"], "bound": w["bound"],
+               "gbs": round(w["bytes"] / us / 1e3, 1),
+               "tflops": round(w["flops"] / us / 1e6, 2)}
+        if name in calls_cold:
+            ent["cold_mean_us"] = round(calls_cold[name]["mean_us"], 3)
+        kernels[name] = ent
+    dw = work[dominant]
+    dus = calls[dominant]["mean_us"]
+    bf16 = wl.dtype == "bf16"
+    if dw["bound"] == "mfma":
+        achieved = dw["flops"] / dus / 1e6
+        peak = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
+        unit = "TFLOP/s"
+    else:
+        achieved = dw["bytes"] / dus / 1e3
+        peak = HBM_PEAK_GBS
+        unit = "GB/s"
+    roofline = {"bound": dw["bound"], "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": load_traffic(dominant),
+                "kernel": dominant, "alg_per_launch": dw["flops"] if dw["bound"] == "mfma"
+                else dw["bytes"], "mean_launch_us": round(dus, 3)}
+
+    att_pr = calls["attend_pruned"]["mean_us"]
+    att_full = calls_full["attend_full"]["mean_us"]
+    step_pr = att_pr + calls["lmhead_block"]["mean_us"] + calls["unmask"]["mean_us"]
+    step_full = (att_full + calls_full["lmhead_block"]["mean_us"] +
+                 calls_full["unmask"]["mean_us"])
+
+    # ---------------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        cpu = cpu_baseline(x, wl, args.cpu_blocks)
+        log(f"[bench] oracle {cpu['value']:.3f} block-steps/s on {cpu['cores']} threads")
+
+    value = steps_per_block / t_sprint
+    rec = {
+        "metric": "denoising block-steps/s (pruned vs full prefix), 1 MI355X",
+        "value": round(value, 2),
+        "unit": "block-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_sprint * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded N(0,1) activations, lognormal key scales, N(0,0.02) LM head)",
+        "config": {"workload": wl.name, "desc": wl.desc, "nseq": lay.nseq,
+                   "prefix": int(lay.total_L), "kept": int(blk.total_kept), "block": wl.Lq,
+                   "steps_per_block": n_steps + 1, "r_text": blk.r_text, "r_img": blk.r_img,
+                   "tau": blk.tau, "step_unit": "one whole block (pass + pruned steps)"},
+        "tokens_per_s": round(wl.Lq * lay.nseq / t_sprint, 1),
+        "full_retention": {"block_ms": round(t_full * 1e3, 4),
+                           "block_steps_per_s": round(steps_per_block / t_full, 2)},
+        "speedup_pruned_vs_full": {"attention_call": round(att_full / att_pr, 4),
+                                   "denoising_step": round(step_full / step_pr, 4),
+                                   "block": round(t_full / t_sprint, 4),
+                                   "pages_claim_context": "up to 1.6x end to end (model, "
+                                                          "hardware and workload not given)"},
+        "graph": graph,
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

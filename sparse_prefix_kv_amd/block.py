@@ -21,6 +21,14 @@ from . import sprint, synth
 BIG_STEPS = 1 << 30   # steps_left for "at least one acceptance per step"
 
 
+class _NullCtx:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *a):
+        return False
+
+
 def _to_dev(a: np.ndarray, dtype: str, device) -> torch.Tensor:
     if dtype == "bf16":
         bits = synth.bf16_bits(a)
@@ -78,6 +86,11 @@ class SprintBlock:
         self.argmax_blk = torch.empty(M, dtype=i32, device=dev)
         self.masked = torch.ones((self.nseq, self.Lq), dtype=torch.uint8, device=dev)
         self.tokens = torch.full((self.nseq, self.Lq), -1, dtype=i32, device=dev)
+        # block-start state (all masked), restored by a device copy so that a
+        # captured graph holds no memset node
+        self.masked0 = self.masked.clone()
+        self.tokens0 = self.tokens.clone()
+        self.timer = None
         self.n_acc = torch.empty(self.nseq, dtype=i32, device=dev)
         dti = sprint.BF16 if dt == "bf16" else sprint.F32
         H, Vv = wl.H, wl.vocab
@@ -99,35 +112,61 @@ class SprintBlock:
         return BIG_STEPS if self.T is None else self.T - t
 
     def reset(self):
-        self.masked.fill_(1)
-        self.tokens.fill_(-1)
+        self.masked.copy_(self.masked0)
+        self.tokens.copy_(self.tokens0)
+
+    def _t(self, name):
+        """Event-timed region around one library call when a timer is set."""
+        return self.timer(name) if self.timer is not None else _NullCtx()
 
     def prefix_confidence(self):
-        sprint.lmhead_confidence(self.hidden, self.W, conf=self.conf_prefix,
-                                 argmax=self.argmax_prefix, ws=self.ws_lm_prefix)
+        with self._t("lmhead_prefix"):
+            sprint.lmhead_confidence(self.hidden, self.W, conf=self.conf_prefix,
+                                     argmax=self.argmax_prefix, ws=self.ws_lm_prefix)
+
+    def score_prefix(self):
+        with self._t("score"):
+            sprint.sprint_score(self.K, self.conf_prefix, self.cu_len, self.alpha,
+                                ibar=self.ibar, score=self.score, ws=self.ws_score)
+
+    def prune_prefix(self):
+        with self._t("prune"):
+            sprint.sprint_prune_kv(self.score, self.modality, self.cu_len, self.keep,
+                                   self.cu_kept, self.total_kept, self.K, self.V,
+                                   K_out=self.K_pr, V_out=self.V_pr, kept_idx=self.kept_idx,
+                                   ws=self.ws_prune)
 
     def score_and_prune(self):
-        sprint.sprint_score(self.K, self.conf_prefix, self.cu_len, self.alpha, ibar=self.ibar,
-                            score=self.score, ws=self.ws_score)
-        sprint.sprint_prune_kv(self.score, self.modality, self.cu_len, self.keep, self.cu_kept,
-                               self.total_kept, self.K, self.V, K_out=self.K_pr, V_out=self.V_pr,
-                               kept_idx=self.kept_idx, ws=self.ws_prune)
+        self.score_prefix()
+        self.prune_prefix()
 
     def attend(self, pruned: bool):
         if pruned:
-            sprint.block_attend(self.Q, self.K_pr, self.V_pr, self.cu_kept, self.max_kept,
-                                self.Kb, self.Vb, O=self.O, ws=self.ws_att_pr)
+            with self._t("attend_pruned"):
+                sprint.block_attend(self.Q, self.K_pr, self.V_pr, self.cu_kept, self.max_kept,
+                                    self.Kb, self.Vb, O=self.O, ws=self.ws_att_pr)
         else:
-            sprint.block_attend(self.Q, self.K, self.V, self.cu_len, self.max_len, self.Kb,
-                                self.Vb, O=self.O, ws=self.ws_att_full)
+            with self._t("attend_full"):
+                sprint.block_attend(self.Q, self.K, self.V, self.cu_len, self.max_len, self.Kb,
+                                    self.Vb, O=self.O, ws=self.ws_att_full)
+
+    def block_confidence(self):
+        M = self.nseq * self.Lq
+        with self._t("lmhead_block"):
+            sprint.lmhead_confidence(self.O.view(M, self.Hq * self.D), self.W,
+                                     conf=self.conf_blk, argmax=self.argmax_blk,
+                                     ws=self.ws_lm_blk)
+
+    def unmask(self, t: int):
+        with self._t("unmask"):
+            sprint.unmask_select(self.conf_blk.view(self.nseq, self.Lq),
+                                 self.argmax_blk.view(self.nseq, self.Lq), self.masked,
+                                 self.tokens, self.tau, self.steps_left(t),
+                                 n_accepted=self.n_acc)
 
     def confidence_and_unmask(self, t: int):
-        M = self.nseq * self.Lq
-        sprint.lmhead_confidence(self.O.view(M, self.Hq * self.D), self.W, conf=self.conf_blk,
-                                 argmax=self.argmax_blk, ws=self.ws_lm_blk)
-        sprint.unmask_select(self.conf_blk.view(self.nseq, self.Lq),
-                             self.argmax_blk.view(self.nseq, self.Lq), self.masked, self.tokens,
-                             self.tau, self.steps_left(t), n_accepted=self.n_acc)
+        self.block_confidence()
+        self.unmask(t)
 
     # ------------------------------------------------------------------ block
     def pruning_pass(self):
