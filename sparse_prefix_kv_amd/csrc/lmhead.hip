@@ -180,6 +180,257 @@ __global__ __launch_bounds__(256) void lmhead_tile_kernel(const char* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-M path (the prefix pass, M = L rows): 256 x 256 block tile, eight
+// waves laid out 2 (vocab) x 4 (tokens), each owning 128 x 64 = 4 x 2 MFMA
+// tiles (128 fp32 accumulators), so two waves share each SIMD and one wave's
+// MFMAs cover the other's barrier and LDS latency.
+//
+// Global -> LDS: buffer loads straight into LDS (buffer_load_dwordx4 ... lds,
+// 1 KB of contiguous LDS per wave instruction) into two stages of 64-deep K
+// chunks (64 KB each: 256 W rows then 256 X rows of 128 bytes).  Every row
+// access is one whole 128-byte line, which keeps the L2 request count (the
+// L1's in-flight request capacity is the feed limit) at its minimum.  The two
+// stages are distinct LDS arrays so the compiler can see that reads of one
+// stage do not alias loads into the other; the loop is unrolled by two.
+//
+// Per chunk: four 16-deep k-slices of 8 MFMAs, the next slice's fragments
+// read under the current slice's MFMAs.  Before the last slice's MFMAs each
+// wave waits for its own loads of the next chunk and for its fragment reads,
+// then a plain s_barrier (no fence: a fence would drain every outstanding
+// load) hands the finished stage back; the chunk after next is then loaded
+// into it while the last slice's MFMAs run.
+//
+// LDS layout: the 16-byte slot of k-chunk c in row R is c ^ ((R >> 1) & 7),
+// so each 16-lane group of a ds_read_b128 fragment read covers all 64 banks.
+//
+// Blocks are mapped XCD-aware: block b runs on XCD b % 8, so each XCD gets a
+// contiguous range of tile ids, ordered in groups of 8 token tiles so the
+// ~32 blocks resident on one XCD share 4 W tiles and 8 X tiles in its L2.
+constexpr int kGB = 256;                     // tile edge (vocab and tokens)
+constexpr int kGKC = 64;                     // reduction depth per stage
+constexpr int kGStageElems = 2 * kGB * kGKC; // A rows then B rows
+constexpr int kGThreads = 512;
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+
+#define SPRINT_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt immediate: at most n vector-memory ops pending, lgkm unrestricted
+constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+// s_waitcnt immediate: vmcnt(0) and lgkmcnt(0)
+constexpr int vm_lgkm_zero_imm() { return (7 << 4); }
+
+// One 64-deep chunk of this wave's rows through buffer loads: instruction j
+// fills rows 32*wave + 8*j + lane/8 of the A (W) and B (X) halves of the
+// stage.  The swizzled k-chunk a lane fetches only depends on the parity of
+// j, so the per-lane part of every address is one of two 32-bit offsets and
+// the rest is a wave-uniform scalar offset.  The buffer descriptors span
+// exactly W and X, so rows past V or M read as zeros.
+__device__ __forceinline__ void gemm_dma(__amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rX,
+                                         uint32_t soA, uint32_t soB, uint32_t rs_bytes,
+                                         uint32_t offE, uint32_t offO, uint16_t* stA,
+                                         uint16_t* stB) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, SPRINT_LDS(stA + j * 512), 16,
+                                             (j & 1) ? offO : offE, soA + j * rs_bytes, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rX, SPRINT_LDS(stB + j * 512), 16,
+                                             (j & 1) ? offO : offE, soB + j * rs_bytes, 0, 0);
+}
+
+// Fragments of one 16-deep k-slice: 4 vocabulary tiles and 2 token tiles.
+__device__ __forceinline__ void gemm_frags(const uint16_t* sA, const uint16_t* sB, int so,
+                                           bf16x8 (&fa)[4], bf16x8 (&fb)[2]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[i] = as_bf16x8(ld16(sA + i * 32 * kGKC + so));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) fb[j] = as_bf16x8(ld16(sB + j * 32 * kGKC + so));
+}
+
+__device__ __forceinline__ void gemm_mma8(const bf16x8 (&fa)[4], const bf16x8 (&fb)[2],
+                                          f32x16 (&acc)[4][2]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = mma32_k16(fa[i], fb[j], acc[i][j]);
+}
+
+// Issue order for one slice: MFMAs and fragment reads alternated; the full
+// sched_barrier keeps later slices' reads from being hoisted.
+__device__ __forceinline__ void gemm_interleave() {
+#pragma unroll
+  for (int g = 0; g < 6; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__global__ __launch_bounds__(kGThreads) void lmhead_gemm_kernel(
+    const uint16_t* __restrict__ X, int64_t M, int H, const uint16_t* __restrict__ W, int V,
+    float4* __restrict__ part, int n_vt, int n_mt, int per_xcd) {
+  __shared__ __align__(16) uint16_t st0[kGStageElems];
+  __shared__ __align__(16) uint16_t st1[kGStageElems];
+  const int b = blockIdx.x;
+  const int t = (b % kXcds) * per_xcd + b / kXcds;
+  if (t >= n_vt * n_mt) return;
+  const int group = kGroupM * n_vt;
+  const int first_m = (t / group) * kGroupM;
+  const int gm = min(n_mt - first_m, kGroupM);
+  const int r_in = t % group;
+  const int mt = first_m + r_in % gm;
+  const int vt = r_in / gm;
+  const int v0 = vt * kGB;
+  const int64_t t0 = static_cast<int64_t>(mt) * kGB;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wv = wave & 1, wt = wave >> 1;
+  const int q = lane & 31, hh = lane >> 5;
+
+  // Load plan: instruction j of this wave fills rows r = 32*wave + 8*j + lane/8,
+  // slot lane%8, which holds k-chunk (lane%8) ^ ((r>>1)&7); that is
+  // (lane&7) ^ ((lane>>4)&7) for even j and the same ^ 4 for odd j.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int c_even = (lane & 7) ^ ((lane >> 4) & 7);
+  const uint32_t lrow_bytes = static_cast<uint32_t>(lane >> 3) * H * 2;
+  const uint32_t offE = lrow_bytes + c_even * 16;
+  const uint32_t offO = lrow_bytes + (c_even ^ 4) * 16;
+  const uint32_t rs_bytes = static_cast<uint32_t>(16) * H;    // 8 rows of bf16
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(W), 0, static_cast<int>(static_cast<int64_t>(V) * H * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(X), 0, static_cast<int>(M * H * 2), 0x00020000);
+  const uint32_t soA = static_cast<uint32_t>(v0 + 32 * wave_u) * H * 2;
+  const uint32_t soB = static_cast<uint32_t>(t0 + 32 * wave_u) * H * 2;
+  uint16_t* const dA0 = st0 + wave_u * 4 * 512;
+  uint16_t* const dB0 = st0 + kGB * kGKC + wave_u * 4 * 512;
+  uint16_t* const dA1 = st1 + wave_u * 4 * 512;
+  uint16_t* const dB1 = st1 + kGB * kGKC + wave_u * 4 * 512;
+
+  // Fragment reads: row R = wv*128 + i*32 + q (A) or wt*64 + j*32 + q (B),
+  // k-chunk 2*ks + hh at slot (2*ks + hh) ^ ((q >> 1) & 7).
+  const int sw = (q >> 1) & 7;
+  int so[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) so[ks] = ((2 * ks + hh) ^ sw) * 8;
+  const int aoff = (wv * 128 + q) * kGKC;
+  const int boff = kGB * kGKC + (wt * 64 + q) * kGKC;
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = H / kGKC;
+  gemm_dma(rW, rX, soA, soB, rs_bytes, offE, offO, dA0, dB0);
+  if (nk > 1) {
+    gemm_dma(rW, rX, soA + 2 * kGKC, soB + 2 * kGKC, rs_bytes, offE, offO, dA1, dB1);
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(8));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+  }
+  __builtin_amdgcn_s_barrier();
+  bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
+  gemm_frags(st0 + aoff, st0 + boff, so[0], fa0, fb0);
+
+#define SPRINT_GEMM_STEP(CUR, NXT, DA, DB, U)                                                \
+  {                                                                                          \
+    const int kc = kb + (U);                                                                 \
+    if (kc < nk) {                                                                           \
+      gemm_frags(CUR + aoff, CUR + boff, so[1], fa1, fb1);                                   \
+      gemm_mma8(fa0, fb0, acc);                                                              \
+      gemm_interleave();                                                                     \
+      gemm_frags(CUR + aoff, CUR + boff, so[2], fa0, fb0);                                   \
+      gemm_mma8(fa1, fb1, acc);                                                              \
+      gemm_interleave();                                                                     \
+      gemm_frags(CUR + aoff, CUR + boff, so[3], fa1, fb1);                                   \
+      gemm_mma8(fa0, fb0, acc);                                                              \
+      gemm_interleave();                                                                     \
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_zero_imm());                                        \
+      __builtin_amdgcn_s_barrier();                                                          \
+      if (kc + 2 < nk) {                                                                     \
+        const uint32_t k2 = 2u * (kc + 2) * kGKC;                                            \
+        gemm_dma(rW, rX, soA + k2, soB + k2, rs_bytes, offE, offO, DA, DB);                  \
+      }                                                                                      \
+      if (kc + 1 < nk) gemm_frags(NXT + aoff, NXT + boff, so[0], fa0, fb0);                  \
+      gemm_mma8(fa1, fb1, acc);                                                              \
+    }                                                                                        \
+  }
+  for (int kb = 0; kb < nk; kb += 2) {
+    SPRINT_GEMM_STEP(st0, st1, dA0, dB0, 0)
+    SPRINT_GEMM_STEP(st1, st0, dA1, dB1, 1)
+  }
+#undef SPRINT_GEMM_STEP
+  __syncthreads();
+
+  // Epilogue: per token column fold this wave's 128 vocabulary rows, then
+  // the partner half-wave, then the other vocabulary wave through LDS.  Rows
+  // past V (only in the last vocabulary tile) are set to -inf first.
+  const int vbase = v0 + wv * 128 + 4 * hh;
+  const bool edge = v0 + kGB > V;             // only the last vocabulary tile
+  Stat* red = reinterpret_cast<Stat*>(st0);   // [256 tokens][2 vocab waves]
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    // streaming fold over the four 32x32 tiles of this token column block,
+    // 16 accumulator values live at a time
+    float mx = -INFINITY, sum = 0.f;
+    int am = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float z[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        z[r] = acc[i][j][r];
+        if (edge && vbase + i * 32 + 8 * (r >> 2) + (r & 3) >= V) z[r] = -INFINITY;
+      }
+      float tm = -INFINITY;
+      int ta = INT_MAX;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (z[r] > tm) {
+          tm = z[r];
+          ta = vbase + i * 32 + 8 * (r >> 2) + (r & 3);
+        }
+      if (tm == -INFINITY) continue;
+      const float mn = fmaxf(mx, tm);
+      const float ml = mn * kLog2e;
+      float ts = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ts += exp2f(fmaf(z[r], kLog2e, -ml));
+      sum = (mx == -INFINITY ? 0.f : sum * exp2f(fmaf(mx, kLog2e, -ml))) + ts;
+      if (tm > mx) am = ta;     // rows ascend with i: strict '>' keeps the lowest index
+      mx = mn;
+    }
+    Stat st{mx, sum, am};
+    Stat other;
+    other.m = shfl_xor_f(st.m, 32);
+    other.s = shfl_xor_f(st.s, 32);
+    other.a = shfl_xor_i(st.a, 32);
+    if (hh == 0) {
+      merge(st, other);
+      red[(wt * 64 + j * 32 + q) * 2 + wv] = st;
+    }
+  }
+  __syncthreads();
+  if (tid < kGB) {
+    const int c = tid;                        // 256 token columns
+    const int64_t tok = t0 + c;
+    if (tok < M) {
+      Stat st = red[c * 2 + 0];
+      merge(st, red[c * 2 + 1]);
+      part[tok * n_vt + vt] = make_float4(st.m, st.s, __int_as_float(st.a), 0.f);
+    }
+  }
+}
+
 // One wave per row: each lane folds a strided subset of tiles in order, then
 // a fixed butterfly merges the lanes.
 __global__ __launch_bounds__(256) void lmhead_merge_kernel(const float4* __restrict__ part,
@@ -233,23 +484,35 @@ hipError_t run_tiles(const void* X, int64_t M, int H, const void* W, int V, floa
 // block, so the grid spreads W over every CU.  Large M (the prefix pass):
 // 128 x 128 tiles.
 inline bool small_m(int64_t M) { return M <= 32; }
-inline int tile_bv(int64_t M) { return small_m(M) ? 128 : 128; }
-
+// bf16, more than one token tile, H in whole 64-deep chunks, and W and X
+// each addressable by a 32-bit buffer descriptor
+inline bool gemm_path(int64_t M, int H, int V, int dtype) {
+  return dtype == 1 && M > kGB && H % (2 * kGKC) == 0 &&
+         static_cast<int64_t>(V) * H * 2 < (int64_t(1) << 31) && M * H * 2 < (int64_t(1) << 31);
+}
+inline int tile_bv(int64_t M, int H, int V, int dtype) {
+  return gemm_path(M, H, V, dtype) ? kGB : 128;
+}
 }  // namespace
 
 size_t lmhead_ws_bytes(int64_t M, int H, int V, int dtype) {
-  (void)H;
-  (void)dtype;
-  const int n_vt = (V + tile_bv(M) - 1) / tile_bv(M);
+  const int n_vt = (V + tile_bv(M, H, V, dtype) - 1) / tile_bv(M, H, V, dtype);
   return align_up(static_cast<size_t>(M) * n_vt * sizeof(float4), 256);
 }
 
 hipError_t launch_lmhead(const void* X, int64_t M, int H, const void* W, int V, int dtype,
                          float* conf, int32_t* argmax, float* lse, void* ws, hipStream_t st) {
-  const int n_vt = (V + tile_bv(M) - 1) / tile_bv(M);
+  const int n_vt = (V + tile_bv(M, H, V, dtype) - 1) / tile_bv(M, H, V, dtype);
   float4* part = static_cast<float4*>(ws);
   hipError_t e;
-  if (dtype == 1)
+  if (gemm_path(M, H, V, dtype)) {
+    const int n_mt = static_cast<int>((M + kGB - 1) / kGB);
+    const int per_xcd = (n_vt * n_mt + kXcds - 1) / kXcds;
+    lmhead_gemm_kernel<<<dim3(per_xcd * kXcds), dim3(kGThreads), 0, st>>>(
+        static_cast<const uint16_t*>(X), M, H, static_cast<const uint16_t*>(W), V, part, n_vt,
+        n_mt, per_xcd);
+    e = hipGetLastError();
+  } else if (dtype == 1)
     e = small_m(M) ? run_tiles<BF16, 4, 1, 1, 1>(X, M, H, W, V, part, n_vt, st)
                    : run_tiles<BF16, 2, 2, 2, 2>(X, M, H, W, V, part, n_vt, st);
   else
