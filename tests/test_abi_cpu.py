@@ -56,7 +56,8 @@ def test_plan_keep():
 
 
 def test_workspace_queries_are_host_only():
-    assert sprint.lmhead_confidence_ws(4096, 2048, 32768, sprint.BF16) >= 4096 * 256 * 16
+    # at least one 16-byte partial per row and vocabulary tile of at most 256 entries
+    assert sprint.lmhead_confidence_ws(4096, 2048, 32768, sprint.BF16) >= 4096 * 128 * 16
     assert sprint.sprint_score_ws(4096, 1) > 0
     assert sprint.sprint_prune_kv_ws(4096, 1) > 0
     assert sprint.block_attend_ws(1, 32, 16, 4, 128, 4096, 1) > 0
