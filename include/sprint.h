@@ -140,7 +140,7 @@ int sprint_prune_kv(const float* score, const uint8_t* modality, const int32_t* 
  *          (full cache, or the pruned cache of sprint_prune_kv)
  *   max_kv host upper bound on any sequence's cache length (sizes the KV split)
  *   Kb, Vb [nseq, Lq, Hkv, D] dtype, or both NULL for prefix-only attention
- *   scale  usually 1/sqrt(D)
+ *   scale  softmax scale, finite and > 0 (usually 1/sqrt(D))
  *   O      [nseq, Lq, Hq, D] dtype out (bf16 rounded to nearest even)
  * Supports D in {64, 128}, Hq % Hkv == 0, (Hq/Hkv)*Lq <= 256, Lq <= 64.
  * Every (sequence) must have at least one key (cache length + block >= 1).

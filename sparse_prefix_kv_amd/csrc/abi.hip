@@ -153,7 +153,8 @@ static int attend_shape_status(int32_t nseq, int32_t Lq, int32_t Hq, int32_t Hkv
 size_t block_attend_ws(int32_t nseq, int32_t Lq, int32_t Hq, int32_t Hkv, int32_t D,
                        int32_t max_kv, int32_t has_block) {
   if (attend_shape_status(nseq, Lq, Hq, Hkv, D, max_kv) != SPRINT_OK) return 0;
-  return attend_plan(nseq, Lq, Hq, Hkv, D, max_kv, has_block, SPRINT_BF16).ws_bytes;
+  // fp32 partials are the larger case; a bf16 call needs no more than this
+  return attend_plan(nseq, Lq, Hq, Hkv, D, max_kv, has_block, SPRINT_F32).ws_bytes;
 }
 
 int block_attend(const void* Q, int32_t nseq, int32_t Lq, int32_t Hq, const void* Kp,
@@ -163,17 +164,23 @@ int block_attend(const void* Q, int32_t nseq, int32_t Lq, int32_t Hq, const void
   if (!dtype_ok(dtype)) return SPRINT_EINVAL;
   const int ss = attend_shape_status(nseq, Lq, Hq, Hkv, D, max_kv);
   if (ss != SPRINT_OK) return ss;
-  if (total_kv < 0 || total_kv > INT32_MAX || !isfinite(scale)) return SPRINT_EINVAL;
+  if (total_kv < 0 || total_kv > INT32_MAX || !isfinite(scale) || !(scale > 0.f))
+    return SPRINT_EINVAL;
   if (!dev16(Q) || !dev16(O) || !dev4(cu_kv)) return SPRINT_EINVAL;
   if ((Kb == nullptr) != (Vb == nullptr)) return SPRINT_EINVAL;
   if (Kb != nullptr && (!dev16(Kb) || !dev16(Vb))) return SPRINT_EINVAL;
   if (Kb == nullptr && max_kv < 1) return SPRINT_EINVAL;  // no keys at all
   if (total_kv > 0 && (!dev16(Kp) || !dev16(Vp))) return SPRINT_EINVAL;
+  // K/V are addressed through 32-bit buffer descriptors
+  const int64_t row_bytes = static_cast<int64_t>(Hkv) * D * (dtype == SPRINT_BF16 ? 2 : 4);
+  if (total_kv * row_bytes >= (int64_t(1) << 31) ||
+      static_cast<int64_t>(nseq) * Lq * row_bytes >= (int64_t(1) << 31))
+    return SPRINT_EUNSUPPORTED;
   const AttnPlan plan = attend_plan(nseq, Lq, Hq, Hkv, D, max_kv, Kb != nullptr, dtype);
   const int st = check_ws(ws, ws_bytes, plan.ws_bytes);
   if (st != SPRINT_OK) return st;
-  return status_of(launch_attend(Q, nseq, Lq, Hq, Kp, Vp, cu_kv, Kb, Vb, Hkv, D, scale, dtype, O,
-                                 plan, ws, as_stream(stream)));
+  return status_of(launch_attend(Q, nseq, Lq, Hq, Kp, Vp, cu_kv, total_kv, Kb, Vb, Hkv, D, scale,
+                                 dtype, O, plan, ws, as_stream(stream)));
 }
 
 // ---------------------------------------------------------------- unmask

@@ -5,20 +5,33 @@
 // floor(h*Hkv/Hq).
 //
 // Work decomposition (split-KV, flash-decoding style):
-//   grid = (splits, Hkv, nseq); a block owns one KV head of one sequence and
-//   one contiguous key range, and ALL (Hq/Hkv)*Lq query rows that read that
-//   head, so every K/V byte is fetched from HBM once per step.  Each wave
-//   owns 32 query rows.
-// Per 32-key tile, staged through LDS:
-//   S^T = K Q^T on bf16 MFMA 32x32x16 (A = key rows from LDS, B = the wave's
+//   a block owns one KV head of one sequence and one contiguous key range,
+//   and ALL R = (Hq/Hkv)*Lq query rows that read that head, as R/32 waves of
+//   32 rows.  Every K/V byte is fetched once per step and shared through LDS.
+//   The block's own K/V (the block keys) are the last tiles of the last range.
+// K/V tiles of 32 keys arrive by buffer loads straight into LDS
+//   (buffer_load_dwordx4 ... lds) into a ring of four stages, three tiles
+//   ahead of the one being used.  The stages are distinct LDS arrays and the
+//   loop is unrolled by four, so the compiler can see that reads of one stage
+//   do not alias loads into another; each wave waits (vmcnt) for its own
+//   loads of a stage, then a plain s_barrier (no fence, which would drain
+//   every outstanding load) publishes it.
+// Per tile and wave:
+//   S^T = K Q^T on MFMA 32x32x16 (A = key rows from LDS, B = the wave's
 //   queries held in registers).  The accumulator gives each lane one query
 //   column and 16 keys, so the online-softmax max needs one cross-half swap
 //   and the row sum stays lane-local.
 //   O^T += V^T P^T with the probabilities taken straight from the S^T
-//   accumulator as the B operand (same lane/key slots, no shuffle); the
-//   per-query rescale is lane-local too.
-// Each split writes (o, m, l) partials in fp32 (m in log2 units); the combine
-// kernel merges them and rounds O to the output dtype.
+//   accumulator as the B operand.  For bf16 the V^T operand comes from the
+//   natural [key][d] layout through transposing LDS reads (ds_read_b64_tr_b16).
+// LDS layouts are XOR-swizzled per 16-byte chunk (DMA writes are contiguous,
+//   so no padding): K chunk c of row r sits in slot c ^ f(r) so the sixteen
+//   rows of a ds_read_b128 pass cover all banks; bf16 V chunk c sits in slot
+//   c ^ 4*(r & 3) (c ^ 4*((r >> 1) & 1) for 128-byte rows) so the four rows of
+//   a transposing-read pass land on disjoint banks.
+// A single key range writes O directly; otherwise each wave writes its rows'
+//   partial (o / l in fp16 for bf16 inputs, fp32 otherwise, plus m and l in
+//   log2 units) and a combine kernel merges the ranges.
 #include <math.h>
 
 #include "sprint_device.hpp"
@@ -27,7 +40,11 @@
 namespace sprint {
 namespace {
 
-constexpr int kKT = 32;  // keys per LDS tile
+constexpr int kKT = 32;       // keys per tile
+constexpr int kStages = 4;    // LDS ring depth
+
+typedef _Float16 half_t;
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 struct AttnArgs {
   const char* Q;
@@ -37,10 +54,47 @@ struct AttnArgs {
   const char* Kb;
   const char* Vb;
   char* O;
-  float* part_o;   // [nseq*Hkv*n_splits*R, D]
-  float* part_ml;  // [nseq*Hkv*n_splits*R, 2]
-  int nseq, Lq, Hq, Hkv, G, R, n_splits, kps, has_block;
+  void* part_o;    // [nseq*Hkv*n_splits*R, D] fp16 (bf16 inputs) or fp32, normalized by l
+  float* part_ml;  // [nseq*Hkv*n_splits*R, 2]  (m in log2 units, l)
+  int nseq, Lq, Hq, Hkv, G, R, n_splits, kps, has_block, n_rg;
+  int64_t total_kv;
   float scale_log2;
+};
+
+__device__ __forceinline__ f32x16 mma(const bf16x8& a, const bf16x8& b, f32x16 c) {
+  return mma32_k16(a, b, c);
+}
+struct F8 {
+  float v[8];
+};
+__device__ __forceinline__ f32x16 mma(const F8& a, const F8& b, f32x16 c) {
+  return mma32_k16(a.v, b.v, c);
+}
+
+#define SPRINT_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt immediate: at most n vector-memory ops pending, lgkm unrestricted
+constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Geometry of one tile for element type T and head dim D.
+template <typename T, int D>
+struct TileGeo {
+  using S = typename T::storage;
+  static constexpr bool kBf16 = sizeof(S) == 2;
+  static constexpr int kRowBytes = D * static_cast<int>(sizeof(S));
+  static constexpr int kChunks = kRowBytes / 16;              // 16-byte chunks per row
+  static constexpr int kTileBytes = kKT * kRowBytes;
+  static constexpr int kInstr = kTileBytes / 1024;            // 1 KB DMA instructions per tile
+  static constexpr int kRowsPerInstr = 1024 / kRowBytes;
+  // K: a ds_read_b128 pass reads 16 consecutive rows at one chunk; rows of
+  // 256+ bytes start on bank 0, 128-byte rows alternate halves
+  __host__ __device__ static constexpr int k_swz(int r) {
+    return kChunks >= 16 ? (r & 15) : ((r >> 1) & (kChunks - 1));
+  }
+  // V (bf16 only): a transposing b64 pass reads 4 consecutive rows at 4 chunks
+  __host__ __device__ static constexpr int v_swz(int r) {
+    return kChunks >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+  }
 };
 
 template <typename T>
@@ -48,7 +102,11 @@ struct Frag;
 template <>
 struct Frag<BF16> {
   using type = bf16x8;
-  __device__ static type load(const uint16_t* p) { return as_bf16x8(ld16(p)); }
+  // 8 consecutive elements starting at element e (multiple of 8) of a row
+  // whose chunks are swizzled by `sw`
+  __device__ static type load_row(const uint16_t* row, int e, int sw) {
+    return as_bf16x8(ld16(row + (((e >> 3) ^ sw) << 3)));
+  }
   __device__ static type zero() { return as_bf16x8(u32x4{0u, 0u, 0u, 0u}); }
   __device__ static type from8(const float (&x)[8]) {
     u32x4 u;
@@ -58,24 +116,15 @@ struct Frag<BF16> {
     u[3] = pack_bf16x2(x[6], x[7]);
     return as_bf16x8(u);
   }
-  __device__ static type gather8(const uint16_t* base, const int (&off)[8]) {
-    u32x4 u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      u[i] = static_cast<uint32_t>(base[off[2 * i]]) |
-             (static_cast<uint32_t>(base[off[2 * i + 1]]) << 16);
-    return as_bf16x8(u);
-  }
-};
-struct F8 {
-  float v[8];
+  __device__ static type qload(const uint16_t* p) { return as_bf16x8(ld16(p)); }
 };
 template <>
 struct Frag<F32> {
   using type = F8;
-  __device__ static type load(const float* p) {
+  __device__ static type load_row(const float* row, int e, int sw) {
     type r;
-    const u32x4 a = ld16(p), b = ld16(p + 4);
+    const u32x4 a = ld16(row + (((e >> 2) ^ sw) << 2));
+    const u32x4 b = ld16(row + ((((e >> 2) + 1) ^ sw) << 2));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       r.v[i] = __uint_as_float(a[i]);
@@ -95,64 +144,124 @@ struct Frag<F32> {
     for (int i = 0; i < 8; ++i) r.v[i] = x[i];
     return r;
   }
-  __device__ static type gather8(const float* base, const int (&off)[8]) {
+  __device__ static type qload(const float* p) {
     type r;
+    const u32x4 a = ld16(p), b = ld16(p + 4);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r.v[i] = base[off[i]];
+    for (int i = 0; i < 4; ++i) {
+      r.v[i] = __uint_as_float(a[i]);
+      r.v[4 + i] = __uint_as_float(b[i]);
+    }
     return r;
   }
 };
 
-__device__ __forceinline__ f32x16 mma(const bf16x8& a, const bf16x8& b, f32x16 c) {
-  return mma32_k16(a, b, c);
-}
-__device__ __forceinline__ f32x16 mma(const F8& a, const F8& b, f32x16 c) {
-  return mma32_k16(a.v, b.v, c);
+// DMA of one tile (K or V rows) into a stage: this wave's instructions
+// j = wave, wave + NW, ... (clamped to the last one: a repeat rewrites the
+// same bytes).  Lane L of instruction j fills LDS bytes 1024*j + 16*L.
+// `voff[p]` is that lane's byte offset within the tile (loop invariant),
+// `soff` the tile's uniform offset.
+__device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t rs, uint32_t soff,
+                                         const uint32_t* voff, char* stage, int wave, int nw,
+                                         int np, int ni) {
+#pragma unroll
+  for (int p = 0; p < np; ++p) {
+    const int j = wave + nw * p < ni ? wave + nw * p : ni - 1;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, SPRINT_LDS(stage + j * 1024), 16, voff[p], soff,
+                                             0, 0);
+  }
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(512) void attend_split_kernel(AttnArgs args) {
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void attend_split_kernel(AttnArgs args) {
   using S = typename T::storage;
   using FR = Frag<T>;
-  constexpr int kPad = 16 / sizeof(S);
-  constexpr int kRow = D + kPad;                     // LDS row pitch (elements)
-  constexpr int kVpr = D * static_cast<int>(sizeof(S)) / 16;  // 16-byte vectors per row
-  constexpr int kEpv = 16 / sizeof(S);               // elements per vector
-  __shared__ __align__(16) S sK[kKT * kRow];
-  __shared__ __align__(16) S sV[kKT * kRow];
+  using GEO = TileGeo<T, D>;
+  constexpr bool kBf16 = GEO::kBf16;
+  constexpr int kNI = GEO::kInstr;
+  constexpr int kP = (kNI + NW - 1) / NW;                // DMA instructions per wave per tensor
+  constexpr int kStageBytes = 2 * GEO::kTileBytes;       // K tile then V tile
+  __shared__ __align__(16) char st0[kStageBytes];
+  __shared__ __align__(16) char st1[kStageBytes];
+  __shared__ __align__(16) char st2[kStageBytes];
+  __shared__ __align__(16) char st3[kStageBytes];
 
-  const int split = blockIdx.x, g = blockIdx.y, seq = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int split = blockIdx.x % args.n_splits;
+  const int g = (blockIdx.x / args.n_splits) % args.Hkv;
+  const int seq = blockIdx.x / (args.n_splits * args.Hkv);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int q = lane & 31, hh = lane >> 5;
+
   const int64_t kv_begin = args.cu_kv[seq];
   const int kv_len = args.cu_kv[seq + 1] - args.cu_kv[seq];
   const int n_keys = kv_len + (args.has_block ? args.Lq : 0);
-  const int k0 = split * args.kps;
+  const int k0 = min(n_keys, split * args.kps);
   const int k1 = min(n_keys, k0 + args.kps);
-  const int64_t pbase =
-      ((static_cast<int64_t>(seq) * args.Hkv + g) * args.n_splits + split) * args.R;
+  // tiles: the range's prefix keys [pk0, pk1), then its block keys [bk0, bk1)
+  const int pk0 = min(k0, kv_len), pk1 = min(k1, kv_len);
+  const int bk0 = max(k0, kv_len) - kv_len, bk1 = max(k1, kv_len) - kv_len;
+  const int n_ptiles = (pk1 - pk0 + kKT - 1) / kKT;
+  const int n_btiles = (bk1 - bk0 + kKT - 1) / kKT;
+  const int nt = n_ptiles + n_btiles;
+
   const int rho = wave * 32 + q;
   const bool row_ok = rho < args.R;
-
-  if (k0 >= k1) {  // empty split: the combine skips it
-    if (row_ok && hh == 0) {
-      args.part_ml[(pbase + rho) * 2 + 0] = -INFINITY;
-      args.part_ml[(pbase + rho) * 2 + 1] = 0.f;
-    }
-    return;
-  }
+  const int gi = row_ok ? rho / args.Lq : 0, qi = row_ok ? rho % args.Lq : 0;
+  const int head = g * args.G + gi;
 
   // Query fragments: lane (q, half) holds row rho, dims [16*ds + 8*half, +8).
   typename FR::type qf[D / 16];
   {
-    const int gi = row_ok ? rho / args.Lq : 0, qi = row_ok ? rho % args.Lq : 0;
-    const int head = g * args.G + gi;
     const S* qrow = reinterpret_cast<const S*>(args.Q) +
                     ((static_cast<int64_t>(seq) * args.Lq + qi) * args.Hq + head) * D;
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds)
-      qf[ds] = row_ok ? FR::load(qrow + 16 * ds + 8 * hh) : FR::zero();
+      qf[ds] = row_ok ? FR::qload(qrow + 16 * ds + 8 * hh) : FR::zero();
   }
+
+  // Buffer descriptors over the prefix cache and the block's own K/V; reads
+  // past either return zeros.
+  const int64_t row_stride = static_cast<int64_t>(args.Hkv) * GEO::kRowBytes;
+  const int pbytes = static_cast<int>(args.total_kv * row_stride);
+  const int bbytes = args.has_block
+                         ? static_cast<int>(static_cast<int64_t>(args.nseq) * args.Lq * row_stride)
+                         : 0;
+  const __amdgpu_buffer_rsrc_t rKp =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(args.Kp), 0, pbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rVp =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(args.Vp), 0, pbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rKb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(args.Kb), 0, bbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rVb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(args.Vb), 0, bbytes, 0x00020000);
+  // per-lane byte offsets inside a tile: row * stride + swizzled chunk
+  uint32_t vK[kP], vV[kP];
+#pragma unroll
+  for (int p = 0; p < kP; ++p) {
+    const int j = wave + NW * p < kNI ? wave + NW * p : kNI - 1;
+    const int row = j * GEO::kRowsPerInstr + lane / GEO::kChunks;
+    const int slot = lane % GEO::kChunks;
+    const int ck = slot ^ GEO::k_swz(row);
+    const int cv = kBf16 ? (slot ^ GEO::v_swz(row)) : ck;
+    vK[p] = static_cast<uint32_t>(row * row_stride + ck * 16);
+    vV[p] = static_cast<uint32_t>(row * row_stride + cv * 16);
+  }
+  const uint32_t head_off = static_cast<uint32_t>(g * GEO::kRowBytes);
+  auto issue = [&](int t, char* stage) {
+    if (t < n_ptiles) {
+      const uint32_t so =
+          static_cast<uint32_t>((kv_begin + pk0 + t * kKT) * row_stride) + head_off;
+      tile_dma(rKp, so, vK, stage, wave, NW, kP, kNI);
+      tile_dma(rVp, so, vV, stage + GEO::kTileBytes, wave, NW, kP, kNI);
+    } else {
+      const uint32_t so = static_cast<uint32_t>(
+                              (static_cast<int64_t>(seq) * args.Lq + bk0 + (t - n_ptiles) * kKT) *
+                              row_stride) + head_off;
+      tile_dma(rKb, so, vK, stage, wave, NW, kP, kNI);
+      tile_dma(rVb, so, vV, stage + GEO::kTileBytes, wave, NW, kP, kNI);
+    }
+  };
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 acc_o[D / 32];
@@ -161,151 +270,248 @@ __global__ __launch_bounds__(512) void attend_split_kernel(AttnArgs args) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[mt][r] = 0.f;
 
-  const int64_t kv_stride = static_cast<int64_t>(args.Hkv) * D;  // elements per cache row
-  for (int t0 = k0; t0 < k1; t0 += kKT) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kKT * kVpr; idx += blockDim.x) {
-      const int r = idx / kVpr, v = idx - r * kVpr;
-      const int key = t0 + r;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (key < k1) {
-        int64_t off;
-        const char *kb, *vb;
-        if (key < kv_len) {
-          off = ((kv_begin + key) * kv_stride + static_cast<int64_t>(g) * D) * sizeof(S);
-          kb = args.Kp;
-          vb = args.Vp;
-        } else {
-          off = (((static_cast<int64_t>(seq) * args.Lq + (key - kv_len)) * args.Hkv + g) * D) *
-                sizeof(S);
-          kb = args.Kb;
-          vb = args.Vb;
-        }
-        kv = ld16(kb + off + v * 16);
-        vv = ld16(vb + off + v * 16);
-      }
-      st16(&sK[r * kRow + v * kEpv], kv);
-      st16(&sV[r * kRow + v * kEpv], vv);
-    }
-    __syncthreads();
+  // K fragment reads: row q, chunk (16*ds + 8*hh) / chunk-elements
+  const int ksw = GEO::k_swz(q);
+  // bf16 V transposed reads: source lane i = lane & 15 of group G = lane >> 4
+  // points at key 4*hh + (i >> 2), column 16*(G & 1) + 4*(i & 3) of a 32-column
+  // slab; lane j of the group then receives column j of those four keys.
+  const int vrow = 4 * hh + ((lane & 15) >> 2);
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    // S^T[key][query] for the 32 keys of the tile.
+  auto compute = [&](const char* stage, int t) {
+    const S* sK = reinterpret_cast<const S*>(stage);
+    const S* sV = reinterpret_cast<const S*>(stage + GEO::kTileBytes);
+    const int valid = t < n_ptiles ? min(kKT, pk1 - pk0 - t * kKT)
+                                   : min(kKT, bk1 - bk0 - (t - n_ptiles) * kKT);
+    // S^T[key][query]
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    const S* krow = sK + q * D;
 #pragma unroll
-    for (int ds = 0; ds < D / 16; ++ds) {
-      const typename FR::type a = FR::load(&sK[q * kRow + 16 * ds + 8 * hh]);
-      s = mma(a, qf[ds], s);
-    }
-    float tmax = -INFINITY;
+    for (int ds = 0; ds < D / 16; ++ds)
+      s = mma(FR::load_row(krow, 16 * ds + 8 * hh, ksw), qf[ds], s);
+    // online softmax in log2 units: m is kept scaled by scale*log2(e) (> 0)
+    const float c = args.scale_log2;
+    if (valid < kKT) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = t0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      const float x = key < k1 ? s[r] * args.scale_log2 : -INFINITY;
-      s[r] = x;
-      tmax = fmaxf(tmax, x);
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * hh + (r & 3) >= valid) s[r] = -INFINITY;
     }
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+    float tmax = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
+    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32)) * c;
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
+    if (__ballot(m_new > m_run)) {       // rescale only when some lane's maximum moved
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
+    }
+    m_run = m_new;
     float p[16];
-    float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      p[r] = exp2f(s[r] - m_new);
-      psum += p[r];
+      p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -m_new));
+      l_run += p[r];
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
-
     // O^T[d][query] += sum_key V[key][d] P[query][key]
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      float pk[8];
+      float pk8[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pk[e] = p[8 * ks + e];
-      const typename FR::type b = FR::from8(pk);
-      int off[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) off[e] = (16 * ks + 8 * (e >> 2) + 4 * hh + (e & 3)) * kRow + q;
+      for (int e = 0; e < 8; ++e) pk8[e] = p[8 * ks + e];
+      const typename FR::type bq = FR::from8(pk8);
 #pragma unroll
       for (int mt = 0; mt < D / 32; ++mt) {
-        const typename FR::type a = FR::gather8(&sV[32 * mt], off);
-        acc_o[mt] = mma(a, b, acc_o[mt]);
+        typename FR::type a;
+        if constexpr (kBf16) {
+          typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+          const int r0 = 16 * ks + vrow, r1 = r0 + 8;
+          const int col = 32 * mt + vcol;
+          const uint16_t* p0 = sV + r0 * D + ((((col >> 3) ^ GEO::v_swz(r0)) << 3) | (col & 7));
+          const uint16_t* p1 = sV + r1 * D + ((((col >> 3) ^ GEO::v_swz(r1)) << 3) | (col & 7));
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(p0));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(p1));
+          a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = 16 * ks + 8 * (e >> 2) + 4 * hh + (e & 3);
+            const int d = 32 * mt + q;
+            a.v[e] = sV[key * D + ((((d >> 2) ^ GEO::k_swz(key)) << 2) | (d & 3))];
+          }
+        }
+        acc_o[mt] = mma(a, bq, acc_o[mt]);
       }
     }
+  };
+
+  // prologue: three tiles in flight
+  if (0 < nt) issue(0, st0);
+  if (1 < nt) issue(1, st1);
+  if (2 < nt) issue(2, st2);
+  constexpr int kPer = 2 * kP;   // vector-memory instructions per wave per tile
+#define SPRINT_ATT_STEP(CUR, NXT3, U)                                                     \
+  {                                                                                       \
+    const int t = tb + (U);                                                               \
+    if (t < nt) {                                                                         \
+      if (t + 2 < nt)                                                                     \
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * kPer));                                \
+      else if (t + 1 < nt)                                                                \
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(kPer));                                    \
+      else                                                                                \
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));                                       \
+      __builtin_amdgcn_s_barrier();                                                       \
+      if (t + 3 < nt) issue(t + 3, NXT3);                                                 \
+      compute(CUR, t);                                                                    \
+    }                                                                                     \
   }
+  for (int tb = 0; tb < nt; tb += kStages) {
+    SPRINT_ATT_STEP(st0, st3, 0)
+    SPRINT_ATT_STEP(st1, st0, 1)
+    SPRINT_ATT_STEP(st2, st1, 2)
+    SPRINT_ATT_STEP(st3, st2, 3)
+  }
+#undef SPRINT_ATT_STEP
 
   const float l_tot = l_run + shfl_xor_f(l_run, 32);
-  if (row_ok) {
-    float* po = args.part_o + (pbase + rho) * D;
+  if (!row_ok) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (args.n_splits == 1) {
+    // the block saw every key: write O directly
+    S* out = reinterpret_cast<S*>(args.O) +
+             ((static_cast<int64_t>(seq) * args.Lq + qi) * args.Hq + head) * D;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = 32 * mt + 8 * r4 + 4 * hh;
-        f32x4 v = {acc_o[mt][4 * r4 + 0], acc_o[mt][4 * r4 + 1], acc_o[mt][4 * r4 + 2],
-                   acc_o[mt][4 * r4 + 3]};
-        *reinterpret_cast<f32x4*>(po + d) = v;
+      for (int r = 0; r < 16; ++r)
+        out[32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3)] = T::from_f32(acc_o[mt][r] * inv);
+    return;
+  }
+  const int64_t prow =
+      ((static_cast<int64_t>(seq) * args.Hkv + g) * args.n_splits + split) * args.R + rho;
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * mt + 8 * r4 + 4 * hh;
+      if constexpr (kBf16) {
+        f16x4 v = {static_cast<half_t>(acc_o[mt][4 * r4 + 0] * inv),
+                   static_cast<half_t>(acc_o[mt][4 * r4 + 1] * inv),
+                   static_cast<half_t>(acc_o[mt][4 * r4 + 2] * inv),
+                   static_cast<half_t>(acc_o[mt][4 * r4 + 3] * inv)};
+        *reinterpret_cast<f16x4*>(static_cast<half_t*>(args.part_o) + prow * D + d) = v;
+      } else {
+        f32x4 v = {acc_o[mt][4 * r4 + 0] * inv, acc_o[mt][4 * r4 + 1] * inv,
+                   acc_o[mt][4 * r4 + 2] * inv, acc_o[mt][4 * r4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(static_cast<float*>(args.part_o) + prow * D + d) = v;
       }
-    if (hh == 0) {
-      args.part_ml[(pbase + rho) * 2 + 0] = m_run;
-      args.part_ml[(pbase + rho) * 2 + 1] = l_tot;
     }
+  if (hh == 0) {
+    args.part_ml[prow * 2 + 0] = m_run;
+    args.part_ml[prow * 2 + 1] = l_tot;
   }
 }
 
-// One wave per output row (sequence, query, head).
+// Combine the key ranges: a block per (sequence, KV head, row group, 32-column
+// slab).  Eight lanes per row fold (m, l) over the ranges in parallel; then
+// every thread accumulates four columns of its row across the ranges with the
+// weights l_s 2^(m_s - m), four ranges per batch of loads.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttnArgs args) {
   using S = typename T::storage;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + wave;
-  const int64_t total_rows = static_cast<int64_t>(args.nseq) * args.Lq * args.Hq;
-  if (row >= total_rows) return;
-  const int head = static_cast<int>(row % args.Hq);
-  const int qi = static_cast<int>((row / args.Hq) % args.Lq);
-  const int seq = static_cast<int>(row / (static_cast<int64_t>(args.Hq) * args.Lq));
-  const int g = head / args.G, gi = head % args.G;
-  const int rho = gi * args.Lq + qi;
-  const int64_t base = (static_cast<int64_t>(seq) * args.Hkv + g) * args.n_splits;
+  constexpr bool kBf16 = sizeof(S) == 2;
+  constexpr int kSlabs = D / 32;
+  const int slab = blockIdx.x % kSlabs;
+  const int rest = blockIdx.x / kSlabs;
+  const int rg = rest % args.n_rg;
+  const int g = (rest / args.n_rg) % args.Hkv;
+  const int seq = rest / (args.n_rg * args.Hkv);
+  const int row = threadIdx.x >> 3, sub = threadIdx.x & 7;
+  const int rr = rg * 32 + row;
+  const bool ok = rr < args.R;
+  const int64_t ubase = (static_cast<int64_t>(seq) * args.Hkv + g) * args.n_splits;
+  const int64_t rstride = static_cast<int64_t>(args.R);
+  const float* pml = args.part_ml + (ubase * rstride + (ok ? rr : 0)) * 2;
   float m = -INFINITY;
-  for (int sp = 0; sp < args.n_splits; ++sp)
-    m = fmaxf(m, args.part_ml[((base + sp) * args.R + rho) * 2]);
-  constexpr int kPer = D / 64;
-  float o[kPer];
+  for (int sp = sub; sp < args.n_splits; sp += 8) m = fmaxf(m, pml[sp * rstride * 2]);
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) o[j] = 0.f;
+  for (int o = 4; o >= 1; o >>= 1) m = fmaxf(m, shfl_xor_f(m, o));
   float l = 0.f;
-  for (int sp = 0; sp < args.n_splits; ++sp) {
-    const int64_t pr = (base + sp) * args.R + rho;
-    const float ms = args.part_ml[pr * 2];
-    if (ms == -INFINITY) continue;
-    const float w = exp2f(ms - m);
-    l += args.part_ml[pr * 2 + 1] * w;
+  for (int sp = sub; sp < args.n_splits; sp += 8) {
+    const float ms = pml[sp * rstride * 2];
+    l += ms == -INFINITY ? 0.f : pml[sp * rstride * 2 + 1] * exp2f(ms - m);
+  }
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) o[j] += w * args.part_o[pr * D + lane + 64 * j];
+  for (int o = 4; o >= 1; o >>= 1) l += shfl_xor_f(l, o);
+  if (!ok) return;
+  const int d = slab * 32 + sub * 4;
+  const int64_t pofs = (ubase * rstride + rr) * D + d;
+  auto load4 = [&](int sp) -> f32x4 {
+    if constexpr (kBf16) {
+      const f16x4 h = *reinterpret_cast<const f16x4*>(static_cast<const half_t*>(args.part_o) +
+                                                      pofs + sp * rstride * D);
+      return f32x4{static_cast<float>(h[0]), static_cast<float>(h[1]), static_cast<float>(h[2]),
+                   static_cast<float>(h[3])};
+    } else {
+      return *reinterpret_cast<const f32x4*>(static_cast<const float*>(args.part_o) + pofs +
+                                             sp * rstride * D);
+    }
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int sp = 0;
+  for (; sp + 4 <= args.n_splits; sp += 4) {
+    float ms[4], ls[4];
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ms[u] = pml[(sp + u) * rstride * 2];
+      ls[u] = pml[(sp + u) * rstride * 2 + 1];
+      v[u] = load4(sp + u);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc += (ms[u] == -INFINITY ? 0.f : ls[u] * exp2f(ms[u] - m)) * v[u];
+  }
+  for (; sp < args.n_splits; ++sp) {
+    const float ms = pml[sp * rstride * 2];
+    const f32x4 v = load4(sp);
+    acc += (ms == -INFINITY ? 0.f : pml[sp * rstride * 2 + 1] * exp2f(ms - m)) * v;
   }
   const float inv = 1.f / l;
-  S* out = reinterpret_cast<S*>(args.O) + row * D;
+  const int gi = rr / args.Lq, qi = rr % args.Lq;
+  const int head = g * args.G + gi;
+  S* out = reinterpret_cast<S*>(args.O) +
+           ((static_cast<int64_t>(seq) * args.Lq + qi) * args.Hq + head) * D + d;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) out[lane + 64 * j] = T::from_f32(o[j] * inv);
+  for (int c = 0; c < 4; ++c) out[c] = T::from_f32(acc[c] * inv);
+}
+
+template <typename T, int D, int NW>
+hipError_t launch_split(const AttnArgs& a, hipStream_t st) {
+  const int blocks = a.nseq * a.Hkv * a.n_splits;
+  attend_split_kernel<T, D, NW><<<dim3(blocks), dim3(64 * NW), 0, st>>>(a);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
-  const int waves = (a.R + 31) / 32;
-  attend_split_kernel<T, D>
-      <<<dim3(a.n_splits, a.Hkv, a.nseq), dim3(64 * waves), 0, st>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t rows = static_cast<int64_t>(a.nseq) * a.Lq * a.Hq;
-  attend_combine_kernel<T, D><<<dim3((rows + 3) / 4), dim3(256), 0, st>>>(a);
+  hipError_t e;
+  if (a.n_rg <= 1)
+    e = launch_split<T, D, 1>(a, st);
+  else if (a.n_rg <= 2)
+    e = launch_split<T, D, 2>(a, st);
+  else if (a.n_rg <= 4)
+    e = launch_split<T, D, 4>(a, st);
+  else
+    e = launch_split<T, D, 8>(a, st);
+  if (e != hipSuccess || a.n_splits == 1) return e;
+  const int blocks = a.nseq * a.Hkv * a.n_rg * (D / 32);
+  attend_combine_kernel<T, D><<<dim3(blocks), dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -313,25 +519,28 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
 
 AttnPlan attend_plan(int nseq, int Lq, int Hq, int Hkv, int D, int max_kv, int has_block,
                      int dtype) {
-  (void)dtype;
   AttnPlan p;
   p.rows = (Hq / Hkv) * Lq;
   const int64_t n_keys = static_cast<int64_t>(max_kv) + (has_block ? Lq : 0);
   const int64_t units = static_cast<int64_t>(nseq) * Hkv;
-  // Largest key range per split that still gives >= 256 blocks; at least one tile.
-  int kps = 2048;
-  while (kps > kKT && units * ((n_keys + kps - 1) / kps) < 256) kps >>= 1;
+  // Keys per range: the largest power of two (at least one tile) that still
+  // gives >= 192 blocks, so most CUs stream a range.
+  int kps = 1 << 20;
+  while (kps > kKT && units * ((n_keys + kps - 1) / kps) < 192) kps >>= 1;
   p.kps = kps;
   p.n_splits = static_cast<int>(n_keys > 0 ? (n_keys + kps - 1) / kps : 1);
+  const size_t es = dtype == 1 ? 2 : 4;
   const size_t parts = static_cast<size_t>(units) * p.n_splits * p.rows;
-  p.ws_bytes = align_up(parts * D * sizeof(float), 256) + align_up(parts * 2 * sizeof(float), 256);
+  p.ws_bytes = p.n_splits == 1 ? 0
+                               : align_up(parts * D * es, 256) +
+                                     align_up(parts * 2 * sizeof(float), 256);
   return p;
 }
 
 hipError_t launch_attend(const void* Q, int nseq, int Lq, int Hq, const void* Kp, const void* Vp,
-                         const int32_t* cu_kv, const void* Kb, const void* Vb, int Hkv, int D,
-                         float scale, int dtype, void* O, const AttnPlan& plan, void* ws,
-                         hipStream_t st) {
+                         const int32_t* cu_kv, int64_t total_kv, const void* Kb, const void* Vb,
+                         int Hkv, int D, float scale, int dtype, void* O, const AttnPlan& plan,
+                         void* ws, hipStream_t st) {
   AttnArgs a;
   a.Q = static_cast<const char*>(Q);
   a.Kp = static_cast<const char*>(Kp);
@@ -340,10 +549,12 @@ hipError_t launch_attend(const void* Q, int nseq, int Lq, int Hq, const void* Kp
   a.Kb = static_cast<const char*>(Kb);
   a.Vb = static_cast<const char*>(Vb);
   a.O = static_cast<char*>(O);
+  const size_t es = dtype == 1 ? 2 : 4;
   const size_t parts = static_cast<size_t>(nseq) * Hkv * plan.n_splits * plan.rows;
-  a.part_o = static_cast<float*>(ws);
-  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                       align_up(parts * D * sizeof(float), 256));
+  a.part_o = ws;
+  a.part_ml = plan.n_splits == 1 ? nullptr
+                                 : reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                                            align_up(parts * D * es, 256));
   a.nseq = nseq;
   a.Lq = Lq;
   a.Hq = Hq;
@@ -353,6 +564,8 @@ hipError_t launch_attend(const void* Q, int nseq, int Lq, int Hq, const void* Kp
   a.n_splits = plan.n_splits;
   a.kps = plan.kps;
   a.has_block = (Kb != nullptr) ? 1 : 0;
+  a.n_rg = (plan.rows + 31) / 32;
+  a.total_kv = total_kv;
   a.scale_log2 = scale * kLog2e;
   if (dtype == 1) return D == 128 ? launch_typed<BF16, 128>(a, st) : launch_typed<BF16, 64>(a, st);
   return D == 128 ? launch_typed<F32, 128>(a, st) : launch_typed<F32, 64>(a, st);

@@ -34,9 +34,9 @@ struct AttnPlan {
 AttnPlan attend_plan(int nseq, int Lq, int Hq, int Hkv, int D, int max_kv, int has_block,
                      int dtype);
 hipError_t launch_attend(const void* Q, int nseq, int Lq, int Hq, const void* Kp, const void* Vp,
-                         const int32_t* cu_kv, const void* Kb, const void* Vb, int Hkv, int D,
-                         float scale, int dtype, void* O, const AttnPlan& plan, void* ws,
-                         hipStream_t st);
+                         const int32_t* cu_kv, int64_t total_kv, const void* Kb, const void* Vb,
+                         int Hkv, int D, float scale, int dtype, void* O, const AttnPlan& plan,
+                         void* ws, hipStream_t st);
 
 // ---- LM-head confidence (fused GEMM + streaming max / log-sum-exp, then merge)
 size_t lmhead_ws_bytes(int64_t M, int H, int V, int dtype);
