@@ -34,17 +34,20 @@
 //   log2 units) and a combine kernel merges the ranges.
 #include <math.h>
 
+#include <type_traits>
+
 #include "sprint_device.hpp"
 #include "sprint_internal.hpp"
 
 namespace sprint {
 namespace {
 
-constexpr int kKT = 32;       // keys per tile
+constexpr int kKT = 32;       // keys per MFMA tile (one S^T accumulator)
 constexpr int kStages = 4;    // LDS ring depth
 
 typedef _Float16 half_t;
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 struct AttnArgs {
   const char* Q;
@@ -73,17 +76,20 @@ __device__ __forceinline__ f32x16 mma(const F8& a, const F8& b, f32x16 c) {
 
 #define SPRINT_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-// s_waitcnt immediate: at most n vector-memory ops pending, lgkm unrestricted
-constexpr int vm_wait_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+// s_waitcnt immediate: at most n vector-memory ops pending (clamped to the
+// 6-bit field: waiting for fewer is always safe), lgkm unrestricted
+constexpr int vm_wait_imm(int n) {
+  return n > 63 ? vm_wait_imm(63) : (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
+}
 
-// Geometry of one tile for element type T and head dim D.
-template <typename T, int D>
+// Geometry of one pipeline stage (KS keys) for element type T and head dim D.
+template <typename T, int D, int KS>
 struct TileGeo {
   using S = typename T::storage;
   static constexpr bool kBf16 = sizeof(S) == 2;
   static constexpr int kRowBytes = D * static_cast<int>(sizeof(S));
   static constexpr int kChunks = kRowBytes / 16;              // 16-byte chunks per row
-  static constexpr int kTileBytes = kKT * kRowBytes;
+  static constexpr int kTileBytes = KS * kRowBytes;           // K (or V) rows of a stage
   static constexpr int kInstr = kTileBytes / 1024;            // 1 KB DMA instructions per tile
   static constexpr int kRowsPerInstr = 1024 / kRowBytes;
   // K: a ds_read_b128 pass reads 16 consecutive rows at one chunk; rows of
@@ -96,6 +102,19 @@ struct TileGeo {
     return kChunks >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
   }
 };
+
+// Max / sum of lanes q and q + 32 (gfx950 v_permlane32_swap: one VALU op
+// instead of an LDS permute).  Both lanes of a pair get the same value.
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <typename T>
 struct Frag;
@@ -168,15 +187,85 @@ __device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t rs, uint32_t sof
   for (int p = 0; p < np; ++p) {
     const int j = wave + nw * p < ni ? wave + nw * p : ni - 1;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, SPRINT_LDS(stage + j * 1024), 16, voff[p], soff,
-                                             0, 0);
+                                             0, kCpolNT);
   }
 }
 
-template <typename T, int D, int NW>
+// ---------------------------------------------------------------- output rows
+// A wave's 32 output rows leave through LDS: each lane stores its 4-column
+// groups of row q (XOR-swizzled 16-byte chunks), then every lane copies one
+// 16-byte chunk of a whole row, so global stores are full contiguous rows
+// instead of 8-byte pieces scattered over 32 rows.
+template <typename E>
+__device__ __forceinline__ E out_cvt(float x);
+template <>
+__device__ __forceinline__ uint16_t out_cvt<uint16_t>(float x) {   // bf16 bits
+  return f32_to_bf16(x);
+}
+template <>
+__device__ __forceinline__ half_t out_cvt<half_t>(float x) {
+  return static_cast<half_t>(x);
+}
+template <>
+__device__ __forceinline__ float out_cvt<float>(float x) {
+  return x;
+}
+
+template <typename E, int D>
+struct RowGeo {
+  static constexpr int kCE = 16 / static_cast<int>(sizeof(E));   // elements per chunk
+  static constexpr int kNC = D / kCE;                             // chunks per row
+  static constexpr int kSw = kNC >= 16 ? 15 : kNC - 1;
+  static constexpr int kRowBytes = D * static_cast<int>(sizeof(E));
+  static constexpr int kWaveBytes = 32 * kRowBytes;
+};
+
+template <typename E, int D>
+__device__ __forceinline__ void stage_rows(char* reg, const f32x16 (&acc)[D / 32], float inv,
+                                           int q, int hh) {
+  using G = RowGeo<E, D>;
+  char* row = reg + q * G::kRowBytes;
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * mt + 8 * r4 + 4 * hh;     // first of 4 consecutive columns
+      const int c = d / G::kCE, e = d % G::kCE;
+      char* dst = row + ((c ^ (q & G::kSw)) * 16) + e * static_cast<int>(sizeof(E));
+      if constexpr (sizeof(E) == 2) {
+        E v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = out_cvt<E>(acc[mt][4 * r4 + i] * inv);
+        *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, v);
+      } else {
+        *reinterpret_cast<f32x4*>(dst) =
+            f32x4{acc[mt][4 * r4] * inv, acc[mt][4 * r4 + 1] * inv, acc[mt][4 * r4 + 2] * inv,
+                  acc[mt][4 * r4 + 3] * inv};
+      }
+    }
+}
+
+// Copy the first `nrows` staged rows to global memory; row_ptr(r) gives the
+// destination of row r.
+template <typename E, int D, typename F>
+__device__ __forceinline__ void flush_rows(const char* reg, int lane, int nrows, F row_ptr) {
+  using G = RowGeo<E, D>;
+  constexpr int kRowsPer = 64 / G::kNC;
+  const int cc = lane % G::kNC, r0 = lane / G::kNC;
+#pragma unroll
+  for (int it = 0; it < 32 / kRowsPer; ++it) {
+    const int rr = it * kRowsPer + r0;
+    if (rr < nrows)
+      st16(row_ptr(rr) + cc * 16, ld16(reg + rr * G::kRowBytes + ((cc ^ (rr & G::kSw)) * 16)));
+  }
+}
+
+template <typename T, int D, int NW, int NSUB>
 __global__ __launch_bounds__(64 * NW) void attend_split_kernel(AttnArgs args) {
   using S = typename T::storage;
   using FR = Frag<T>;
-  using GEO = TileGeo<T, D>;
+  constexpr int KS = kKT * NSUB;                          // keys per pipeline stage
+  using GEO = TileGeo<T, D, KS>;
   constexpr bool kBf16 = GEO::kBf16;
   constexpr int kNI = GEO::kInstr;
   constexpr int kP = (kNI + NW - 1) / NW;                // DMA instructions per wave per tensor
@@ -201,8 +290,8 @@ __global__ __launch_bounds__(64 * NW) void attend_split_kernel(AttnArgs args) {
   // tiles: the range's prefix keys [pk0, pk1), then its block keys [bk0, bk1)
   const int pk0 = min(k0, kv_len), pk1 = min(k1, kv_len);
   const int bk0 = max(k0, kv_len) - kv_len, bk1 = max(k1, kv_len) - kv_len;
-  const int n_ptiles = (pk1 - pk0 + kKT - 1) / kKT;
-  const int n_btiles = (bk1 - bk0 + kKT - 1) / kKT;
+  const int n_ptiles = (pk1 - pk0 + KS - 1) / KS;
+  const int n_btiles = (bk1 - bk0 + KS - 1) / KS;
   const int nt = n_ptiles + n_btiles;
 
   const int rho = wave * 32 + q;
@@ -220,21 +309,16 @@ __global__ __launch_bounds__(64 * NW) void attend_split_kernel(AttnArgs args) {
       qf[ds] = row_ok ? FR::qload(qrow + 16 * ds + 8 * hh) : FR::zero();
   }
 
-  // Buffer descriptors over the prefix cache and the block's own K/V; reads
-  // past either return zeros.
+  // Buffer descriptors over the prefix cache or the block's own K/V (reads
+  // past either return zeros).  The descriptor of a tile is built from the
+  // selected base pointer and size, both wave-uniform scalars: selecting
+  // between two finished descriptors instead makes the compiler keep them in
+  // scratch memory and drain every outstanding load before each tile.
   const int64_t row_stride = static_cast<int64_t>(args.Hkv) * GEO::kRowBytes;
   const int pbytes = static_cast<int>(args.total_kv * row_stride);
   const int bbytes = args.has_block
                          ? static_cast<int>(static_cast<int64_t>(args.nseq) * args.Lq * row_stride)
                          : 0;
-  const __amdgpu_buffer_rsrc_t rKp =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(args.Kp), 0, pbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rVp =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(args.Vp), 0, pbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rKb =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(args.Kb), 0, bbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rVb =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(args.Vb), 0, bbytes, 0x00020000);
   // per-lane byte offsets inside a tile: row * stride + swizzled chunk
   uint32_t vK[kP], vV[kP];
 #pragma unroll
@@ -248,19 +332,22 @@ __global__ __launch_bounds__(64 * NW) void attend_split_kernel(AttnArgs args) {
     vV[p] = static_cast<uint32_t>(row * row_stride + cv * 16);
   }
   const uint32_t head_off = static_cast<uint32_t>(g * GEO::kRowBytes);
+  const uint32_t pre_base = static_cast<uint32_t>((kv_begin + pk0) * row_stride) + head_off;
+  const uint32_t blk_base =
+      static_cast<uint32_t>((static_cast<int64_t>(seq) * args.Lq + bk0) * row_stride) + head_off;
   auto issue = [&](int t, char* stage) {
-    if (t < n_ptiles) {
-      const uint32_t so =
-          static_cast<uint32_t>((kv_begin + pk0 + t * kKT) * row_stride) + head_off;
-      tile_dma(rKp, so, vK, stage, wave, NW, kP, kNI);
-      tile_dma(rVp, so, vV, stage + GEO::kTileBytes, wave, NW, kP, kNI);
-    } else {
-      const uint32_t so = static_cast<uint32_t>(
-                              (static_cast<int64_t>(seq) * args.Lq + bk0 + (t - n_ptiles) * kKT) *
-                              row_stride) + head_off;
-      tile_dma(rKb, so, vK, stage, wave, NW, kP, kNI);
-      tile_dma(rVb, so, vV, stage + GEO::kTileBytes, wave, NW, kP, kNI);
-    }
+    const bool pre = t < n_ptiles;
+    const char* kb = pre ? args.Kp : args.Kb;
+    const char* vb = pre ? args.Vp : args.Vb;
+    const int nb = pre ? pbytes : bbytes;
+    const uint32_t so = (pre ? pre_base : blk_base) +
+                        static_cast<uint32_t>((pre ? t : t - n_ptiles) * KS * row_stride);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kb), 0, nb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vb), 0, nb, 0x00020000);
+    tile_dma(rk, so, vK, stage, wave, NW, kP, kNI);
+    tile_dma(rv, so, vV, stage + GEO::kTileBytes, wave, NW, kP, kNI);
   };
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -278,30 +365,39 @@ __global__ __launch_bounds__(64 * NW) void attend_split_kernel(AttnArgs args) {
   const int vrow = 4 * hh + ((lane & 15) >> 2);
   const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
+  // One stage: NSUB independent 32-key S^T accumulators (their MFMA chains
+  // interleave), one softmax update over all NSUB*32 keys, then P V.
   auto compute = [&](const char* stage, int t) {
     const S* sK = reinterpret_cast<const S*>(stage);
     const S* sV = reinterpret_cast<const S*>(stage + GEO::kTileBytes);
-    const int valid = t < n_ptiles ? min(kKT, pk1 - pk0 - t * kKT)
-                                   : min(kKT, bk1 - bk0 - (t - n_ptiles) * kKT);
-    // S^T[key][query]
-    f32x16 s;
+    const int valid = t < n_ptiles ? min(KS, pk1 - pk0 - t * KS)
+                                   : min(KS, bk1 - bk0 - (t - n_ptiles) * KS);
+    // S^T[key][query]; the K swizzle of row 32u + q equals that of row q
+    f32x16 s[NSUB];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    const S* krow = sK + q * D;
+    for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[u][r] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds)
-      s = mma(FR::load_row(krow, 16 * ds + 8 * hh, ksw), qf[ds], s);
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u)
+        s[u] = mma(FR::load_row(sK + (32 * u + q) * D, 16 * ds + 8 * hh, ksw), qf[ds], s[u]);
     // online softmax in log2 units: m is kept scaled by scale*log2(e) (> 0)
     const float c = args.scale_log2;
-    if (valid < kKT) {
+    if (valid < KS) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + 4 * hh + (r & 3) >= valid) s[r] = -INFINITY;
+      for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * u + 8 * (r >> 2) + 4 * hh + (r & 3) >= valid) s[u][r] = -INFINITY;
     }
-    float tmax = s[0];
+    float tmax = s[0][0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, s[r]);
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32)) * c;
+    for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[u][r]);
+    tmax = pair_max(tmax) * c;
     const float m_new = fmaxf(m_run, tmax);
     if (__ballot(m_new > m_run)) {       // rescale only when some lane's maximum moved
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -312,45 +408,52 @@ __global__ __launch_bounds__(64 * NW) void attend_split_kernel(AttnArgs args) {
         for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
     }
     m_run = m_new;
-    float p[16];
+    float p[NSUB][16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -m_new));
-      l_run += p[r];
-    }
+    for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[u][r] = __builtin_amdgcn_exp2f(fmaf(s[u][r], c, -m_new));
+        l_run += p[u][r];
+      }
     // O^T[d][query] += sum_key V[key][d] P[query][key]
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      float pk8[8];
+    for (int u = 0; u < NSUB; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pk8[e] = p[8 * ks + e];
-      const typename FR::type bq = FR::from8(pk8);
+      for (int ks = 0; ks < 2; ++ks) {
+        float pk8[8];
 #pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) {
-        typename FR::type a;
-        if constexpr (kBf16) {
-          typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
-          const int r0 = 16 * ks + vrow, r1 = r0 + 8;
-          const int col = 32 * mt + vcol;
-          const uint16_t* p0 = sV + r0 * D + ((((col >> 3) ^ GEO::v_swz(r0)) << 3) | (col & 7));
-          const uint16_t* p1 = sV + r1 * D + ((((col >> 3) ^ GEO::v_swz(r1)) << 3) | (col & 7));
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(p0));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(p1));
-          a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        } else {
+        for (int e = 0; e < 8; ++e) pk8[e] = p[u][8 * ks + e];
+        const typename FR::type bq = FR::from8(pk8);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int key = 16 * ks + 8 * (e >> 2) + 4 * hh + (e & 3);
-            const int d = 32 * mt + q;
-            a.v[e] = sV[key * D + ((((d >> 2) ^ GEO::k_swz(key)) << 2) | (d & 3))];
+        for (int mt = 0; mt < D / 32; ++mt) {
+          typename FR::type a;
+          if constexpr (kBf16) {
+            typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+            const int r0 = 32 * u + 16 * ks + vrow, r1 = r0 + 8;
+            const int col = 32 * mt + vcol;
+            const uint16_t* p0 =
+                sV + r0 * D + ((((col >> 3) ^ GEO::v_swz(r0)) << 3) | (col & 7));
+            const uint16_t* p1 =
+                sV + r1 * D + ((((col >> 3) ^ GEO::v_swz(r1)) << 3) | (col & 7));
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(p0));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(p1));
+            a = __builtin_bit_cast(bf16x8,
+                                   __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int key = 32 * u + 16 * ks + 8 * (e >> 2) + 4 * hh + (e & 3);
+              const int d = 32 * mt + q;
+              a.v[e] = sV[key * D + ((((d >> 2) ^ GEO::k_swz(key)) << 2) | (d & 3))];
+            }
           }
+          acc_o[mt] = mma(a, bq, acc_o[mt]);
         }
-        acc_o[mt] = mma(a, bq, acc_o[mt]);
       }
-    }
   };
 
-  // prologue: three tiles in flight
+  // prologue: three stages in flight
   if (0 < nt) issue(0, st0);
   if (1 < nt) issue(1, st1);
   if (2 < nt) issue(2, st2);
@@ -378,123 +481,155 @@ __global__ __launch_bounds__(64 * NW) void attend_split_kernel(AttnArgs args) {
   }
 #undef SPRINT_ATT_STEP
 
-  const float l_tot = l_run + shfl_xor_f(l_run, 32);
-  if (!row_ok) return;
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int nrows = max(0, min(32, args.R - wave * 32));
+  // this wave's staging region: after the barrier the stages are free
+  __syncthreads();
+  using PE = typename std::conditional<kBf16, half_t, float>::type;   // partial element
+  constexpr int kOutWave = RowGeo<S, D>::kWaveBytes;
+  constexpr int kPartWave = RowGeo<PE, D>::kWaveBytes;
+  constexpr int kWaveBytes = kOutWave > kPartWave ? kOutWave : kPartWave;
+  constexpr int kWps = kStageBytes / kWaveBytes;                      // wave regions per stage
+  static_assert(kWps * kStages >= NW, "staging regions");
+  const int sidx = wave / kWps;
+  char* reg = (sidx == 0 ? st0 : sidx == 1 ? st1 : sidx == 2 ? st2 : st3) +
+              (wave % kWps) * kWaveBytes;
   if (args.n_splits == 1) {
     // the block saw every key: write O directly
-    S* out = reinterpret_cast<S*>(args.O) +
-             ((static_cast<int64_t>(seq) * args.Lq + qi) * args.Hq + head) * D;
-#pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        out[32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3)] = T::from_f32(acc_o[mt][r] * inv);
+    stage_rows<S, D>(reg, acc_o, inv, q, hh);
+    __syncthreads();
+    flush_rows<S, D>(reg, lane, nrows, [&](int rr) {
+      const int rh = wave * 32 + rr;
+      const int hd = g * args.G + rh / args.Lq;
+      return args.O + ((static_cast<int64_t>(seq) * args.Lq + rh % args.Lq) * args.Hq + hd) *
+                          static_cast<int64_t>(D * sizeof(S));
+    });
     return;
   }
-  const int64_t prow =
-      ((static_cast<int64_t>(seq) * args.Hkv + g) * args.n_splits + split) * args.R + rho;
-#pragma unroll
-  for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d = 32 * mt + 8 * r4 + 4 * hh;
-      if constexpr (kBf16) {
-        f16x4 v = {static_cast<half_t>(acc_o[mt][4 * r4 + 0] * inv),
-                   static_cast<half_t>(acc_o[mt][4 * r4 + 1] * inv),
-                   static_cast<half_t>(acc_o[mt][4 * r4 + 2] * inv),
-                   static_cast<half_t>(acc_o[mt][4 * r4 + 3] * inv)};
-        *reinterpret_cast<f16x4*>(static_cast<half_t*>(args.part_o) + prow * D + d) = v;
-      } else {
-        f32x4 v = {acc_o[mt][4 * r4 + 0] * inv, acc_o[mt][4 * r4 + 1] * inv,
-                   acc_o[mt][4 * r4 + 2] * inv, acc_o[mt][4 * r4 + 3] * inv};
-        *reinterpret_cast<f32x4*>(static_cast<float*>(args.part_o) + prow * D + d) = v;
-      }
-    }
-  if (hh == 0) {
-    args.part_ml[prow * 2 + 0] = m_run;
-    args.part_ml[prow * 2 + 1] = l_tot;
-  }
+  const int64_t pbase =
+      ((static_cast<int64_t>(seq) * args.Hkv + g) * args.n_splits + split) * args.R + wave * 32;
+  stage_rows<PE, D>(reg, acc_o, inv, q, hh);
+  __syncthreads();
+  flush_rows<PE, D>(reg, lane, nrows, [&](int rr) {
+    return static_cast<char*>(args.part_o) + (pbase + rr) * static_cast<int64_t>(D * sizeof(PE));
+  });
+  if (hh == 0 && row_ok)
+    *reinterpret_cast<float2*>(args.part_ml + (pbase + q) * 2) = make_float2(m_run, l_tot);
 }
 
-// Combine the key ranges: a block per (sequence, KV head, row group, 32-column
-// slab).  Eight lanes per row fold (m, l) over the ranges in parallel; then
-// every thread accumulates four columns of its row across the ranges with the
-// weights l_s 2^(m_s - m), four ranges per batch of loads.
+// Combine the key ranges: one wave per output row (of one sequence and KV
+// head).  A lane owns 8 columns and every (64/(D/8))-th range, so all of its
+// loads for a batch of eight ranges are in flight together; it folds them
+// with the running (m, l) in log2 units, then a butterfly over the lanes
+// that share its columns merges the range groups.  The fold order is fixed,
+// so the result is bitwise reproducible.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttnArgs args) {
   using S = typename T::storage;
   constexpr bool kBf16 = sizeof(S) == 2;
-  constexpr int kSlabs = D / 32;
-  const int slab = blockIdx.x % kSlabs;
-  const int rest = blockIdx.x / kSlabs;
-  const int rg = rest % args.n_rg;
-  const int g = (rest / args.n_rg) % args.Hkv;
-  const int seq = rest / (args.n_rg * args.Hkv);
-  const int row = threadIdx.x >> 3, sub = threadIdx.x & 7;
-  const int rr = rg * 32 + row;
-  const bool ok = rr < args.R;
-  const int64_t ubase = (static_cast<int64_t>(seq) * args.Hkv + g) * args.n_splits;
+  constexpr int kCL = D / 8;        // lanes across the columns
+  constexpr int kSG = 64 / kCL;     // lanes across the ranges
+  constexpr int kNB = 8;            // ranges per lane per batch
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n_rb = (args.R + 3) / 4;
+  const int rb = blockIdx.x % n_rb;
+  const int unit = blockIdx.x / n_rb;           // seq * Hkv + g
+  const int rr = rb * 4 + wave;
+  if (rr >= args.R) return;
+  const int g = unit % args.Hkv, seq = unit / args.Hkv;
+  const int cl = lane % kCL, sg = lane / kCL;
+  const int d = cl * 8;
   const int64_t rstride = static_cast<int64_t>(args.R);
-  const float* pml = args.part_ml + (ubase * rstride + (ok ? rr : 0)) * 2;
-  float m = -INFINITY;
-  for (int sp = sub; sp < args.n_splits; sp += 8) m = fmaxf(m, pml[sp * rstride * 2]);
+  const int64_t row0 = static_cast<int64_t>(unit) * args.n_splits * rstride + rr;
+  float m = -INFINITY, l = 0.f;
+  float acc[8];
 #pragma unroll
-  for (int o = 4; o >= 1; o >>= 1) m = fmaxf(m, shfl_xor_f(m, o));
-  float l = 0.f;
-  for (int sp = sub; sp < args.n_splits; sp += 8) {
-    const float ms = pml[sp * rstride * 2];
-    l += ms == -INFINITY ? 0.f : pml[sp * rstride * 2 + 1] * exp2f(ms - m);
-  }
+  for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+  for (int base = sg; base < args.n_splits; base += kSG * kNB) {
+    float ms[kNB], ls[kNB], v[kNB][8];
 #pragma unroll
-  for (int o = 4; o >= 1; o >>= 1) l += shfl_xor_f(l, o);
-  if (!ok) return;
-  const int d = slab * 32 + sub * 4;
-  const int64_t pofs = (ubase * rstride + rr) * D + d;
-  auto load4 = [&](int sp) -> f32x4 {
-    if constexpr (kBf16) {
-      const f16x4 h = *reinterpret_cast<const f16x4*>(static_cast<const half_t*>(args.part_o) +
-                                                      pofs + sp * rstride * D);
-      return f32x4{static_cast<float>(h[0]), static_cast<float>(h[1]), static_cast<float>(h[2]),
-                   static_cast<float>(h[3])};
-    } else {
-      return *reinterpret_cast<const f32x4*>(static_cast<const float*>(args.part_o) + pofs +
-                                             sp * rstride * D);
+    for (int u = 0; u < kNB; ++u) {
+      const int sp = base + kSG * u;
+      const bool ok = sp < args.n_splits;
+      const int64_t prow = row0 + static_cast<int64_t>(ok ? sp : 0) * rstride;
+      const float2 ml = ok ? *reinterpret_cast<const float2*>(args.part_ml + prow * 2)
+                           : make_float2(-INFINITY, 0.f);
+      ms[u] = ml.x;
+      ls[u] = ml.y;
+      if constexpr (kBf16) {
+        const u32x4 h = ok ? ld16(static_cast<const half_t*>(args.part_o) + prow * D + d)
+                           : u32x4{0u, 0u, 0u, 0u};
+        const f16x8 hv = __builtin_bit_cast(f16x8, h);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[u][c] = static_cast<float>(hv[c]);
+      } else {
+        const float* src = static_cast<const float*>(args.part_o) + prow * D + d;
+        const u32x4 a = ok ? ld16(src) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 b = ok ? ld16(src + 4) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          v[u][c] = __uint_as_float(a[c]);
+          v[u][4 + c] = __uint_as_float(b[c]);
+        }
+      }
     }
-  };
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  int sp = 0;
-  for (; sp + 4 <= args.n_splits; sp += 4) {
-    float ms[4], ls[4];
-    f32x4 v[4];
+    float mb = m;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ms[u] = pml[(sp + u) * rstride * 2];
-      ls[u] = pml[(sp + u) * rstride * 2 + 1];
-      v[u] = load4(sp + u);
+    for (int u = 0; u < kNB; ++u) mb = fmaxf(mb, ms[u]);
+    if (mb == -INFINITY) continue;              // only empty ranges so far
+    const float a = m == -INFINITY ? 0.f : exp2f(m - mb);
+    l *= a;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] *= a;
+#pragma unroll
+    for (int u = 0; u < kNB; ++u) {
+      const float w = ms[u] == -INFINITY ? 0.f : ls[u] * exp2f(ms[u] - mb);
+      l += w;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = fmaf(w, v[u][c], acc[c]);
     }
+    m = mb;
+  }
+  // merge the range groups (the same arithmetic on both lanes of a pair)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      acc += (ms[u] == -INFINITY ? 0.f : ls[u] * exp2f(ms[u] - m)) * v[u];
+  for (int o = kCL; o < 64; o <<= 1) {
+    const float m2 = shfl_xor_f(m, o), l2 = shfl_xor_f(l, o);
+    const float mn = fmaxf(m, m2);
+    const float a = m == -INFINITY ? 0.f : exp2f(m - mn);
+    const float b = m2 == -INFINITY ? 0.f : exp2f(m2 - mn);
+    l = l * a + l2 * b;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = acc[c] * a + shfl_xor_f(acc[c], o) * b;
+    m = mn;
   }
-  for (; sp < args.n_splits; ++sp) {
-    const float ms = pml[sp * rstride * 2];
-    const f32x4 v = load4(sp);
-    acc += (ms == -INFINITY ? 0.f : pml[sp * rstride * 2 + 1] * exp2f(ms - m)) * v;
-  }
+  if (sg != 0) return;
   const float inv = 1.f / l;
   const int gi = rr / args.Lq, qi = rr % args.Lq;
   const int head = g * args.G + gi;
   S* out = reinterpret_cast<S*>(args.O) +
            ((static_cast<int64_t>(seq) * args.Lq + qi) * args.Hq + head) * D + d;
+  if constexpr (kBf16) {
+    u32x4 o;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) out[c] = T::from_f32(acc[c] * inv);
+    for (int c = 0; c < 4; ++c) o[c] = pack_bf16x2(acc[2 * c] * inv, acc[2 * c + 1] * inv);
+    st16(out, o);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) out[c] = acc[c] * inv;
+  }
+}
+
+// bf16 stages hold 64 keys (two S^T tiles); fp32 stages 32 keys (LDS size).
+template <typename T>
+constexpr int nsub() {
+  return sizeof(typename T::storage) == 2 ? 2 : 1;
 }
 
 template <typename T, int D, int NW>
 hipError_t launch_split(const AttnArgs& a, hipStream_t st) {
   const int blocks = a.nseq * a.Hkv * a.n_splits;
-  attend_split_kernel<T, D, NW><<<dim3(blocks), dim3(64 * NW), 0, st>>>(a);
+  attend_split_kernel<T, D, NW, nsub<T>()><<<dim3(blocks), dim3(64 * NW), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -510,7 +645,7 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
   else
     e = launch_split<T, D, 8>(a, st);
   if (e != hipSuccess || a.n_splits == 1) return e;
-  const int blocks = a.nseq * a.Hkv * a.n_rg * (D / 32);
+  const int blocks = a.nseq * a.Hkv * ((a.R + 3) / 4);
   attend_combine_kernel<T, D><<<dim3(blocks), dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }
@@ -523,10 +658,10 @@ AttnPlan attend_plan(int nseq, int Lq, int Hq, int Hkv, int D, int max_kv, int h
   p.rows = (Hq / Hkv) * Lq;
   const int64_t n_keys = static_cast<int64_t>(max_kv) + (has_block ? Lq : 0);
   const int64_t units = static_cast<int64_t>(nseq) * Hkv;
-  // Keys per range: the largest power of two (at least one tile) that still
-  // gives >= 192 blocks, so most CUs stream a range.
+  // Keys per range: the largest power of two (at least one 64-key stage)
+  // that still gives >= 192 blocks, so most CUs stream a range.
   int kps = 1 << 20;
-  while (kps > kKT && units * ((n_keys + kps - 1) / kps) < 192) kps >>= 1;
+  while (kps > 2 * kKT && units * ((n_keys + kps - 1) / kps) < 192) kps >>= 1;
   p.kps = kps;
   p.n_splits = static_cast<int>(n_keys > 0 ? (n_keys + kps - 1) / kps : 1);
   const size_t es = dtype == 1 ? 2 : 4;

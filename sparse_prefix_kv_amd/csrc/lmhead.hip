@@ -431,6 +431,170 @@ __global__ __launch_bounds__(kGThreads) void lmhead_gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small-M path (a denoising step: M = 32 or 64 block tokens).  The work is
+// streaming W once from HBM (V*H*2 bytes against 2*M*V*H flops), so the
+// kernel is built around bytes in flight: a block owns 128 vocabulary rows
+// and the whole reduction, and streams 64-deep K chunks of those rows (16 KB)
+// plus the matching X chunk (4 KB per 32 tokens, an L2 hit) through a ring
+// of six LDS stages with buffer loads straight into LDS, five chunks ahead.
+// Each wave turns a chunk into 4*NT MFMAs (32 vocabulary rows x 32*NT
+// tokens), far below the time the chunk takes to arrive.  Same swizzle and
+// epilogue fold as the large-M kernel.
+constexpr int kSBV = 128;     // vocabulary rows per block
+constexpr int kSStages = 6;
+
+template <int NT>
+__global__ __launch_bounds__(256) void lmhead_stream_kernel(const uint16_t* __restrict__ X,
+                                                            int64_t M, int H,
+                                                            const uint16_t* __restrict__ W, int V,
+                                                            float4* __restrict__ part, int n_vt) {
+  constexpr int kBT = 32 * NT;
+  constexpr int kStElems = (kSBV + kBT) * kGKC;
+  __shared__ __align__(16) uint16_t s0[kStElems];
+  __shared__ __align__(16) uint16_t s1[kStElems];
+  __shared__ __align__(16) uint16_t s2[kStElems];
+  __shared__ __align__(16) uint16_t s3[kStElems];
+  __shared__ __align__(16) uint16_t s4[kStElems];
+  __shared__ __align__(16) uint16_t s5[kStElems];
+  __shared__ Stat red[kBT][4];
+
+  const int vt = blockIdx.x;
+  const int v0 = vt * kSBV;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kBT;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 31, hh = lane >> 5;
+
+  // DMA plan: instruction i of a stage half fills rows 8i + lane/8, slot
+  // lane%8 = k-chunk (lane%8) ^ ((row >> 1) & 7), which depends only on the
+  // parity of i.  W instructions 4*wave + j, X instructions wave + 4*p.
+  const int c_even = (lane & 7) ^ ((lane >> 4) & 7);
+  const uint32_t lrow_bytes = static_cast<uint32_t>(lane >> 3) * H * 2;
+  const uint32_t offE = lrow_bytes + c_even * 16;
+  const uint32_t offO = lrow_bytes + (c_even ^ 4) * 16;
+  const uint32_t rs8 = static_cast<uint32_t>(16) * H;        // 8 rows of bf16
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(W), 0, static_cast<int>(static_cast<int64_t>(V) * H * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(X), 0, static_cast<int>(M * H * 2), 0x00020000);
+  const uint32_t soA = static_cast<uint32_t>(v0 + 32 * wave) * H * 2;
+  const uint32_t soB = static_cast<uint32_t>(t0 + 8 * wave) * H * 2;
+  const uint32_t offX = (wave & 1) ? offO : offE;
+  auto issue = [&](int kc, uint16_t* stage) {
+    const uint32_t kb = static_cast<uint32_t>(kc) * (2 * kGKC);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, SPRINT_LDS(stage + (4 * wave + j) * 512), 16,
+                                               (j & 1) ? offO : offE, soA + j * rs8 + kb, 0,
+                                               kCpolNT);
+#pragma unroll
+    for (int p = 0; p < NT; ++p)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rX, SPRINT_LDS(stage + kSBV * kGKC + (wave + 4 * p) * 512), 16, offX,
+          soB + p * 4 * rs8 + kb, 0, 0);
+  };
+
+  const int sw = (q >> 1) & 7;
+  const int aoff = (32 * wave + q) * kGKC;
+  const int boff = kSBV * kGKC + q * kGKC;
+  f32x16 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
+  auto compute = [&](const uint16_t* stage) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int so = ((2 * ks + hh) ^ sw) * 8;
+      const bf16x8 a = as_bf16x8(ld16(stage + aoff + so));
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        acc[n] = mma32_k16(a, as_bf16x8(ld16(stage + boff + n * 32 * kGKC + so)), acc[n]);
+    }
+  };
+
+  const int nk = H / kGKC;
+  constexpr int kPer = 4 + NT;     // vector-memory instructions per wave per chunk
+  if (0 < nk) issue(0, s0);
+  if (1 < nk) issue(1, s1);
+  if (2 < nk) issue(2, s2);
+  if (3 < nk) issue(3, s3);
+  if (4 < nk) issue(4, s4);
+#define SPRINT_STREAM_STEP(CUR, NXT, U)                                                   \
+  {                                                                                       \
+    const int kc = kb + (U);                                                              \
+    if (kc < nk) {                                                                        \
+      const int pend = min(kSStages - 2, nk - 1 - kc);                                    \
+      if (pend >= 4)                                                                      \
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(4 * kPer));                                \
+      else if (pend == 3)                                                                 \
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(3 * kPer));                                \
+      else if (pend == 2)                                                                 \
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * kPer));                                \
+      else if (pend == 1)                                                                 \
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(kPer));                                    \
+      else                                                                                \
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));                                       \
+      __builtin_amdgcn_s_barrier();                                                       \
+      if (kc + kSStages - 1 < nk) issue(kc + kSStages - 1, NXT);                          \
+      compute(CUR);                                                                       \
+    }                                                                                     \
+  }
+  for (int kb = 0; kb < nk; kb += kSStages) {
+    SPRINT_STREAM_STEP(s0, s5, 0)
+    SPRINT_STREAM_STEP(s1, s0, 1)
+    SPRINT_STREAM_STEP(s2, s1, 2)
+    SPRINT_STREAM_STEP(s3, s2, 3)
+    SPRINT_STREAM_STEP(s4, s3, 4)
+    SPRINT_STREAM_STEP(s5, s4, 5)
+  }
+#undef SPRINT_STREAM_STEP
+
+  // Epilogue: per token column fold this wave's 32 vocabulary rows, the
+  // partner half-wave, then the four waves (vocabulary order) through LDS.
+  const int vbase = v0 + 32 * wave + 4 * hh;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    Stat st{-INFINITY, 0.f, INT_MAX};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int v = vbase + 8 * (r >> 2) + (r & 3);
+      if (v < V && acc[n][r] > st.m) {
+        st.m = acc[n][r];
+        st.a = v;
+      }
+    }
+    if (st.m != -INFINITY) {
+      const float ml = st.m * kLog2e;
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (vbase + 8 * (r >> 2) + (r & 3) < V) sum += exp2f(fmaf(acc[n][r], kLog2e, -ml));
+      st.s = sum;
+    }
+    Stat other;
+    other.m = shfl_xor_f(st.m, 32);
+    other.s = shfl_xor_f(st.s, 32);
+    other.a = shfl_xor_i(st.a, 32);
+    if (hh == 0) {
+      merge(st, other);
+      red[n * 32 + q][wave] = st;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kBT) {
+    const int c = threadIdx.x;
+    const int64_t tok = t0 + c;
+    if (tok < M) {
+      Stat st = red[c][0];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) merge(st, red[c][w]);
+      part[tok * n_vt + vt] = make_float4(st.m, st.s, __int_as_float(st.a), 0.f);
+    }
+  }
+}
+
 // One wave per row: each lane folds a strided subset of tiles in order, then
 // a fixed butterfly merges the lanes.
 __global__ __launch_bounds__(256) void lmhead_merge_kernel(const float4* __restrict__ part,
@@ -480,15 +644,21 @@ hipError_t run_tiles(const void* X, int64_t M, int H, const void* W, int V, floa
   return hipGetLastError();
 }
 
-// Small M (a denoising step's block): 32 tokens x 128 vocabulary rows per
-// block, so the grid spreads W over every CU.  Large M (the prefix pass):
-// 128 x 128 tiles.
+// Kernel choice.  bf16 with W and X each addressable by a 32-bit buffer
+// descriptor: M <= 64 streams W once (lmhead_stream_kernel); larger M runs
+// the 256 x 256 tile GEMM (H in whole 128-deep pairs of chunks).  Anything
+// else (fp32, odd shapes) takes the generic tile kernel: 32 tokens x 128
+// vocabulary rows per block for M <= 32, 128 x 128 tiles otherwise.
 inline bool small_m(int64_t M) { return M <= 32; }
-// bf16, more than one token tile, H in whole 64-deep chunks, and W and X
-// each addressable by a 32-bit buffer descriptor
+inline bool bf16_buffers(int64_t M, int H, int V, int dtype) {
+  return dtype == 1 && static_cast<int64_t>(V) * H * 2 < (int64_t(1) << 31) &&
+         M * H * 2 < (int64_t(1) << 31);
+}
+inline bool stream_path(int64_t M, int H, int V, int dtype) {
+  return bf16_buffers(M, H, V, dtype) && M <= 64 && H % kGKC == 0;
+}
 inline bool gemm_path(int64_t M, int H, int V, int dtype) {
-  return dtype == 1 && M > kGB && H % (2 * kGKC) == 0 &&
-         static_cast<int64_t>(V) * H * 2 < (int64_t(1) << 31) && M * H * 2 < (int64_t(1) << 31);
+  return bf16_buffers(M, H, V, dtype) && M > 64 && H % (2 * kGKC) == 0;
 }
 inline int tile_bv(int64_t M, int H, int V, int dtype) {
   return gemm_path(M, H, V, dtype) ? kGB : 128;
@@ -505,7 +675,18 @@ hipError_t launch_lmhead(const void* X, int64_t M, int H, const void* W, int V, 
   const int n_vt = (V + tile_bv(M, H, V, dtype) - 1) / tile_bv(M, H, V, dtype);
   float4* part = static_cast<float4*>(ws);
   hipError_t e;
-  if (gemm_path(M, H, V, dtype)) {
+  if (stream_path(M, H, V, dtype)) {
+    const dim3 grid(n_vt);
+    if (M <= 32)
+      lmhead_stream_kernel<1><<<grid, dim3(256), 0, st>>>(static_cast<const uint16_t*>(X), M, H,
+                                                         static_cast<const uint16_t*>(W), V, part,
+                                                         n_vt);
+    else
+      lmhead_stream_kernel<2><<<grid, dim3(256), 0, st>>>(static_cast<const uint16_t*>(X), M, H,
+                                                         static_cast<const uint16_t*>(W), V, part,
+                                                         n_vt);
+    e = hipGetLastError();
+  } else if (gemm_path(M, H, V, dtype)) {
     const int n_mt = static_cast<int>((M + kGB - 1) / kGB);
     const int per_xcd = (n_vt * n_mt + kXcds - 1) / kXcds;
     lmhead_gemm_kernel<<<dim3(per_xcd * kXcds), dim3(kGThreads), 0, st>>>(

@@ -229,16 +229,31 @@ __global__ __launch_bounds__(kCopyThreads) void compact_kernel(
   const int64_t slot0 = s_slot0, limit = s_limit;
   const int64_t row_bytes = static_cast<int64_t>(row_vecs) * 16;
   const int units = nk * row_vecs;
-  for (int u = threadIdx.x; u < units; u += kCopyThreads) {
-    const int r = u / row_vecs, v = u - r * row_vecs;
-    const int64_t slot = slot0 + r;
-    if (slot < 0 || slot >= limit) continue;
-    const int64_t src = s_pos[r] * row_bytes + v * 16;
-    const int64_t dst = slot * row_bytes + v * 16;
-    const u32x4 kv = ld16(K + src);
-    const u32x4 vv = ld16(V + src);
-    st16(K_out + dst, kv);
-    st16(V_out + dst, vv);
+  // four 16-byte vectors of K and of V per thread in flight per round; the
+  // source rows are read once (non-temporal), the pruned cache is written
+  // with ordinary stores since the denoising steps read it next
+  constexpr int kU = 4;
+  for (int u0 = threadIdx.x; u0 < units; u0 += kU * kCopyThreads) {
+    u32x4 kv[kU], vv[kU];
+    int64_t dst[kU];
+    bool ok[kU];
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const int u = u0 + i * kCopyThreads;
+      const int r = u / row_vecs, v = u - r * row_vecs;
+      const int64_t slot = slot0 + r;
+      ok[i] = u < units && slot >= 0 && slot < limit;
+      const int64_t src = ok[i] ? s_pos[r] * row_bytes + v * 16 : 0;
+      dst[i] = slot * row_bytes + v * 16;
+      kv[i] = ok[i] ? ld16_nt(K + src) : u32x4{0u, 0u, 0u, 0u};
+      vv[i] = ok[i] ? ld16_nt(V + src) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < kU; ++i)
+      if (ok[i]) {
+        st16(K_out + dst[i], kv[i]);
+        st16(V_out + dst[i], vv[i]);
+      }
   }
 }
 

@@ -1,22 +1,27 @@
 // Composite prefix score: mean-normalised key norm blended with the prefix
 // confidence (LLaDA2.0-Uni, SPRINT "Sparse Prefix Retention").
 //
-// Two launches over chunks of 256 positions (a chunk never spans sequences):
+// Two launches over chunks of 64 positions (a chunk never spans sequences):
 //   1. keynorm_kernel: n_i = ||K[i]|| (fp32 accumulation) into `ibar`, plus
 //      the chunk's sum of norms into the workspace;
 //   2. score_kernel: every chunk re-derives its sequence's mean from the
 //      chunk sums in one fixed order (so all chunks agree bitwise), then
 //      writes I_i = n_i / mean and s_i = alpha*I_i + (1-alpha)*c_i in place.
 // HBM-bound: it reads each key row once (Hkv*D elements) and 12 bytes of
-// per-position floats.
+// per-position floats.  Eight lanes share a row: one wave instruction reads
+// 128 contiguous bytes of eight rows (whole cache lines), and every lane has
+// all of its loads for two rows in flight before it reduces.  Summation
+// order is fixed (lane-strided vectors, then a butterfly), so results are
+// bitwise reproducible.
 #include "sprint_device.hpp"
 #include "sprint_internal.hpp"
 
 namespace sprint {
 namespace {
 
-constexpr int kChunk = 256;
-constexpr int kThreads = 256;
+constexpr int kChunk = 64;     // positions per block
+constexpr int kThreads = 256;  // 4 waves x 2 passes x 8 rows = 64 rows
+constexpr int kLanesPerRow = 8;
 
 template <typename T>
 __device__ __forceinline__ float sumsq16(u32x4 x);
@@ -43,13 +48,12 @@ __device__ __forceinline__ float sumsq16<F32>(u32x4 x) {
   return acc;
 }
 
-// G lanes cooperate on one key row of `row_vecs` 16-byte vectors; G is the
-// largest power of two <= min(64, row_vecs).
+// row_vecs = 16-byte vectors per key row (a multiple of 8 for D in {64, 128}).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void keynorm_kernel(const char* __restrict__ K,
                                                            const int32_t* __restrict__ cu_len,
                                                            int nseq, int64_t total_L,
-                                                           int row_vecs, int G,
+                                                           int row_vecs,
                                                            float* __restrict__ norms,
                                                            float* __restrict__ partial) {
   SeqChunk sc;
@@ -59,51 +63,61 @@ __global__ __launch_bounds__(kThreads) void keynorm_kernel(const char* __restric
   const int64_t rem = sc.begin + sc.len - p0;
   const int n = rem < kChunk ? static_cast<int>(rem) : kChunk;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int gl = lane & (G - 1), grp = lane / G, groups = 64 / G;
-  const int rows_per_iter = (kThreads / 64) * groups;
+  const int gl = lane & (kLanesPerRow - 1), grp = lane / kLanesPerRow;
   const int64_t row_bytes = static_cast<int64_t>(row_vecs) * 16;
-  for (int r0 = 0; r0 < n; r0 += rows_per_iter) {
-    const int r = r0 + wave * groups + grp;
-    float ss = 0.f;
-    if (r < n) {
-      const char* row = K + (p0 + r) * row_bytes;
-      for (int v = gl; v < row_vecs; v += G) ss += sumsq16<T>(ld16(row + v * 16));
+  // this lane's two rows: r_p = 16*wave + 8*p + grp
+  const int r0 = 16 * wave + grp, r1 = r0 + 8;
+  const bool ok0 = r0 < n, ok1 = r1 < n;
+  const char* row0 = K + (p0 + (ok0 ? r0 : 0)) * row_bytes;
+  const char* row1 = K + (p0 + (ok1 ? r1 : 0)) * row_bytes;
+  float ss0 = 0.f, ss1 = 0.f;
+#pragma unroll 4
+  for (int v = gl; v < row_vecs; v += kLanesPerRow) {
+    const u32x4 a = ok0 ? ld16_nt(row0 + v * 16) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 b = ok1 ? ld16_nt(row1 + v * 16) : u32x4{0u, 0u, 0u, 0u};
+    ss0 += sumsq16<T>(a);
+    ss1 += sumsq16<T>(b);
+  }
+#pragma unroll
+  for (int m = kLanesPerRow >> 1; m >= 1; m >>= 1) {
+    ss0 += shfl_xor_f(ss0, m);
+    ss1 += shfl_xor_f(ss1, m);
+  }
+  if (gl == 0) {
+    if (ok0) {
+      const float nv = sqrtf(ss0);
+      s_norm[r0] = nv;
+      norms[p0 + r0] = nv;
     }
-    for (int m = G >> 1; m >= 1; m >>= 1) ss += shfl_xor_f(ss, m);
-    if (r < n && gl == 0) {
-      const float nv = sqrtf(ss);
-      s_norm[r] = nv;
-      norms[p0 + r] = nv;
+    if (ok1) {
+      const float nv = sqrtf(ss1);
+      s_norm[r1] = nv;
+      norms[p0 + r1] = nv;
     }
   }
   __syncthreads();
   if (wave == 0) {
-    float acc = 0.f;
-    for (int i = lane; i < n; i += 64) acc += s_norm[i];
+    float acc = lane < n ? s_norm[lane] : 0.f;
     acc = wave_sum(acc);
     if (lane == 0) partial[blockIdx.x] = acc;
   }
 }
 
-__global__ __launch_bounds__(kThreads) void score_kernel(const float* __restrict__ conf,
-                                                         const int32_t* __restrict__ cu_len,
-                                                         int nseq, int64_t total_L,
-                                                         const float* __restrict__ partial,
-                                                         float alpha, float* __restrict__ ibar,
-                                                         float* __restrict__ score) {
+// One wave per 64-position chunk.
+__global__ __launch_bounds__(64) void score_kernel(const float* __restrict__ conf,
+                                                   const int32_t* __restrict__ cu_len, int nseq,
+                                                   int64_t total_L,
+                                                   const float* __restrict__ partial, float alpha,
+                                                   float* __restrict__ ibar,
+                                                   float* __restrict__ score) {
   SeqChunk sc;
   if (!find_seq_chunk(cu_len, nseq, kChunk, total_L, blockIdx.x, sc)) return;
-  __shared__ float s_mean;
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    float acc = 0.f;
-    for (int i = lane; i < sc.nchunks; i += 64) acc += partial[sc.first + i];
-    acc = wave_sum(acc);
-    if (lane == 0) s_mean = acc / static_cast<float>(sc.len);
-  }
-  __syncthreads();
-  const float mean = s_mean;
-  const int64_t p = sc.begin + static_cast<int64_t>(sc.c) * kChunk + threadIdx.x;
+  const int lane = threadIdx.x;
+  float acc = 0.f;
+  for (int i = lane; i < sc.nchunks; i += 64) acc += partial[sc.first + i];
+  acc = wave_sum(acc);
+  const float mean = acc / static_cast<float>(sc.len);
+  const int64_t p = sc.begin + static_cast<int64_t>(sc.c) * kChunk + lane;
   if (p < sc.begin + sc.len) {
     const float ib = mean > 0.f ? ibar[p] / mean : 1.f;
     ibar[p] = ib;
@@ -123,20 +137,18 @@ hipError_t launch_score(const void* K, const float* conf, const int32_t* cu_len,
   if (total_L == 0) return hipSuccess;
   const int es = dtype == 1 ? 2 : 4;
   const int row_vecs = Hkv * D * es / 16;
-  int G = 1;
-  while (G * 2 <= row_vecs && G * 2 <= 64) G *= 2;
   const int64_t nblk = chunk_bound(total_L, nseq, kChunk);
   float* partial = static_cast<float*>(ws);
   if (dtype == 1)
     keynorm_kernel<BF16><<<dim3(nblk), dim3(kThreads), 0, st>>>(
-        static_cast<const char*>(K), cu_len, nseq, total_L, row_vecs, G, ibar, partial);
+        static_cast<const char*>(K), cu_len, nseq, total_L, row_vecs, ibar, partial);
   else
     keynorm_kernel<F32><<<dim3(nblk), dim3(kThreads), 0, st>>>(
-        static_cast<const char*>(K), cu_len, nseq, total_L, row_vecs, G, ibar, partial);
+        static_cast<const char*>(K), cu_len, nseq, total_L, row_vecs, ibar, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  score_kernel<<<dim3(nblk), dim3(kThreads), 0, st>>>(conf, cu_len, nseq, total_L, partial,
-                                                       alpha, ibar, score);
+  score_kernel<<<dim3(nblk), dim3(64), 0, st>>>(conf, cu_len, nseq, total_L, partial, alpha, ibar,
+                                                score);
   return hipGetLastError();
 }
 

@@ -86,6 +86,13 @@ __device__ __forceinline__ f32x16 mma32_k16(const float (&a)[8], const float (&b
 
 // 16-byte vector load/store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Non-temporal load for data streamed once (global_load ... nt): the caches
+// do not keep the line, which on MI355X raises the rate of cold HBM streams.
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+// Cache-policy operand of buffer loads: non-temporal.
+constexpr int kCpolNT = 2;
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
