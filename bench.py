@@ -10,11 +10,14 @@ single-sequence prefix of 4096 positions (1024 text + 3072 image), 16/4
 heads of dim 128, vocabulary 32768, pass + 8 steps.
 
 Printed: one JSON line.  `value` is denoising block-steps per second
-(1 pass + 8 pruned steps = 9 block-steps per block and sequence), from the
-eager timed region in which HIP events bracket every library call on the
-stream it runs on.  The same line carries the full-retention baseline, the
-HIP-graph replay rate, per-call timings (warm and cache-flushed), the
-roofline of the dominant call and the CPU oracle timed on the host.
+(1 pass + 8 pruned steps = 9 block-steps per block and sequence) of the
+whole block replayed as one HIP graph (launch overhead off the GPU's
+critical path), after checking that a replay leaves exactly the state an
+eager run leaves.  The same line carries the eager (host-launched) rate, the
+full-retention baseline, per-call GPU times (each call captured 20 times
+back to back in a graph, HIP events around the replay on the stream it runs
+on; and cache-flushed single calls), the roofline of the dominant call and
+the CPU oracle timed on the host.
 """
 from __future__ import annotations
 
@@ -46,7 +49,6 @@ def parse():
     ap.add_argument("--cold-iters", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=2)
-    ap.add_argument("--no-graph", action="store_true")
     return ap.parse_args()
 
 
@@ -174,56 +176,87 @@ def main():
     torch.cuda.synchronize()
     log("[bench] warmup done")
 
-    # ---------------------------------------------------------------- timed: SPRINT
-    timer = EventTimer(torch)
-    blk.timer = timer
+    # ---------------------------------------------------------------- eager (host-launched)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         blk.run_block(n_steps)
     torch.cuda.synchronize()
-    t_sprint = (time.perf_counter() - t0) / args.steps
-    calls = timer.summary()
-    log(f"[bench] SPRINT block {t_sprint * 1e3:.3f} ms")
+    t_eager = (time.perf_counter() - t0) / args.steps
+    log(f"[bench] eager SPRINT block {t_eager * 1e3:.3f} ms")
 
-    # ---------------------------------------------------------------- timed: full retention
-    timer_full = EventTimer(torch)
-    blk.timer = timer_full
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        blk.run_full_block(n_steps)
-    torch.cuda.synchronize()
-    t_full = (time.perf_counter() - t0) / args.steps
-    calls_full = timer_full.summary()
-    blk.timer = None
-    log(f"[bench] full-retention block {t_full * 1e3:.3f} ms")
+    # ---------------------------------------------------------------- graphs
+    def capture(fn):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
 
-    # ---------------------------------------------------------------- graph replay
-    graph = None
-    if not args.no_graph:
-        try:
-            s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s):
-                blk.run_block(n_steps)
-            torch.cuda.current_stream().wait_stream(s)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                blk.run_block(n_steps)
-            torch.cuda.synchronize()
+    def state():
+        return (blk.tokens.clone(), blk.masked.clone(), blk.kept_idx.clone(), blk.O.clone())
+
+    def replay_rate(g, reps):
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(reps):
             g.replay()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(args.steps):
-                g.replay()
-            torch.cuda.synchronize()
-            t_graph = (time.perf_counter() - t0) / args.steps
-            graph = {"block_ms": t_graph * 1e3, "block_steps_per_s": steps_per_block / t_graph}
-            log(f"[bench] graph-replayed SPRINT block {t_graph * 1e3:.3f} ms")
-        except Exception as e:  # graph capture is an extra, never the headline
-            graph = {"error": repr(e)[:200]}
+        e1.record()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps, e0.elapsed_time(e1) * 1e-3 / reps
+
+    g_sprint = capture(lambda: blk.run_block(n_steps))
+    g_full = capture(lambda: blk.run_full_block(n_steps))
+    # a replay must leave exactly what an eager run leaves
+    blk.run_block(n_steps)
+    torch.cuda.synchronize()
+    ref = state()
+    blk.tokens.fill_(-7)
+    blk.O.zero_()
+    g_sprint.replay()
+    torch.cuda.synchronize()
+    graph_ok = all(torch.equal(a, b) for a, b in zip(ref, state()))
+    if not graph_ok:
+        log("[bench] WARNING: graph replay differs from the eager run; reporting eager")
+    _, t_graph = replay_rate(g_sprint, args.steps)
+    _, t_full = replay_rate(g_full, args.steps)
+    t_sprint = t_graph if graph_ok else t_eager
+    log(f"[bench] graph SPRINT block {t_graph * 1e3:.3f} ms, full-retention block "
+        f"{t_full * 1e3:.3f} ms")
+    del g_sprint, g_full
+
+    # ---------------------------------------------------------------- per-call GPU time
+    reps = 20
+    call_fns = {
+        "lmhead_prefix": blk.prefix_confidence,
+        "score": blk.score_prefix,
+        "prune": blk.prune_prefix,
+        "attend_full": lambda: blk.attend(False),
+        "attend_pruned": lambda: blk.attend(True),
+        "lmhead_block": blk.block_confidence,
+        "unmask": lambda: blk.unmask(1),
+    }
+    calls = {}
+    for name, fn in call_fns.items():
+        blk.reset()
+        g = capture(lambda: [fn() for _ in range(reps)])
+        ts = sorted(replay_rate(g, 3)[1] / reps for _ in range(5))
+        calls[name] = {"us": ts[len(ts) // 2] * 1e6, "min_us": ts[0] * 1e6}
+        del g
+    launches = {"lmhead_prefix": 1, "score": 1, "prune": 1, "attend_full": 1,
+                "attend_pruned": n_steps, "lmhead_block": n_steps + 1, "unmask": n_steps + 1}
+    launches_full = {"attend_full": n_steps + 1, "lmhead_block": n_steps + 1,
+                     "unmask": n_steps + 1}
 
     # ---------------------------------------------------------------- cold per-call timings
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
@@ -235,33 +268,32 @@ def main():
             with cold(name):
                 fn()
     blk.reset()
-    cold_run("lmhead_prefix", blk.prefix_confidence)
-    cold_run("score", blk.score_prefix)
-    cold_run("prune", blk.prune_prefix)
-    cold_run("attend_full", lambda: blk.attend(False))
-    cold_run("attend_pruned", lambda: blk.attend(True))
-    cold_run("lmhead_block", blk.block_confidence)
+    for name, fn in call_fns.items():
+        cold_run(name, fn)
     torch.cuda.synchronize()
     calls_cold = cold.summary()
     del flush
 
     # ---------------------------------------------------------------- roofline
     work = work_model(blk)
-    per_block = {k: v["mean_us"] * v["n"] / args.steps for k, v in calls.items()}
+    per_block = {k: calls[k]["us"] * launches[k] for k in calls}
     dominant = max(per_block, key=per_block.get)
     kernels = {}
     for name, st in calls.items():
         w = work[name]
-        us = st["mean_us"]
-        ent = {"mean_us": round(us, 3), "launches_per_block": st["n"] // args.steps,
+        us = st["us"]
+        ent = {"us": round(us, 3), "launches_per_block": launches[name],
+               "us_per_block": round(us * launches[name], 2),
                "alg_bytes": w["bytes"], "alg_flops": w["flops"], "bound": w["bound"],
                "gbs": round(w["bytes"] / us / 1e3, 1),
                "tflops": round(w["flops"] / us / 1e6, 2)}
         if name in calls_cold:
-            ent["cold_mean_us"] = round(calls_cold[name]["mean_us"], 3)
+            cu = calls_cold[name]["median_us"]
+            ent["cold_us"] = round(cu, 3)
+            ent["cold_gbs"] = round(w["bytes"] / cu / 1e3, 1)
         kernels[name] = ent
     dw = work[dominant]
-    dus = calls[dominant]["mean_us"]
+    dus = calls[dominant]["us"]
     bf16 = wl.dtype == "bf16"
     if dw["bound"] == "mfma":
         achieved = dw["flops"] / dus / 1e6
@@ -276,11 +308,10 @@ def main():
                 "kernel": dominant, "alg_per_launch": dw["flops"] if dw["bound"] == "mfma"
                 else dw["bytes"], "mean_launch_us": round(dus, 3)}
 
-    att_pr = calls["attend_pruned"]["mean_us"]
-    att_full = calls_full["attend_full"]["mean_us"]
-    step_pr = att_pr + calls["lmhead_block"]["mean_us"] + calls["unmask"]["mean_us"]
-    step_full = (att_full + calls_full["lmhead_block"]["mean_us"] +
-                 calls_full["unmask"]["mean_us"])
+    att_pr = calls["attend_pruned"]["us"]
+    att_full = calls["attend_full"]["us"]
+    step_pr = att_pr + calls["lmhead_block"]["us"] + calls["unmask"]["us"]
+    step_full = att_full + calls["lmhead_block"]["us"] + calls["unmask"]["us"]
 
     # ---------------------------------------------------------------- CPU baseline
     cpu = None
@@ -308,6 +339,9 @@ def main():
                    "steps_per_block": n_steps + 1, "r_text": blk.r_text, "r_img": blk.r_img,
                    "tau": blk.tau, "step_unit": "one whole block (pass + pruned steps)"},
         "tokens_per_s": round(wl.Lq * lay.nseq / t_sprint, 1),
+        "timing": "HIP graph replay of whole blocks" if graph_ok else "eager",
+        "eager": {"block_ms": round(t_eager * 1e3, 4),
+                  "block_steps_per_s": round(steps_per_block / t_eager, 2)},
         "full_retention": {"block_ms": round(t_full * 1e3, 4),
                            "block_steps_per_s": round(steps_per_block / t_full, 2)},
         "speedup_pruned_vs_full": {"attention_call": round(att_full / att_pr, 4),
@@ -315,7 +349,6 @@ def main():
                                    "block": round(t_full / t_sprint, 4),
                                    "pages_claim_context": "up to 1.6x end to end (model, "
                                                           "hardware and workload not given)"},
-        "graph": graph,
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,

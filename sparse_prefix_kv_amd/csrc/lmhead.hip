@@ -595,6 +595,164 @@ __global__ __launch_bounds__(256) void lmhead_stream_kernel(const uint16_t* __re
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small-M path through registers (M <= 64, H a multiple of 256): W is read
+// with coalesced non-temporal loads (each wave instruction covers eight whole
+// 128-byte row segments, the pattern that streams HBM fastest on MI355X)
+// into a ring of four 64-deep chunks per wave, then written to a
+// double-buffered LDS stage in the swizzled layout the MFMA fragment reads
+// use.  One barrier per chunk: a stage is rewritten two chunks later, after
+// every wave has passed the barrier that follows its last read.  The barrier
+// is a bare s_barrier after an LDS-only wait, so the global loads in flight
+// are never drained.  Same block shape and epilogue as the DMA kernel.
+constexpr int kRRing = 4;      // 64-deep chunks in flight per wave
+
+// s_waitcnt immediate: lgkmcnt(0), vmcnt and expcnt unrestricted
+constexpr int lgkm_zero_imm() { return 15 | (7 << 4) | (3 << 14); }
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(lgkm_zero_imm());
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int NT, int NW>
+__global__ __launch_bounds__(64 * NW) void lmhead_ring_kernel(const uint16_t* __restrict__ X,
+                                                              int64_t M, int H,
+                                                              const uint16_t* __restrict__ W,
+                                                              int V, float4* __restrict__ part,
+                                                              int n_vt) {
+  constexpr int kBV = 32 * NW;               // vocabulary rows per block
+  constexpr int kBT = 32 * NT;
+  constexpr int kXP = 4 * NT / NW;           // X load instructions per wave per chunk
+  static_assert(kXP * NW == 4 * NT, "X rows split evenly over the waves");
+  constexpr int kStElems = (kBV + kBT) * kGKC;
+  __shared__ __align__(16) uint16_t s0[kStElems];
+  __shared__ __align__(16) uint16_t s1[kStElems];
+  __shared__ Stat red[kBT][NW];
+
+  const int vt = blockIdx.x;
+  const int v0 = vt * kBV;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 31, hh = lane >> 5;
+  const int lr = lane >> 3, lc = lane & 7;
+
+  // load plan: W rows 32*wave + 8*j + lr, X rows 8*(wave + NW*p) + lr, chunk
+  // lc of each 64-deep slice; LDS slot lc ^ ((row >> 1) & 7).  Rows past V
+  // or M are clamped (their results are discarded in the epilogue).
+  const uint16_t* wsrc[4];
+  int wdst[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int R = 32 * wave + 8 * j + lr;
+    wsrc[j] = W + static_cast<int64_t>(min(v0 + R, V - 1)) * H + 8 * lc;
+    wdst[j] = R * kGKC + ((lc ^ ((R >> 1) & 7)) << 3);
+  }
+  const uint16_t* xsrc[kXP];
+  int xdst[kXP];
+#pragma unroll
+  for (int p = 0; p < kXP; ++p) {
+    const int R = 8 * (wave + NW * p) + lr;
+    xsrc[p] = X + min(static_cast<int64_t>(R), M - 1) * H + 8 * lc;
+    xdst[p] = kBV * kGKC + R * kGKC + ((lc ^ ((R >> 1) & 7)) << 3);
+  }
+  u32x4 rw[kRRing][4], rx[kRRing][kXP];
+  auto load = [&](int slot, int kc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rw[slot][j] = ld16_nt(wsrc[j] + kc * kGKC);
+#pragma unroll
+    for (int p = 0; p < kXP; ++p) rx[slot][p] = ld16(xsrc[p] + kc * kGKC);
+  };
+  auto put = [&](int slot, uint16_t* stage) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st16(stage + wdst[j], rw[slot][j]);
+#pragma unroll
+    for (int p = 0; p < kXP; ++p) st16(stage + xdst[p], rx[slot][p]);
+  };
+
+  const int sw = (q >> 1) & 7;
+  const int aoff = (32 * wave + q) * kGKC;
+  const int boff = kBV * kGKC + q * kGKC;
+  f32x16 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[n][r] = 0.f;
+  auto compute = [&](const uint16_t* stage) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int so = ((2 * ks + hh) ^ sw) * 8;
+      const bf16x8 a = as_bf16x8(ld16(stage + aoff + so));
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        acc[n] = mma32_k16(a, as_bf16x8(ld16(stage + boff + n * 32 * kGKC + so)), acc[n]);
+    }
+  };
+
+  const int nk = H / kGKC;                 // a multiple of kRRing
+#pragma unroll
+  for (int p = 0; p < kRRing; ++p) load(p, p);
+  for (int c0 = 0; c0 < nk - kRRing; c0 += kRRing) {
+#pragma unroll
+    for (int p = 0; p < kRRing; ++p) {
+      uint16_t* stage = (p & 1) ? s1 : s0;
+      put(p, stage);
+      load(p, c0 + kRRing + p);
+      lds_barrier();
+      compute(stage);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kRRing; ++p) {
+    uint16_t* stage = (p & 1) ? s1 : s0;
+    put(p, stage);
+    lds_barrier();
+    compute(stage);
+  }
+
+  const int vbase = v0 + 32 * wave + 4 * hh;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    Stat st{-INFINITY, 0.f, INT_MAX};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int v = vbase + 8 * (r >> 2) + (r & 3);
+      if (v < V && acc[n][r] > st.m) {
+        st.m = acc[n][r];
+        st.a = v;
+      }
+    }
+    if (st.m != -INFINITY) {
+      const float ml = st.m * kLog2e;
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (vbase + 8 * (r >> 2) + (r & 3) < V) sum += exp2f(fmaf(acc[n][r], kLog2e, -ml));
+      st.s = sum;
+    }
+    Stat other;
+    other.m = shfl_xor_f(st.m, 32);
+    other.s = shfl_xor_f(st.s, 32);
+    other.a = shfl_xor_i(st.a, 32);
+    if (hh == 0) {
+      merge(st, other);
+      red[n * 32 + q][wave] = st;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kBT) {
+    const int c = threadIdx.x;
+    if (c < M) {
+      Stat st = red[c][0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) merge(st, red[c][w]);
+      part[static_cast<int64_t>(c) * n_vt + vt] = make_float4(st.m, st.s, __int_as_float(st.a), 0.f);
+    }
+  }
+}
+
 // One wave per row: each lane folds a strided subset of tiles in order, then
 // a fixed butterfly merges the lanes.
 __global__ __launch_bounds__(256) void lmhead_merge_kernel(const float4* __restrict__ part,
@@ -629,6 +787,53 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(const float4* __restr
   }
 }
 
+// Small M: one 256-thread block per row, so a row's tiles are read by 256
+// threads at once (each folds tiles t = tid, tid + 256, ... in order, four
+// loads in flight), then a fixed butterfly in each wave and the four waves in
+// order.  The fold order depends only on n_vt: results are reproducible.
+__global__ __launch_bounds__(256) void lmhead_merge_row_kernel(const float4* __restrict__ part,
+                                                               int n_vt,
+                                                               float* __restrict__ conf,
+                                                               int32_t* __restrict__ argmax,
+                                                               float* __restrict__ lse) {
+  __shared__ Stat wst[4];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float4* pr = part + row * n_vt;
+  Stat st{-INFINITY, 0.f, INT_MAX};
+  for (int t0 = tid; t0 < n_vt; t0 += 4 * 256) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + 256 * u;
+      v[u] = t < n_vt ? pr[t] : make_float4(-INFINITY, 0.f, __int_as_float(INT_MAX), 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) merge(st, Stat{v[u].x, v[u].y, __float_as_int(v[u].z)});
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    Stat o;
+    o.m = shfl_xor_f(st.m, m);
+    o.s = shfl_xor_f(st.s, m);
+    o.a = shfl_xor_i(st.a, m);
+    Stat lo = (lane & m) ? o : st;
+    const Stat hi = (lane & m) ? st : o;
+    merge(lo, hi);
+    st = lo;
+  }
+  if (lane == 0) wst[wave] = st;
+  __syncthreads();
+  if (tid == 0) {
+    Stat r = wst[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) merge(r, wst[w]);
+    conf[row] = 1.f / r.s;
+    argmax[row] = r.a;
+    if (lse) lse[row] = r.m + logf(r.s);
+  }
+}
+
 struct TileShape {
   int BV, BT;
 };
@@ -644,16 +849,24 @@ hipError_t run_tiles(const void* X, int64_t M, int H, const void* W, int V, floa
   return hipGetLastError();
 }
 
-// Kernel choice.  bf16 with W and X each addressable by a 32-bit buffer
-// descriptor: M <= 64 streams W once (lmhead_stream_kernel); larger M runs
-// the 256 x 256 tile GEMM (H in whole 128-deep pairs of chunks).  Anything
-// else (fp32, odd shapes) takes the generic tile kernel: 32 tokens x 128
-// vocabulary rows per block for M <= 32, 128 x 128 tiles otherwise.
+// Kernel choice.  bf16, M <= 64 streams W once: through the register ring
+// (H a multiple of 256), else through buffer-to-LDS loads (W and X each
+// addressable by a 32-bit buffer descriptor).  Larger M runs the 256 x 256
+// tile GEMM (H in whole 128-deep pairs of chunks).  Anything else (fp32,
+// odd shapes) takes the generic tile kernel: 32 tokens x 128 vocabulary rows
+// per block for M <= 32, 128 x 128 tiles otherwise.
 inline bool small_m(int64_t M) { return M <= 32; }
 inline bool bf16_buffers(int64_t M, int H, int V, int dtype) {
   return dtype == 1 && static_cast<int64_t>(V) * H * 2 < (int64_t(1) << 31) &&
          M * H * 2 < (int64_t(1) << 31);
 }
+inline bool ring_path(int64_t M, int H, int V, int dtype) {
+  return dtype == 1 && M <= 64 && H % (kGKC * kRRing) == 0;
+}
+// Waves (32 vocabulary rows each) per ring block: two below V = 65536 so
+// the grid still holds about 512 blocks or more (two streams per CU overlap
+// each other's start and end), four above.
+inline int ring_waves(int V) { return V < 65536 ? 2 : 4; }
 inline bool stream_path(int64_t M, int H, int V, int dtype) {
   return bf16_buffers(M, H, V, dtype) && M <= 64 && H % kGKC == 0;
 }
@@ -661,6 +874,7 @@ inline bool gemm_path(int64_t M, int H, int V, int dtype) {
   return bf16_buffers(M, H, V, dtype) && M > 64 && H % (2 * kGKC) == 0;
 }
 inline int tile_bv(int64_t M, int H, int V, int dtype) {
+  if (ring_path(M, H, V, dtype)) return 32 * ring_waves(V);
   return gemm_path(M, H, V, dtype) ? kGB : 128;
 }
 }  // namespace
@@ -675,7 +889,20 @@ hipError_t launch_lmhead(const void* X, int64_t M, int H, const void* W, int V, 
   const int n_vt = (V + tile_bv(M, H, V, dtype) - 1) / tile_bv(M, H, V, dtype);
   float4* part = static_cast<float4*>(ws);
   hipError_t e;
-  if (stream_path(M, H, V, dtype)) {
+  if (ring_path(M, H, V, dtype)) {
+    const uint16_t* x16 = static_cast<const uint16_t*>(X);
+    const uint16_t* w16 = static_cast<const uint16_t*>(W);
+    const int nw = ring_waves(V);
+    if (M <= 32 && nw == 2)
+      lmhead_ring_kernel<1, 2><<<dim3(n_vt), dim3(128), 0, st>>>(x16, M, H, w16, V, part, n_vt);
+    else if (M <= 32)
+      lmhead_ring_kernel<1, 4><<<dim3(n_vt), dim3(256), 0, st>>>(x16, M, H, w16, V, part, n_vt);
+    else if (nw == 2)
+      lmhead_ring_kernel<2, 2><<<dim3(n_vt), dim3(128), 0, st>>>(x16, M, H, w16, V, part, n_vt);
+    else
+      lmhead_ring_kernel<2, 4><<<dim3(n_vt), dim3(256), 0, st>>>(x16, M, H, w16, V, part, n_vt);
+    e = hipGetLastError();
+  } else if (stream_path(M, H, V, dtype)) {
     const dim3 grid(n_vt);
     if (M <= 32)
       lmhead_stream_kernel<1><<<grid, dim3(256), 0, st>>>(static_cast<const uint16_t*>(X), M, H,
@@ -700,8 +927,12 @@ hipError_t launch_lmhead(const void* X, int64_t M, int H, const void* W, int V, 
     e = small_m(M) ? run_tiles<F32, 4, 1, 1, 1>(X, M, H, W, V, part, n_vt, st)
                    : run_tiles<F32, 2, 2, 2, 2>(X, M, H, W, V, part, n_vt, st);
   if (e != hipSuccess) return e;
-  lmhead_merge_kernel<<<dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0, st>>>(
-      part, M, n_vt, conf, argmax, lse);
+  if (M <= 256)
+    lmhead_merge_row_kernel<<<dim3(static_cast<unsigned>(M)), dim3(256), 0, st>>>(
+        part, n_vt, conf, argmax, lse);
+  else
+    lmhead_merge_kernel<<<dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0, st>>>(
+        part, M, n_vt, conf, argmax, lse);
   return hipGetLastError();
 }
 

@@ -58,7 +58,9 @@ def _check_lmhead(X, W, conf, amax, lse, rows=None):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("M,H,V", [(1, 64, 100), (5, 128, 4096 + 77), (32, 256, 4096),
-                                   (33, 256, 1000), (200, 128, 3000), (300, 2048, 513)])
+                                   (33, 256, 1000), (200, 128, 3000), (300, 2048, 513),
+                                   (1, 512, 100), (17, 512, 4096 + 77), (40, 1024, 1000),
+                                   (64, 512, 257), (48, 256, 65536 + 11)])
 def test_lmhead_small(dtype, M, H, V):
     X = synth.normal_array((M, H), 11 + M, 1.0, dtype)
     W = synth.normal_array((V, H), 12 + V, 0.02, dtype)
