@@ -48,7 +48,10 @@ def parse():
     ap.add_argument("--workload", default="single4k")
     ap.add_argument("--cold-iters", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=2)
+    ap.add_argument("--cpu-blocks", type=int, default=8)
+    ap.add_argument("--profile-call", default=None,
+                    help="only launch this call --steps times (for rocprofv3 counter runs); "
+                         "'copy' launches a 256 MiB device-to-device copy for calibration")
     return ap.parse_args()
 
 
@@ -147,6 +150,30 @@ def cpu_baseline(x, wl, n_blocks):
                       f"fp64 NumPy, {dt:.2f} s"}
 
 
+def profile_call(args, blk, n_steps, torch):
+    """Launch one call (or a calibration copy) a few times and exit: a short
+    program for rocprofv3 counter passes."""
+    if args.profile_call == "copy":
+        n = 256 * 1024 * 1024 // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        fn = lambda: b.copy_(a)
+        what = "copy of 268435456 bytes"
+    else:
+        fns = {"lmhead_prefix": blk.prefix_confidence, "score": blk.score_prefix,
+               "prune": blk.prune_prefix, "attend_full": lambda: blk.attend(False),
+               "attend_pruned": lambda: blk.attend(True), "lmhead_block": blk.block_confidence,
+               "unmask": lambda: blk.unmask(1)}
+        blk.run_block(n_steps)
+        fn = fns[args.profile_call]
+        what = args.profile_call
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        fn()
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_call": what, "launches": args.steps}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -168,6 +195,10 @@ def main():
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name}, {props.multi_processor_count} CUs; kept "
         f"{blk.total_kept} of {lay.total_L} prefix positions")
+
+    if args.profile_call:
+        profile_call(args, blk, n_steps, torch)
+        return
 
     # ---------------------------------------------------------------- warmup
     for _ in range(args.warmup):
@@ -217,6 +248,11 @@ def main():
 
     g_sprint = capture(lambda: blk.run_block(n_steps))
     g_full = capture(lambda: blk.run_full_block(n_steps))
+    # SPRINT with every position kept (r_text = r_img = 1): the pruning pass's
+    # overhead without any attention saving
+    blk_r1 = SprintBlock(x, "cuda", r_text=1.0, r_img=1.0)
+    blk_r1.run_block(n_steps)
+    g_r1 = capture(lambda: blk_r1.run_block(n_steps))
     # a replay must leave exactly what an eager run leaves
     blk.run_block(n_steps)
     torch.cuda.synchronize()
@@ -230,10 +266,11 @@ def main():
         log("[bench] WARNING: graph replay differs from the eager run; reporting eager")
     _, t_graph = replay_rate(g_sprint, args.steps)
     _, t_full = replay_rate(g_full, args.steps)
+    _, t_r1 = replay_rate(g_r1, args.steps)
     t_sprint = t_graph if graph_ok else t_eager
     log(f"[bench] graph SPRINT block {t_graph * 1e3:.3f} ms, full-retention block "
         f"{t_full * 1e3:.3f} ms")
-    del g_sprint, g_full
+    del g_sprint, g_full, g_r1, blk_r1
 
     # ---------------------------------------------------------------- per-call GPU time
     reps = 20
@@ -259,12 +296,16 @@ def main():
                      "unmask": n_steps + 1}
 
     # ---------------------------------------------------------------- cold per-call timings
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    # cold: before each call, read a 512 MB buffer (twice the Infinity Cache)
+    # so the call's operands are not cached; a read leaves no dirty lines
+    # whose write-back would be charged to the call
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
     cold = EventTimer(torch)
 
     def cold_run(name, fn):
         for i in range(args.cold_iters):
-            flush.fill_(float(i))
+            torch.sum(flush, dim=0, out=sink)
             with cold(name):
                 fn()
     blk.reset()
@@ -303,10 +344,13 @@ def main():
         achieved = dw["bytes"] / dus / 1e3
         peak = HBM_PEAK_GBS
         unit = "GB/s"
+    cus = calls_cold[dominant]["median_us"]
+    cold_achieved = (dw["flops"] / cus / 1e6) if dw["bound"] == "mfma" else (dw["bytes"] / cus / 1e3)
     roofline = {"bound": dw["bound"], "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": load_traffic(dominant),
                 "kernel": dominant, "alg_per_launch": dw["flops"] if dw["bound"] == "mfma"
-                else dw["bytes"], "mean_launch_us": round(dus, 3)}
+                else dw["bytes"], "mean_launch_us": round(dus, 3),
+                "cold_launch_us": round(cus, 3), "cold_frac": round(cold_achieved / peak, 4)}
 
     att_pr = calls["attend_pruned"]["us"]
     att_full = calls["attend_full"]["us"]
@@ -344,6 +388,11 @@ def main():
                   "block_steps_per_s": round(steps_per_block / t_eager, 2)},
         "full_retention": {"block_ms": round(t_full * 1e3, 4),
                            "block_steps_per_s": round(steps_per_block / t_full, 2)},
+        "sprint_keep_all": {"block_ms": round(t_r1 * 1e3, 4),
+                            "block_steps_per_s": round(steps_per_block / t_r1, 2),
+                            "note": "r_text = r_img = 1: pruning-pass overhead only"},
+        "pruning_pass_us": round(calls["lmhead_prefix"]["us"] + calls["score"]["us"] +
+                                 calls["prune"]["us"], 2),
         "speedup_pruned_vs_full": {"attention_call": round(att_full / att_pr, 4),
                                    "denoising_step": round(step_full / step_pr, 4),
                                    "block": round(t_full / t_sprint, 4),
