@@ -658,10 +658,12 @@ AttnPlan attend_plan(int nseq, int Lq, int Hq, int Hkv, int D, int max_kv, int h
   p.rows = (Hq / Hkv) * Lq;
   const int64_t n_keys = static_cast<int64_t>(max_kv) + (has_block ? Lq : 0);
   const int64_t units = static_cast<int64_t>(nseq) * Hkv;
-  // Keys per range: the largest power of two (at least one 64-key stage)
-  // that still gives >= 192 blocks, so most CUs stream a range.
+  // Keys per range: the largest power of two that still gives >= 192 blocks,
+  // so most CUs stream a range, but at least two 64-key stages: below that a
+  // block is all fixed latency, and more ranges only add partials to write
+  // and combine (and past 256 blocks a second partial wave).
   int kps = 1 << 20;
-  while (kps > 2 * kKT && units * ((n_keys + kps - 1) / kps) < 192) kps >>= 1;
+  while (kps > 4 * kKT && units * ((n_keys + kps - 1) / kps) < 192) kps >>= 1;
   p.kps = kps;
   p.n_splits = static_cast<int>(n_keys > 0 ? (n_keys + kps - 1) / kps : 1);
   const size_t es = dtype == 1 ? 2 : 4;
