@@ -9,13 +9,16 @@
 //   and ALL R = (Hq/Hkv)*Lq query rows that read that head, as R/32 waves of
 //   32 rows.  Every K/V byte is fetched once per step and shared through LDS.
 //   The block's own K/V (the block keys) are the last tiles of the last range.
-// K/V tiles of 32 keys arrive by buffer loads straight into LDS
-//   (buffer_load_dwordx4 ... lds) into a ring of four stages, three tiles
-//   ahead of the one being used.  The stages are distinct LDS arrays and the
-//   loop is unrolled by four, so the compiler can see that reads of one stage
-//   do not alias loads into another; each wave waits (vmcnt) for its own
-//   loads of a stage, then a plain s_barrier (no fence, which would drain
-//   every outstanding load) publishes it.
+// K/V stages of 64 keys (two 32-key tiles) arrive by buffer loads straight
+//   into LDS (buffer_load_dwordx4 ... lds, non-temporal).  bf16 blocks of up
+//   to four waves run two blocks per CU, each with a ring of two stages (one
+//   in flight) and at most 256 registers per lane, so every SIMD interleaves
+//   two waves; other shapes use one block per CU with a ring of four stages
+//   (three in flight).  The stages are distinct LDS arrays and the loop is
+//   unrolled over them, so the compiler can see that reads of one stage do
+//   not alias loads into another; each wave waits (vmcnt) for its own loads
+//   of a stage, then a plain s_barrier (no fence, which would drain every
+//   outstanding load) publishes it.
 // Per tile and wave:
 //   S^T = K Q^T on MFMA 32x32x16 (A = key rows from LDS, B = the wave's
 //   queries held in registers).  The accumulator gives each lane one query
@@ -260,8 +263,13 @@ __device__ __forceinline__ void flush_rows(const char* reg, int lane, int nrows,
   }
 }
 
-template <typename T, int D, int NW, int NSUB>
-__global__ __launch_bounds__(64 * NW) void attend_split_kernel(AttnArgs args) {
+// STG = 4: one block per CU, a four-stage ring (three stages in flight).
+// STG = 2: two blocks per CU, each with a two-stage ring (one stage in
+// flight) and at most 256 registers per lane, so each SIMD interleaves two
+// waves: one wave's softmax and LDS latency under the other's MFMAs.
+template <typename T, int D, int NW, int NSUB, int STG>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(STG == 2 ? 2 : 1)))
+void attend_split_kernel(AttnArgs args) {
   using S = typename T::storage;
   using FR = Frag<T>;
   constexpr int KS = kKT * NSUB;                          // keys per pipeline stage
@@ -272,8 +280,8 @@ __global__ __launch_bounds__(64 * NW) void attend_split_kernel(AttnArgs args) {
   constexpr int kStageBytes = 2 * GEO::kTileBytes;       // K tile then V tile
   __shared__ __align__(16) char st0[kStageBytes];
   __shared__ __align__(16) char st1[kStageBytes];
-  __shared__ __align__(16) char st2[kStageBytes];
-  __shared__ __align__(16) char st3[kStageBytes];
+  __shared__ __align__(16) char st2[STG == 4 ? kStageBytes : 16];
+  __shared__ __align__(16) char st3[STG == 4 ? kStageBytes : 16];
 
   const int split = blockIdx.x % args.n_splits;
   const int g = (blockIdx.x / args.n_splits) % args.Hkv;
@@ -453,11 +461,30 @@ __global__ __launch_bounds__(64 * NW) void attend_split_kernel(AttnArgs args) {
       }
   };
 
+  constexpr int kPer = 2 * kP;   // vector-memory instructions per wave per tile
+  if constexpr (STG == 2) {
+    // one stage in flight: at step t only tile t is outstanding
+    if (0 < nt) issue(0, st0);
+#define SPRINT_ATT_STEP2(CUR, NXT, U)                                                     \
+  {                                                                                       \
+    const int t = tb + (U);                                                               \
+    if (t < nt) {                                                                         \
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));                                         \
+      __builtin_amdgcn_s_barrier();                                                       \
+      if (t + 1 < nt) issue(t + 1, NXT);                                                  \
+      compute(CUR, t);                                                                    \
+    }                                                                                     \
+  }
+    for (int tb = 0; tb < nt; tb += 2) {
+      SPRINT_ATT_STEP2(st0, st1, 0)
+      SPRINT_ATT_STEP2(st1, st0, 1)
+    }
+#undef SPRINT_ATT_STEP2
+  } else {
   // prologue: three stages in flight
   if (0 < nt) issue(0, st0);
   if (1 < nt) issue(1, st1);
   if (2 < nt) issue(2, st2);
-  constexpr int kPer = 2 * kP;   // vector-memory instructions per wave per tile
 #define SPRINT_ATT_STEP(CUR, NXT3, U)                                                     \
   {                                                                                       \
     const int t = tb + (U);                                                               \
@@ -480,6 +507,7 @@ __global__ __launch_bounds__(64 * NW) void attend_split_kernel(AttnArgs args) {
     SPRINT_ATT_STEP(st3, st2, 3)
   }
 #undef SPRINT_ATT_STEP
+  }
 
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -491,7 +519,7 @@ __global__ __launch_bounds__(64 * NW) void attend_split_kernel(AttnArgs args) {
   constexpr int kPartWave = RowGeo<PE, D>::kWaveBytes;
   constexpr int kWaveBytes = kOutWave > kPartWave ? kOutWave : kPartWave;
   constexpr int kWps = kStageBytes / kWaveBytes;                      // wave regions per stage
-  static_assert(kWps * kStages >= NW, "staging regions");
+  static_assert(kWps * STG >= NW, "staging regions");
   const int sidx = wave / kWps;
   char* reg = (sidx == 0 ? st0 : sidx == 1 ? st1 : sidx == 2 ? st2 : st3) +
               (wave % kWps) * kWaveBytes;
@@ -626,10 +654,16 @@ constexpr int nsub() {
   return sizeof(typename T::storage) == 2 ? 2 : 1;
 }
 
+// bf16 with up to four waves per block uses the two-stage, two-blocks-per-CU
+// form (about 15% faster than the four-stage ring at every cache size measured,
+// 3.5k to 28k keys); fp32 and eight-wave blocks keep the four-stage ring.
+constexpr int kSplitStages = 2;
+
 template <typename T, int D, int NW>
 hipError_t launch_split(const AttnArgs& a, hipStream_t st) {
   const int blocks = a.nseq * a.Hkv * a.n_splits;
-  attend_split_kernel<T, D, NW, nsub<T>()><<<dim3(blocks), dim3(64 * NW), 0, st>>>(a);
+  constexpr int stg = (sizeof(typename T::storage) == 2 && NW <= 4) ? kSplitStages : 4;
+  attend_split_kernel<T, D, NW, nsub<T>(), stg><<<dim3(blocks), dim3(64 * NW), 0, st>>>(a);
   return hipGetLastError();
 }
 
