@@ -372,42 +372,46 @@ __global__ __launch_bounds__(kGThreads) void lmhead_gemm_kernel(
   __syncthreads();
 
   // Epilogue: per token column fold this wave's 128 vocabulary rows, then
-  // the partner half-wave, then the other vocabulary wave through LDS.  Rows
-  // past V (only in the last vocabulary tile) are set to -inf first.
+  // the partner half-wave, then the other vocabulary wave through LDS.
+  // Per column a lane holds 64 logits (4 tiles x 16); rows ascend with
+  // (i, r).  One max, the lowest row holding it (scanning down, so the last
+  // match written is the lowest row), then one pass of raw exp2 (arguments
+  // <= 0) for the sum.  Rows past V exist only in the last vocabulary tile
+  // and are masked to -inf there.
   const int vbase = v0 + wv * 128 + 4 * hh;
-  const bool edge = v0 + kGB > V;             // only the last vocabulary tile
+  if (v0 + kGB > V) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (vbase + i * 32 + 8 * (r >> 2) + (r & 3) >= V) acc[i][j][r] = -INFINITY;
+  }
   Stat* red = reinterpret_cast<Stat*>(st0);   // [256 tokens][2 vocab waves]
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    // streaming fold over the four 32x32 tiles of this token column block,
-    // 16 accumulator values live at a time
-    float mx = -INFINITY, sum = 0.f;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
     int am = INT_MAX;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float z[16];
+    for (int i = 3; i >= 0; --i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        z[r] = acc[i][j][r];
-        if (edge && vbase + i * 32 + 8 * (r >> 2) + (r & 3) >= V) z[r] = -INFINITY;
-      }
-      float tm = -INFINITY;
-      int ta = INT_MAX;
+      for (int r = 15; r >= 0; --r)
+        am = acc[i][j][r] == mx ? vbase + i * 32 + 8 * (r >> 2) + (r & 3) : am;
+    float sum = 0.f;
+    if (mx != -INFINITY) {
+      const float ml = mx * kLog2e;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (z[r] > tm) {
-          tm = z[r];
-          ta = vbase + i * 32 + 8 * (r >> 2) + (r & 3);
-        }
-      if (tm == -INFINITY) continue;
-      const float mn = fmaxf(mx, tm);
-      const float ml = mn * kLog2e;
-      float ts = 0.f;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ts += exp2f(fmaf(z[r], kLog2e, -ml));
-      sum = (mx == -INFINITY ? 0.f : sum * exp2f(fmaf(mx, kLog2e, -ml))) + ts;
-      if (tm > mx) am = ta;     // rows ascend with i: strict '>' keeps the lowest index
-      mx = mn;
+        for (int r = 0; r < 16; ++r)
+          sum += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -ml));
+    } else {
+      am = INT_MAX;
     }
     Stat st{mx, sum, am};
     Stat other;
