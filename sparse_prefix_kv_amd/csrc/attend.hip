@@ -263,18 +263,11 @@ __device__ __forceinline__ void flush_rows(const char* reg, int lane, int nrows,
   }
 }
 
-// NG = 1, STG = 4: one block per CU, a four-stage ring (three stages in
-//   flight).
-// NG = 1, STG = 2: two blocks per CU, each with a two-stage ring (one stage
-//   in flight) and at most 256 registers per lane.
-// NG = 2: one block per CU with two groups of NW waves over the same rows;
-//   group g computes stages 2p + g of each pair p from a four-stage ring (one
-//   pair in flight), each group with its own online-softmax state, merged
-//   through LDS at the end.  Every SIMD interleaves two waves without adding
-//   key ranges (and so partials to combine).
-template <typename T, int D, int NW, int NSUB, int STG, int NG>
-__global__ __launch_bounds__(64 * NW * NG)
-__attribute__((amdgpu_waves_per_eu((STG == 2 || NG == 2) ? 2 : 1)))
+// STG = 4: one block per CU, a four-stage ring (three stages in flight).
+// STG = 2: two blocks per CU, each with a two-stage ring (one stage in
+//   flight) and at most 256 registers per lane.
+template <typename T, int D, int NW, int NSUB, int STG>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(STG == 2 ? 2 : 1)))
 void attend_split_kernel(AttnArgs args) {
   using S = typename T::storage;
   using FR = Frag<T>;
@@ -282,12 +275,12 @@ void attend_split_kernel(AttnArgs args) {
   using GEO = TileGeo<T, D, KS>;
   constexpr bool kBf16 = GEO::kBf16;
   constexpr int kNI = GEO::kInstr;
-  constexpr int kNWT = NW * NG;                          // waves in the block
+  constexpr int kNWT = NW;                               // waves in the block
   constexpr int kP = (kNI + kNWT - 1) / kNWT;            // DMA instructions per wave per tensor
   constexpr int kStageBytes = 2 * GEO::kTileBytes;       // K tile then V tile
   __shared__ __align__(16) char st0[kStageBytes];
   __shared__ __align__(16) char st1[kStageBytes];
-  constexpr int kRing = NG == 2 ? 4 : STG;
+  constexpr int kRing = STG;
   __shared__ __align__(16) char st2[kRing == 4 ? kStageBytes : 16];
   __shared__ __align__(16) char st3[kRing == 4 ? kStageBytes : 16];
 
@@ -295,7 +288,7 @@ void attend_split_kernel(AttnArgs args) {
   const int g = (blockIdx.x / args.n_splits) % args.Hkv;
   const int seq = blockIdx.x / (args.n_splits * args.Hkv);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = wave / NW, rw = wave % NW;           // wave group, row wave
+  const int rw = wave;                                 // row wave
   const int lane = threadIdx.x & 63;
   const int q = lane & 31, hh = lane >> 5;
 
@@ -479,69 +472,7 @@ void attend_split_kernel(AttnArgs args) {
   };
 
   constexpr int kPer = 2 * kP;   // vector-memory instructions per wave per tile
-  if constexpr (NG == 2) {
-    // pair p = stages 2p, 2p + 1 in (st0, st1) for even p, (st2, st3) for odd
-    // p; group g computes stage 2p + g.  Pairs 0 and 1 are issued up front;
-    // afterwards pair p + 1 is issued at step p, once every wave is done with
-    // pair p - 1, whose stages it reuses.
-    auto issue_pair = [&](int p, char* sa, char* sb) {
-      if (2 * p < nt) issue(2 * p, sa);
-      if (2 * p + 1 < nt) issue(2 * p + 1, sb);
-    };
-    issue_pair(0, st0, st1);
-    issue_pair(1, st2, st3);
-    const int np = (nt + 1) / 2;
-    const int n1 = min(nt, 4) - min(nt, 2);               // stages of pair 1
-#define SPRINT_ATT_PAIR(SA, SB, OA, OB, U)                                                \
-  {                                                                                       \
-    const int p = pb + (U);                                                               \
-    if (p < np) {                                                                         \
-      if (p == 0 && n1 == 2)                                                              \
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * kPer));                                \
-      else if (p == 0 && n1 == 1)                                                         \
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(kPer));                                    \
-      else                                                                                \
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));                                       \
-      __builtin_amdgcn_s_barrier();                                                       \
-      if (p >= 1 && p + 1 < np) issue_pair(p + 1, OA, OB);                                \
-      const int t = 2 * p + grp;                                                          \
-      if (t < nt) compute(grp ? SB : SA, t);                                              \
-    }                                                                                     \
-  }
-    for (int pb = 0; pb < np; pb += 2) {
-      SPRINT_ATT_PAIR(st0, st1, st2, st3, 0)
-      SPRINT_ATT_PAIR(st2, st3, st0, st1, 1)
-    }
-#undef SPRINT_ATT_PAIR
-    // merge group 1's state into group 0's, through LDS (row wave rw uses
-    // stage rw: D/2 + 2 floats per lane)
-    __syncthreads();
-    float* mg = reinterpret_cast<float*>(rw == 0 ? st0 : rw == 1 ? st1 : rw == 2 ? st2 : st3);
-    constexpr int kAcc = D / 2;                          // accumulators per lane
-    static_assert((kAcc + 2) * 64 * 4 <= kStageBytes, "group merge region");
-    if (grp == 1) {
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mg[(mt * 16 + r) * 64 + lane] = acc_o[mt][r];
-      mg[kAcc * 64 + lane] = m_run;
-      mg[(kAcc + 1) * 64 + lane] = l_run;
-    }
-    __syncthreads();
-    if (grp == 0) {
-      const float m1 = mg[kAcc * 64 + lane], l1 = mg[(kAcc + 1) * 64 + lane];
-      const float mn = fmaxf(m_run, m1);
-      const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
-      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mn);
-      l_run = l_run * a0 + l1 * a1;
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc_o[mt][r] = acc_o[mt][r] * a0 + mg[(mt * 16 + r) * 64 + lane] * a1;
-      m_run = mn;
-    }
-  } else if constexpr (STG == 2) {
+  if constexpr (STG == 2) {
     // one stage in flight: at step t only tile t is outstanding
     if (0 < nt) issue(0, st0);
 #define SPRINT_ATT_STEP2(CUR, NXT, U)                                                     \
@@ -591,7 +522,6 @@ void attend_split_kernel(AttnArgs args) {
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int nrows = max(0, min(32, args.R - rw * 32));
-  const bool act = grp == 0;                           // group 0 holds the merged state
   // this wave's staging region: after the barrier the stages are free
   __syncthreads();
   using PE = typename std::conditional<kBf16, half_t, float>::type;   // partial element
@@ -605,10 +535,9 @@ void attend_split_kernel(AttnArgs args) {
               (rw % kWps) * kWaveBytes;
   if (args.n_splits == 1) {
     // the block saw every key: write O directly
-    if (act) stage_rows<S, D>(reg, acc_o, inv, q, hh);
+    stage_rows<S, D>(reg, acc_o, inv, q, hh);
     __syncthreads();
-    if (act)
-      flush_rows<S, D>(reg, lane, nrows, [&](int rr) {
+    flush_rows<S, D>(reg, lane, nrows, [&](int rr) {
         const int rh = rw * 32 + rr;
         const int hd = g * args.G + rh / args.Lq;
         return args.O + ((static_cast<int64_t>(seq) * args.Lq + rh % args.Lq) * args.Hq + hd) *
@@ -618,9 +547,8 @@ void attend_split_kernel(AttnArgs args) {
   }
   const int64_t pbase =
       ((static_cast<int64_t>(seq) * args.Hkv + g) * args.n_splits + split) * args.R + rw * 32;
-  if (act) stage_rows<PE, D>(reg, acc_o, inv, q, hh);
+  stage_rows<PE, D>(reg, acc_o, inv, q, hh);
   __syncthreads();
-  if (!act) return;
   flush_rows<PE, D>(reg, lane, nrows, [&](int rr) {
     return static_cast<char*>(args.part_o) + (pbase + rr) * static_cast<int64_t>(D * sizeof(PE));
   });
@@ -741,15 +669,11 @@ constexpr int nsub() {
 // 3.5k to 28k keys); fp32 and eight-wave blocks keep the four-stage ring.
 constexpr int kSplitStages = 2;
 
-constexpr int kSplitGroups = 1;
-
 template <typename T, int D, int NW>
 hipError_t launch_split(const AttnArgs& a, hipStream_t st) {
   const int blocks = a.nseq * a.Hkv * a.n_splits;
-  constexpr bool kSmall = sizeof(typename T::storage) == 2 && NW <= 4;
-  constexpr int stg = kSmall ? kSplitStages : 4;
-  constexpr int ng = kSmall ? kSplitGroups : 1;
-  attend_split_kernel<T, D, NW, nsub<T>(), stg, ng><<<dim3(blocks), dim3(64 * NW * ng), 0, st>>>(a);
+  constexpr int stg = (sizeof(typename T::storage) == 2 && NW <= 4) ? kSplitStages : 4;
+  attend_split_kernel<T, D, NW, nsub<T>(), stg><<<dim3(blocks), dim3(64 * NW), 0, st>>>(a);
   return hipGetLastError();
 }
 

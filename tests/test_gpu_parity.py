@@ -174,6 +174,7 @@ PRUNE_LAYOUTS = [
     [((0, 1),), ((1, 1),), ((0, 3), (1, 4)), ((1, 2000), (0, 70), (1, 1000))],
     [((0, 100),)],
     [((1, 3333),)],
+    [((0, 10), (1, 5)), (), ((1, 20),), ()],          # empty sequences
 ]
 
 

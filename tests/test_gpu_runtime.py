@@ -1,0 +1,105 @@
+"""Runtime properties the C ABI promises beyond parity: bitwise-reproducible
+results, correct use of the caller's stream, and whole blocks that replay
+correctly as HIP graphs (each replay checked against an eager run, with eager
+work and synchronisations in between)."""
+import numpy as np
+import pytest
+import torch
+
+from sparse_prefix_kv_amd import sprint, synth
+from sparse_prefix_kv_amd.block import SprintBlock, _to_dev
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def _f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def _u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(DEV)
+
+
+def _attend_inputs(kv_lens, seed):
+    nseq, Lq, Hq, Hkv, D = len(kv_lens), 32, 16, 4, 128
+    cu = np.concatenate([[0], np.cumsum(kv_lens)]).astype(np.int32)
+    Q = _to_dev(synth.normal_array((nseq, Lq, Hq, D), seed, 1.0, "bf16"), "bf16", DEV)
+    K = _to_dev(synth.normal_array((cu[-1], Hkv, D), seed + 1, 1.0, "bf16"), "bf16", DEV)
+    V = _to_dev(synth.normal_array((cu[-1], Hkv, D), seed + 2, 1.0, "bf16"), "bf16", DEV)
+    Kb = _to_dev(synth.normal_array((nseq, Lq, Hkv, D), seed + 3, 1.0, "bf16"), "bf16", DEV)
+    Vb = _to_dev(synth.normal_array((nseq, Lq, Hkv, D), seed + 4, 1.0, "bf16"), "bf16", DEV)
+    return Q, K, V, _i32(cu), int(max(kv_lens)), Kb, Vb
+
+
+def test_repeated_calls_are_bitwise_identical():
+    Q, K, V, cu, mx, Kb, Vb = _attend_inputs([3000, 11000], 5)
+    o1 = sprint.block_attend(Q, K, V, cu, mx, Kb, Vb)
+    o2 = sprint.block_attend(Q, K, V, cu, mx, Kb, Vb)
+    assert torch.equal(o1, o2)
+    for M, H, V_ in [(32, 2048, 32768), (4096, 2048, 4096), (40, 256, 1000)]:
+        X = _to_dev(synth.normal_array((M, H), M, 1.0, "bf16"), "bf16", DEV)
+        W = _to_dev(synth.normal_array((V_, H), V_, 0.02, "bf16"), "bf16", DEV)
+        c1, a1 = sprint.lmhead_confidence(X, W)
+        c2, a2 = sprint.lmhead_confidence(X, W)
+        assert torch.equal(c1, c2) and torch.equal(a1, a2)
+    lay = synth.layout_from_runs([((0, 1000), (1, 3000)), ((1, 500),)])
+    Kk = _to_dev(synth.normal_array((lay.total_L, 4, 128), 9, 1.0, "bf16"), "bf16", DEV)
+    conf = _f32(synth.random_scores(lay.total_L, 3, 0))
+    cu_l = _i32(lay.cu_len)
+    i1, s1 = sprint.sprint_score(Kk, conf, cu_l)
+    i2, s2 = sprint.sprint_score(Kk, conf, cu_l)
+    assert torch.equal(i1, i2) and torch.equal(s1, s2)
+
+
+def test_calls_run_on_the_given_stream():
+    Q, K, V, cu, mx, Kb, Vb = _attend_inputs([4000], 6)
+    ref = sprint.block_attend(Q, K, V, cu, mx, Kb, Vb)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out = torch.empty_like(ref)
+    with torch.cuda.stream(side):
+        # a long producer on the side stream first: the call must queue behind it
+        big = torch.ones(64 << 20, device=DEV)
+        big.mul_(2.0)
+        sprint.block_attend(Q, K, V, cu, mx, Kb, Vb, O=out, stream=side)
+    side.synchronize()
+    assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "single4k"])
+def test_block_graph_replays_match_eager(name):
+    x = synth.make_inputs(synth.WORKLOADS[name], 0)
+    blk = SprintBlock(x, DEV)
+    n_steps = (blk.T - 1) if blk.T is not None else blk.Lq - 1
+
+    def state():
+        return (blk.tokens.clone(), blk.masked.clone(), blk.kept_idx.clone(), blk.O.clone(),
+                blk.conf_blk.clone())
+
+    blk.run_block(n_steps)
+    torch.cuda.synchronize()
+    ref = state()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        blk.run_block(n_steps)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        blk.run_block(n_steps)
+    for rep in range(3):
+        blk.tokens.fill_(-7)          # eager work between replays
+        blk.O.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = state()
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), f"replay {rep} differs"
+    del g
