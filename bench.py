@@ -10,10 +10,11 @@ single-sequence prefix of 4096 positions (1024 text + 3072 image), 16/4
 heads of dim 128, vocabulary 32768, pass + 8 steps.
 
 Printed: one JSON line.  `value` is denoising block-steps per second
-(1 pass + 8 pruned steps = 9 block-steps per block and sequence) of the
-whole block replayed as one HIP graph (launch overhead off the GPU's
-critical path), after checking that a replay leaves exactly the state an
-eager run leaves.  The same line carries the eager (host-launched) rate, the
+(1 pass + 8 pruned steps = 9 block-steps per block and sequence): the faster
+of the whole block replayed as one HIP graph (after checking that a replay
+leaves exactly the state an eager run leaves) and the same blocks launched
+eagerly from the host; `timing` names which.  The same line carries both
+rates, the
 full-retention baseline, per-call GPU times (each call captured 20 times
 back to back in a graph, HIP events around the replay on the stream it runs
 on; and cache-flushed single calls), the roofline of the dominant call and
@@ -267,7 +268,10 @@ def main():
     _, t_graph = replay_rate(g_sprint, args.steps)
     _, t_full = replay_rate(g_full, args.steps)
     _, t_r1 = replay_rate(g_r1, args.steps)
-    t_sprint = t_graph if graph_ok else t_eager
+    # the same verified work launched two ways; the faster is the headline
+    t_sprint = min(t_graph, t_eager) if graph_ok else t_eager
+    timing = ("HIP graph replay of whole blocks" if graph_ok and t_graph <= t_eager
+              else "eager launches (host-queued)")
     log(f"[bench] graph SPRINT block {t_graph * 1e3:.3f} ms, full-retention block "
         f"{t_full * 1e3:.3f} ms")
     del g_sprint, g_full, g_r1, blk_r1
@@ -383,9 +387,12 @@ def main():
                    "steps_per_block": n_steps + 1, "r_text": blk.r_text, "r_img": blk.r_img,
                    "tau": blk.tau, "step_unit": "one whole block (pass + pruned steps)"},
         "tokens_per_s": round(wl.Lq * lay.nseq / t_sprint, 1),
-        "timing": "HIP graph replay of whole blocks" if graph_ok else "eager",
+        "timing": timing,
         "eager": {"block_ms": round(t_eager * 1e3, 4),
                   "block_steps_per_s": round(steps_per_block / t_eager, 2)},
+        "graph": {"block_ms": round(t_graph * 1e3, 4),
+                  "block_steps_per_s": round(steps_per_block / t_graph, 2),
+                  "replay_matches_eager": bool(graph_ok)},
         "full_retention": {"block_ms": round(t_full * 1e3, 4),
                            "block_steps_per_s": round(steps_per_block / t_full, 2)},
         "sprint_keep_all": {"block_ms": round(t_r1 * 1e3, 4),
