@@ -169,6 +169,28 @@ int unmask_select(const float* conf, const int32_t* argmax, int32_t nseq, int32_
                   int32_t steps_left, uint8_t* masked, int32_t* tokens, int32_t* n_accepted,
                   void* stream);
 
+/* ------------------------------------------------------------------------
+ * Prefix growth between blocks (block-wise generation, SPRINT introduction;
+ * Sparse Prefix Retention: each block's first step sees the complete cache,
+ * so a finished block joins the prefix before the next block is scored and
+ * pruned).  Appends n_blk rows to every sequence of a packed array:
+ *   out rows [cu_old[s] + s*n_blk, cu_old[s+1] + s*n_blk) = old rows
+ *   [cu_old[s], cu_old[s+1]), followed by blk rows [s*n_blk, (s+1)*n_blk).
+ * Rows are opaque bytes (K, V, hidden-state or modality rows), bit-copied.
+ *   old    [total_old rows of row_bytes], packed by cu_old [nseq+1] int32
+ *          (cu_old[0] = 0, non-decreasing, cu_old[nseq] = total_old)
+ *   blk    [nseq * n_blk rows] (sequence s's rows first-to-last)
+ *   out    [total_old + nseq*n_blk rows] out; must not overlap old or blk
+ *   cu_out [nseq+1] int32 out, cu_old[s] + s*n_blk; may be NULL; must not
+ *          alias cu_old
+ * Rows of 16-byte multiples with 16-byte aligned pointers move as 16-byte
+ * vectors, other rows byte by byte.  Rows whose sequence range is
+ * inconsistent with total_old are left unwritten (no out-of-range access).
+ * ------------------------------------------------------------------------ */
+int sprint_append_rows(const void* old, const int32_t* cu_old, int32_t nseq, int64_t total_old,
+                       const void* blk, int32_t n_blk, int64_t row_bytes, void* out,
+                       int32_t* cu_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,4 +7,5 @@ from .sprint_oracle import *  # noqa: F401,F403
 from .sprint_oracle import (attention, compact, composite_score, fixed_schedule_count,
                             keep_count, key_norm_importance, key_norms, lmhead_confidence,
                             lmhead_top2_gap, min_acceptances, run_block, select_kept,
-                            unmask_select, BlockResult)
+                            unmask_select, BlockResult, append_block, store_as,
+                            run_generation)

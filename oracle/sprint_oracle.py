@@ -27,6 +27,13 @@ pools all runs of that modality in the sequence; GQA head h reads KV head
 floor(h*Hkv/Hq); scores are scaled by 1/sqrt(D); "exceeds tau" is strict;
 m is the current masked count and t the 0-based step.
 
+Generation over several blocks (``append_block``, ``store_as``,
+``run_generation``) reads the SPRINT introduction's B blocks x T steps with
+the pass of "Sparse Prefix Retention" seeing the complete prefix: a finished
+block's own K/V rows, its last step's outputs (as the hidden states of its
+positions, stored in the workload's dtype) and the generated modality join
+every sequence before the next block.
+
 Parity status: every function below is pinned by the tests in
 ``tests/test_oracle_pins.py`` (closed forms, invariants, brute force).  The
 one thing no pin can reach is the *reading* of the lost score equation
@@ -321,3 +328,76 @@ def run_block(Q, K, V, Kb, Vb, hidden, W, cu_len, modality, r_text, r_img,
         res.tokens.append(tokens.copy())
         res.n_accepted.append(nacc)
     return res
+
+
+# --------------------------------------------------------------------------
+# Block-wise generation: B blocks over a growing prefix
+# --------------------------------------------------------------------------
+
+def append_block(old, cu_len, blk):
+    """Prefix growth between blocks (SPRINT introduction: blocks are generated
+    one after another; Sparse Prefix Retention: a block's first step sees the
+    complete prefix, earlier blocks included).
+
+    old: rows [total, ...] packed by cu_len [nseq+1]; blk: [nseq, n_blk, ...].
+    Sequence s of the result holds its old rows, then its block rows.
+    Returns (new rows, new cu_len).
+    """
+    old = np.asarray(old)
+    blk = np.asarray(blk)
+    cu = np.asarray(cu_len, dtype=np.int64)
+    nseq = len(cu) - 1
+    parts = []
+    for s in range(nseq):
+        parts.append(old[cu[s]:cu[s + 1]])
+        parts.append(blk[s])
+    new = np.concatenate(parts, axis=0) if parts else old[:0]
+    n_blk = blk.shape[1]
+    cu_new = cu + n_blk * np.arange(nseq + 1, dtype=np.int64)
+    return new, cu_new
+
+
+def store_as(x, dtype: str) -> np.ndarray:
+    """Values as the workload stores them: float32 ("f32") or bfloat16 ("bf16",
+    round to nearest, ties to even), returned as float64."""
+    x32 = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    if dtype == "f32":
+        return x32.astype(np.float64)
+    bits = x32.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    bits = ((bits + 0x7FFF + lsb) >> 16) << 16
+    return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def run_generation(blocks, K, V, hidden, W, cu_len, modality, gen_modality: int, r_text, r_img,
+                   tau, T: Optional[int], n_steps: int, dtype: str, alpha: float = 0.5):
+    """B SPRINT blocks one after another (SPRINT introduction; Sparse Prefix
+    Retention; Non-uniform Token Unmasking).
+
+    blocks: list of (Q, Kb, Vb) per block.  Block b runs run_block over the
+    prefix grown by blocks < b; afterwards its own K/V rows, its last step's
+    outputs (the hidden states of its positions, stored in `dtype`) and
+    `gen_modality` are appended to every sequence.  Returns the BlockResult
+    of every block and the prefix layouts (cu_len) they saw.
+    """
+    cu = np.asarray(cu_len, dtype=np.int64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    hidden = np.asarray(hidden, dtype=np.float64)
+    modality = np.asarray(modality)
+    results, layouts = [], []
+    for b, (Q, Kb, Vb) in enumerate(blocks):
+        res = run_block(Q, K, V, Kb, Vb, hidden, W, cu, modality, r_text, r_img, tau, T,
+                        n_steps, alpha)
+        results.append(res)
+        layouts.append(cu.copy())
+        if b + 1 == len(blocks):
+            break
+        nseq, Lq, Hq, D = np.asarray(Q).shape
+        O = store_as(res.outputs[-1], dtype).reshape(nseq, Lq, Hq * D)
+        K, _ = append_block(K, cu, Kb)
+        V, _ = append_block(V, cu, Vb)
+        hidden, _ = append_block(hidden, cu, O)
+        modality, cu = append_block(modality, cu,
+                                    np.full((nseq, Lq), gen_modality, dtype=modality.dtype))
+    return results, layouts

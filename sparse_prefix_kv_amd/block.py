@@ -41,7 +41,9 @@ class SprintBlock:
 
     def __init__(self, x: synth.Inputs, device="cuda", r_text: Optional[float] = None,
                  r_img: Optional[float] = None, tau: Optional[float] = None,
-                 T: Optional[int] = "wl", alpha: Optional[float] = None):
+                 T: Optional[int] = "wl", alpha: Optional[float] = None, grow: int = 0):
+        """`grow`: rows per sequence the prefix may gain later (blocks appended
+        by a generation loop); buffers and workspaces are sized for it once."""
         wl = x.wl
         lay = x.layout
         self.wl, self.layout = wl, lay
@@ -54,37 +56,31 @@ class SprintBlock:
         self.device = dev
         dt = wl.dtype
         self.nseq, self.Lq, self.Hq, self.Hkv, self.D = lay.nseq, wl.Lq, wl.Hq, wl.Hkv, wl.D
-        self.total_L = lay.total_L
         self.Q = _to_dev(x.Q, dt, dev)
-        self.K = _to_dev(x.K, dt, dev)
-        self.V = _to_dev(x.V, dt, dev)
         self.Kb = _to_dev(x.Kb, dt, dev)
         self.Vb = _to_dev(x.Vb, dt, dev)
-        self.hidden = _to_dev(x.hidden, dt, dev) if x.hidden is not None else None
         self.W = _to_dev(x.W, dt, dev)
-        self.cu_len = torch.from_numpy(lay.cu_len.astype(np.int32)).to(dev)
-        self.modality = torch.from_numpy(lay.modality).to(dev)
-        self.max_len = int(lay.lens.max())
-        keep, cu_kept, total_kept = sprint.sprint_plan_keep(lay.n_text, lay.n_img, self.r_text,
-                                                            self.r_img)
-        self.keep_host, self.cu_kept_host, self.total_kept = keep, cu_kept, total_kept
-        self.keep = torch.tensor(keep, dtype=torch.int32, device=dev)
-        self.cu_kept = torch.tensor(cu_kept, dtype=torch.int32, device=dev)
-        self.max_kept = int(np.max(np.diff(cu_kept)))
-        tl, tk = self.total_L, max(total_kept, 1)
-        f32, i32 = torch.float32, torch.int32
-        self.conf_prefix = torch.empty(tl, dtype=f32, device=dev)
-        self.argmax_prefix = torch.empty(tl, dtype=i32, device=dev)
-        self.ibar = torch.empty(tl, dtype=f32, device=dev)
-        self.score = torch.empty(tl, dtype=f32, device=dev)
-        self.K_pr = torch.empty((tk, self.Hkv, self.D), dtype=self.K.dtype, device=dev)[:total_kept]
-        self.V_pr = torch.empty((tk, self.Hkv, self.D), dtype=self.K.dtype, device=dev)[:total_kept]
-        self.kept_idx = torch.empty(tk, dtype=i32, device=dev)[:total_kept]
+        f32, i32, u8 = torch.float32, torch.int32, torch.uint8
+        # largest prefix this object will see: every sequence grown by `grow`
+        lens_max = lay.lens.astype(np.int64) + grow
+        tl_max = int(lens_max.sum())
+        _, cu_kept_max, kept_max = sprint.sprint_plan_keep(lay.n_text + grow, lay.n_img + grow,
+                                                           self.r_text, self.r_img)
+        tk_max = max(kept_max, 1)
+        self._cap_L = max(tl_max, 1)
+        self.conf_prefix_buf = torch.empty(self._cap_L, dtype=f32, device=dev)
+        self.argmax_prefix_buf = torch.empty(self._cap_L, dtype=i32, device=dev)
+        self.ibar_buf = torch.empty(self._cap_L, dtype=f32, device=dev)
+        self.score_buf = torch.empty(self._cap_L, dtype=f32, device=dev)
+        kdt = self.Q.dtype
+        self.K_pr_buf = torch.empty((tk_max, self.Hkv, self.D), dtype=kdt, device=dev)
+        self.V_pr_buf = torch.empty((tk_max, self.Hkv, self.D), dtype=kdt, device=dev)
+        self.kept_idx_buf = torch.empty(tk_max, dtype=i32, device=dev)
         self.O = torch.empty_like(self.Q)
         M = self.nseq * self.Lq
         self.conf_blk = torch.empty(M, dtype=f32, device=dev)
         self.argmax_blk = torch.empty(M, dtype=i32, device=dev)
-        self.masked = torch.ones((self.nseq, self.Lq), dtype=torch.uint8, device=dev)
+        self.masked = torch.ones((self.nseq, self.Lq), dtype=u8, device=dev)
         self.tokens = torch.full((self.nseq, self.Lq), -1, dtype=i32, device=dev)
         # block-start state (all masked), restored by a device copy so that a
         # captured graph holds no memset node
@@ -94,18 +90,57 @@ class SprintBlock:
         self.n_acc = torch.empty(self.nseq, dtype=i32, device=dev)
         dti = sprint.BF16 if dt == "bf16" else sprint.F32
         H, Vv = wl.H, wl.vocab
-        u8 = torch.uint8
+        max_len_max = int(lens_max.max())
+        max_kept_max = int(np.max(np.diff(cu_kept_max)))
 
         def ws(n):
             return torch.empty(max(int(n), 256), dtype=u8, device=dev)
-        self.ws_lm_prefix = ws(sprint.lmhead_confidence_ws(tl, H, Vv, dti)) if tl else None
+        # workspace sizes grow with the sizes they are queried for
+        self.ws_lm_prefix = ws(sprint.lmhead_confidence_ws(self._cap_L, H, Vv, dti))
         self.ws_lm_blk = ws(sprint.lmhead_confidence_ws(M, H, Vv, dti))
-        self.ws_score = ws(sprint.sprint_score_ws(tl, self.nseq))
-        self.ws_prune = ws(sprint.sprint_prune_kv_ws(tl, self.nseq))
-        self.ws_att_full = ws(sprint.block_attend_ws(self.nseq, self.Lq, self.Hq, self.Hkv, self.D,
-                                                     self.max_len, True))
-        self.ws_att_pr = ws(sprint.block_attend_ws(self.nseq, self.Lq, self.Hq, self.Hkv, self.D,
-                                                   self.max_kept, True))
+        self.ws_score = ws(sprint.sprint_score_ws(self._cap_L, self.nseq))
+        self.ws_prune = ws(sprint.sprint_prune_kv_ws(self._cap_L, self.nseq))
+        # the attention split plan is not monotone in the cache length: size
+        # for every length the prefix can pass through
+        def att_ws(lo, hi):
+            return max(sprint.block_attend_ws(self.nseq, self.Lq, self.Hq, self.Hkv, self.D, n, True)
+                       for n in range(int(lo), int(hi) + 1))
+        _, cu_kept0, _ = sprint.sprint_plan_keep(lay.n_text, lay.n_img, self.r_text, self.r_img)
+        self.ws_att_full = ws(att_ws(lay.lens.max(), max_len_max))
+        self.ws_att_pr = ws(att_ws(np.max(np.diff(cu_kept0)), max_kept_max))
+        # the workload's own prefix
+        K = _to_dev(x.K, dt, dev)
+        V = _to_dev(x.V, dt, dev)
+        hidden = _to_dev(x.hidden, dt, dev) if x.hidden is not None else None
+        cu_len = torch.from_numpy(lay.cu_len.astype(np.int32)).to(dev)
+        modality = torch.from_numpy(lay.modality).to(dev)
+        keep, cu_kept, total_kept = sprint.sprint_plan_keep(lay.n_text, lay.n_img, self.r_text,
+                                                            self.r_img)
+        self.set_prefix(K, V, hidden, modality, cu_len, lay.lens,
+                        torch.tensor(keep, dtype=i32, device=dev),
+                        torch.tensor(cu_kept, dtype=i32, device=dev), cu_kept)
+
+    def set_prefix(self, K, V, hidden, modality, cu_len, lens, keep, cu_kept, cu_kept_host):
+        """Point the block at a (possibly grown) prefix: device K, V, hidden,
+        modality and cu_len; host `lens` per sequence; device keep/cu_kept and
+        the host copy of cu_kept (from sprint_plan_keep)."""
+        tl = int(K.shape[0])
+        if tl > self._cap_L:
+            raise ValueError(f"prefix of {tl} rows exceeds the {self._cap_L} sized for")
+        self.K, self.V, self.hidden, self.modality, self.cu_len = K, V, hidden, modality, cu_len
+        self.total_L = tl
+        self.max_len = int(np.max(lens))
+        self.keep, self.cu_kept = keep, cu_kept
+        self.cu_kept_host = list(cu_kept_host)
+        self.total_kept = int(cu_kept_host[-1])
+        self.max_kept = int(np.max(np.diff(cu_kept_host)))
+        self.conf_prefix = self.conf_prefix_buf[:tl]
+        self.argmax_prefix = self.argmax_prefix_buf[:tl]
+        self.ibar = self.ibar_buf[:tl]
+        self.score = self.score_buf[:tl]
+        self.K_pr = self.K_pr_buf[:self.total_kept]
+        self.V_pr = self.V_pr_buf[:self.total_kept]
+        self.kept_idx = self.kept_idx_buf[:self.total_kept]
 
     # ------------------------------------------------------------------ pieces
     def steps_left(self, t: int) -> int:

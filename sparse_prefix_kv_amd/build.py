@@ -33,7 +33,8 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
-SOURCES = ["abi.hip", "score.hip", "prune.hip", "attend.hip", "lmhead.hip", "unmask.hip"]
+SOURCES = ["abi.hip", "score.hip", "prune.hip", "attend.hip", "lmhead.hip", "unmask.hip",
+           "append.hip"]
 
 
 def _compile(src: str) -> str:

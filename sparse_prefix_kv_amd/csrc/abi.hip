@@ -195,4 +195,31 @@ int unmask_select(const float* conf, const int32_t* argmax, int32_t nseq, int32_
                                  n_accepted, as_stream(stream)));
 }
 
+// ---------------------------------------------------------------- append
+int sprint_append_rows(const void* old, const int32_t* cu_old, int32_t nseq, int64_t total_old,
+                       const void* blk, int32_t n_blk, int64_t row_bytes, void* out,
+                       int32_t* cu_out, void* stream) {
+  if (nseq < 1 || n_blk < 0 || total_old < 0 || row_bytes < 1 || row_bytes > (int64_t(1) << 31))
+    return SPRINT_EINVAL;
+  if (!dev4(cu_old) || (cu_out != nullptr && (!aligned(cu_out, 4) || cu_out == cu_old)))
+    return SPRINT_EINVAL;
+  const int64_t total_rows = total_old + static_cast<int64_t>(nseq) * n_blk;
+  if (total_rows > INT32_MAX) return SPRINT_EINVAL;
+  if (total_old > 0 && old == nullptr) return SPRINT_EINVAL;
+  if (n_blk > 0 && blk == nullptr) return SPRINT_EINVAL;
+  if (total_rows > 0 && out == nullptr) return SPRINT_EINVAL;
+  // out must not overlap either source
+  const auto overlaps = [](const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && pa < pb + static_cast<uintptr_t>(nb) &&
+           pb < pa + static_cast<uintptr_t>(na);
+  };
+  const int64_t out_bytes = total_rows * row_bytes;
+  if (overlaps(out, out_bytes, old, total_old * row_bytes) ||
+      overlaps(out, out_bytes, blk, static_cast<int64_t>(nseq) * n_blk * row_bytes))
+    return SPRINT_EINVAL;
+  return status_of(launch_append_rows(old, cu_old, nseq, total_old, blk, n_blk, row_bytes, out,
+                                      cu_out, as_stream(stream)));
+}
+
 }  // extern "C"

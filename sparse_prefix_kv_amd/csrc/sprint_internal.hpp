@@ -48,4 +48,9 @@ hipError_t launch_unmask(const float* conf, const int32_t* argmax, int nseq, int
                          int steps_left, uint8_t* masked, int32_t* tokens, int32_t* n_accepted,
                          hipStream_t st);
 
+// ---- prefix growth between blocks
+hipError_t launch_append_rows(const void* old, const int32_t* cu_old, int nseq, int64_t total_old,
+                              const void* blk, int n_blk, int64_t row_bytes, void* out,
+                              int32_t* cu_out, hipStream_t st);
+
 }  // namespace sprint

@@ -8,6 +8,7 @@ computation happens in the library's HIP kernels; there is no fallback.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional, Sequence
 
@@ -49,6 +50,8 @@ _SIGS = {
                                     _c_void_p, _c_void_p, _size, _c_void_p]),
     "unmask_select": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _f32, _i32, _c_void_p,
                                      _c_void_p, _c_void_p, _c_void_p]),
+    "sprint_append_rows": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i64, _c_void_p, _i32, _i64,
+                                          _c_void_p, _c_void_p, _c_void_p]),
 }
 
 EXPORTS = tuple(_SIGS)
@@ -246,3 +249,36 @@ def unmask_select(conf, argmax, masked, tokens, tau: float, steps_left: int, n_a
         _ptr(conf), _ptr(argmax), nseq, Lq, float(tau), int(steps_left), _ptr(masked),
         _ptr(tokens), _ptr(n_accepted), _stream(stream)))
     return n_accepted
+
+
+def sprint_append_rows(old, cu_old, blk, out=None, cu_out=None, stream=None):
+    """Append each sequence's block rows after its packed rows (prefix growth).
+
+    old [total_old, ...] packed by cu_old [nseq+1]; blk [nseq, n_blk, ...] or
+    [nseq*n_blk, ...] with the same row shape and dtype.  Returns (out, cu_out).
+    """
+    _dev(old, "old")
+    _dev(blk, "blk")
+    if old.dtype != blk.dtype:
+        raise TypeError("old and blk must share a dtype")
+    nseq = cu_old.numel() - 1
+    row_shape = tuple(old.shape[1:])
+    row_elems = math.prod(row_shape)
+    total_old = old.shape[0]
+    if row_elems == 0 or blk.numel() % (row_elems * nseq) != 0:
+        raise ValueError("blk must hold whole rows of old's shape, the same count per sequence")
+    n_blk = blk.numel() // (row_elems * nseq)
+    row_bytes = old.element_size() * row_elems
+    total = total_old + nseq * n_blk
+    dev = old.device
+    out = torch.empty((total, *row_shape), dtype=old.dtype, device=dev) if out is None else out
+    _dev(out, "out")
+    if out.shape[0] < total:
+        raise ValueError("out has fewer rows than old + block rows")
+    if cu_out is None:
+        cu_out = torch.empty(nseq + 1, dtype=torch.int32, device=dev)
+    _check("sprint_append_rows", lib().sprint_append_rows(
+        _ptr(old) if total_old else None, _ptr(cu_old), nseq, total_old,
+        _ptr(blk) if n_blk else None, n_blk, row_bytes, _ptr(out) if total else None,
+        _ptr(cu_out), _stream(stream)))
+    return out, cu_out

@@ -21,6 +21,11 @@ Draw order (numpy ``default_rng(seed)``, one generator, in this order):
   8. W ~ N(0, 0.02^2)      [Vocab, H]
 Values are drawn in float32; bf16 workloads round them to nearest-even bf16
 (the float32 arrays then hold exactly the bf16 values).
+
+Generation over several blocks: block 0 uses the draws above; block b >= 1
+draws its own Q, Kb, Vb (same shapes and laws, in that order) from
+``default_rng([seed, b])``.  The rows a finished block adds to the prefix
+are not drawn: they are that block's own K/V and outputs.
 """
 from __future__ import annotations
 
@@ -50,6 +55,7 @@ class Workload:
     tau: float = 0.95
     T: Optional[int] = 9            # steps per block incl. the pass; None: >=1 per step
     alpha: float = 0.5
+    gen_modality: int = TEXT        # modality of the positions a generation appends
     desc: str = ""
 
     @property
@@ -82,8 +88,9 @@ WORKLOADS: Dict[str, Workload] = {
              "pass + 8 steps"),
     "imggen16k": Workload(
         "imggen16k", "bf16", Hq=16, Hkv=4, D=128, Lq=32, vocab=32768,
-        segments=(((TEXT, 512), (IMAGE, 15872)),), T=9,
-        desc="bf16, prefix 16384 = 512 text + 15872 image, H 2048, V 32768"),
+        segments=(((TEXT, 512), (IMAGE, 15872)),), T=9, gen_modality=IMAGE,
+        desc="bf16, prefix 16384 = 512 text + 15872 image, H 2048, V 32768, "
+             "blocks of image positions"),
     "ragged8": Workload(
         "ragged8", "bf16", Hq=16, Hkv=4, D=128, Lq=32, vocab=65536,
         ragged=(8, 2048, 16384, 0.25, 0.9), T=9,
@@ -203,6 +210,20 @@ def make_inputs(wl: Workload, seed: int = 0, with_lmhead: bool = True,
             hidden = bf16_round(hidden)
             W = bf16_round(W)
     return Inputs(wl, lay, Q, K, V, Kb, Vb, hidden, W, ks)
+
+
+def make_block_inputs(wl: Workload, nseq: int, b: int, seed: int = 0):
+    """Q, Kb, Vb of block b >= 1 of a generation (see module docstring)."""
+    if b < 1:
+        raise ValueError("block 0 takes its inputs from make_inputs")
+    rng = np.random.default_rng([seed, b])
+    f32 = np.float32
+    Q = rng.standard_normal((nseq, wl.Lq, wl.Hq, wl.D), dtype=f32)
+    Kb = rng.standard_normal((nseq, wl.Lq, wl.Hkv, wl.D), dtype=f32)
+    Vb = rng.standard_normal((nseq, wl.Lq, wl.Hkv, wl.D), dtype=f32)
+    if wl.dtype == "bf16":
+        Q, Kb, Vb = (bf16_round(a) for a in (Q, Kb, Vb))
+    return Q, Kb, Vb
 
 
 # ---------------------------------------------------------------------------

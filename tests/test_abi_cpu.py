@@ -25,7 +25,7 @@ def _header_functions():
 def test_library_exports_every_declared_function():
     lib = sprint.lib()
     declared = _header_functions()
-    assert len(declared) >= 13
+    assert len(declared) >= 14
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(sprint.EXPORTS)
@@ -128,3 +128,24 @@ def test_attend_and_unmask_reject_before_hip():
     assert _call("unmask_select", *a) == 1
     a = list(um); a[6] = None
     assert _call("unmask_select", *a) == 1
+
+
+def test_append_rejects_before_hip():
+    # old, cu_old, nseq, total_old, blk, n_blk, row_bytes, out, cu_out, stream
+    ap = [FAKE, FAKE, 2, 100, FAKE + (1 << 20), 32, 1024, FAKE + (1 << 24), FAKE + 64, None]
+    a = list(ap); a[2] = 0
+    assert _call("sprint_append_rows", *a) == 1                     # no sequences
+    a = list(ap); a[5] = -1
+    assert _call("sprint_append_rows", *a) == 1                     # negative block rows
+    a = list(ap); a[6] = 0
+    assert _call("sprint_append_rows", *a) == 1                     # empty rows
+    a = list(ap); a[8] = FAKE
+    assert _call("sprint_append_rows", *a) == 1                     # cu_out aliases cu_old
+    a = list(ap); a[7] = FAKE + 1024
+    assert _call("sprint_append_rows", *a) == 1                     # out overlaps old
+    a = list(ap); a[7] = FAKE + (1 << 20) + 64
+    assert _call("sprint_append_rows", *a) == 1                     # out overlaps blk
+    a = list(ap); a[0] = None
+    assert _call("sprint_append_rows", *a) == 1                     # NULL old with rows
+    a = list(ap); a[1] = FAKE + 2
+    assert _call("sprint_append_rows", *a) == 1                     # misaligned cu_old

@@ -418,3 +418,114 @@ def test_block_pruned_counts_and_validity():
     assert _dominance_ok(r.score, set(r.kept_idx.tolist()) & set(img), img)
     assert abs(r.ibar.sum() - 32) < 1e-12
     assert r.masks[-1].sum() == 0
+
+
+# -------------------------------------------------------------- generation
+
+def test_append_block_hand_example_and_empty_sequence():
+    # sequences of 2, 0 and 3 rows, two block rows each
+    old = np.arange(10).reshape(5, 2)
+    blk = np.arange(100, 112).reshape(3, 2, 2)
+    new, cu = oracle.append_block(old, [0, 2, 2, 5], blk)
+    assert new.tolist() == [[0, 1], [2, 3], [100, 101], [102, 103],
+                            [104, 105], [106, 107],
+                            [4, 5], [6, 7], [8, 9], [108, 109], [110, 111]]
+    assert cu.tolist() == [0, 4, 6, 11]
+
+
+def test_append_block_single_sequence_is_concatenate_and_removal_inverts():
+    rng = np.random.default_rng(5)
+    old = rng.standard_normal((7, 3, 4))
+    blk = rng.standard_normal((1, 5, 3, 4))
+    new, cu = oracle.append_block(old, [0, 7], blk)
+    np.testing.assert_array_equal(new, np.concatenate([old, blk[0]]))
+    assert cu.tolist() == [0, 12]
+    # several sequences: dropping each sequence's last n_blk rows gives old back,
+    # and those rows are the sequence's block rows in order
+    lens = [4, 0, 9, 1]
+    cu0 = np.concatenate([[0], np.cumsum(lens)])
+    old = rng.standard_normal((int(cu0[-1]), 6))
+    blk = rng.standard_normal((4, 3, 6))
+    new, cu1 = oracle.append_block(old, cu0, blk)
+    assert len(new) == len(old) + 12
+    keep = np.ones(len(new), bool)
+    for s in range(4):
+        keep[cu1[s + 1] - 3:cu1[s + 1]] = False
+        np.testing.assert_array_equal(new[cu1[s + 1] - 3:cu1[s + 1]], blk[s])
+    np.testing.assert_array_equal(new[keep], old)
+
+
+def test_store_as_rounds_like_torch_bfloat16():
+    import torch
+    rng = np.random.default_rng(2)
+    x = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-6, 6, 4000),
+                        [1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 0.0, 2.0 ** -130]])
+    got = oracle.store_as(x, "bf16")
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(got, ref)
+    # halfway cases go to the even neighbour
+    assert got[-5] == 1.0 and got[-4] == 1 + 2.0 ** -6 and got[-3] == -1.0
+    np.testing.assert_array_equal(oracle.store_as(x, "f32"), x.astype(np.float32))
+
+
+def _gen_inputs(n_blocks, seed=0, gen_modality=0):
+    wl = synth.Workload("t", "f32", Hq=4, Hkv=2, D=8, Lq=6, vocab=64,
+                        segments=(((0, 14), (1, 10)), ((1, 9), (0, 3))), tau=0.9, T=4,
+                        r_text=1.0, r_img=0.5, gen_modality=gen_modality)
+    x = synth.make_inputs(wl, seed)
+    blocks = [(x.Q, x.Kb, x.Vb)] + [synth.make_block_inputs(wl, 2, b, seed)
+                                    for b in range(1, n_blocks)]
+    return wl, x, blocks
+
+
+def test_generation_one_block_is_run_block():
+    wl, x, blocks = _gen_inputs(1)
+    lay = x.layout
+    res, lays = oracle.run_generation(blocks, x.K, x.V, x.hidden, x.W, lay.cu_len, lay.modality,
+                                      0, 1.0, 0.5, 0.9, 4, 3, "f32")
+    one = oracle.run_block(x.Q, x.K, x.V, x.Kb, x.Vb, x.hidden, x.W, lay.cu_len, lay.modality,
+                           1.0, 0.5, 0.9, 4, 3)
+    np.testing.assert_array_equal(res[0].kept_idx, one.kept_idx)
+    np.testing.assert_array_equal(res[0].tokens[-1], one.tokens[-1])
+    assert len(res) == 1 and lays[0].tolist() == lay.cu_len.tolist()
+
+
+@pytest.mark.parametrize("gen_modality", [0, 1])
+def test_generation_prefix_grows_by_finished_blocks(gen_modality):
+    B = 3
+    wl, x, blocks = _gen_inputs(B, seed=4, gen_modality=gen_modality)
+    lay = x.layout
+    res, lays = oracle.run_generation(blocks, x.K, x.V, x.hidden, x.W, lay.cu_len, lay.modality,
+                                      gen_modality, 1.0, 0.5, 0.9, 4, 3, "f32")
+    for b in range(B):
+        cu = lays[b]
+        # every sequence has grown by one block per finished block
+        np.testing.assert_array_equal(np.diff(cu), lay.lens + b * wl.Lq)
+        # keep counts follow the grown modality counts
+        n_gen = b * wl.Lq
+        for s in range(2):
+            nt = int(lay.n_text[s]) + (n_gen if gen_modality == 0 else 0)
+            ni = int(lay.n_img[s]) + (n_gen if gen_modality == 1 else 0)
+            kept_s = res[b].cu_kept[s + 1] - res[b].cu_kept[s]
+            assert kept_s == nt + ni // 2
+        assert res[b].masks[-1].sum() == 0
+    # block 1's key norms see block 0's own keys at the end of each sequence:
+    # recompute the norms of those rows from Kb directly
+    cu1 = lays[1]
+    Kb0 = blocks[0][1]
+    for s in range(2):
+        rows = np.arange(cu1[s + 1] - wl.Lq, cu1[s + 1])
+        n_rows = np.sqrt((Kb0[s].astype(np.float64) ** 2).sum(axis=(1, 2)))
+        seg = np.arange(cu1[s], cu1[s + 1])
+        # I_i / I_j = n_i / n_j within a sequence
+        ratio = res[1].ibar[rows] / res[1].ibar[seg[0]]
+        n0 = np.sqrt((x.K[lay.cu_len[s]].astype(np.float64) ** 2).sum())
+        np.testing.assert_allclose(ratio, n_rows / n0, rtol=1e-12)
+    # block 1's prefix confidences of block 0's rows come from block 0's last
+    # outputs, stored as float32
+    O0 = res[0].outputs[-1].astype(np.float32).astype(np.float64)
+    c, _, _ = oracle.lmhead_confidence(O0.reshape(2 * wl.Lq, -1), x.W)
+    for s in range(2):
+        rows = np.arange(cu1[s + 1] - wl.Lq, cu1[s + 1])
+        np.testing.assert_allclose(res[1].conf_prefix[rows], c[s * wl.Lq:(s + 1) * wl.Lq],
+                                   rtol=1e-12)
