@@ -29,6 +29,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -50,6 +52,8 @@ def parse():
     ap.add_argument("--cold-iters", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=8)
+    ap.add_argument("--gen-blocks", type=int, default=8,
+                    help="blocks of the generation measurement (0: skip it)")
     ap.add_argument("--profile-call", default=None,
                     help="only launch this call --steps times (for rocprofv3 counter runs); "
                          "'copy' launches a 256 MiB device-to-device copy for calibration")
@@ -175,13 +179,88 @@ def profile_call(args, blk, n_steps, torch):
     print(json.dumps({"profile_call": what, "launches": args.steps}), flush=True)
 
 
+def measure_generation(args, x, wl, n_steps, torch, reps=5):
+    """B consecutive blocks over a growing prefix (each block's rows join the
+    prefix before the next pass), SPRINT vs the unpruned baseline, plus the
+    steps each block actually needs under the adaptive schedule."""
+    from sparse_prefix_kv_amd.gen import SprintGeneration
+    B = args.gen_blocks
+    gen = SprintGeneration(x, B, "cuda")
+    nseq, Lq = gen.nseq, gen.Lq
+
+    def timed(full):
+        gen.run(n_steps, full=full)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            gen.run(n_steps, full=full)
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[len(ts) // 2]
+    t_sp = timed(False)
+    t_full = timed(True)
+    # steps until every position of the block is accepted (host-checked here,
+    # outside the timed runs)
+    blk = gen.blk
+    finished, max_conf = [], 0.0
+    for b in range(B):
+        gen.begin_block(b)
+        blk.reset()
+        blk.pruning_pass(not gen.conf_carried(b))
+        t = 0
+        max_conf = max(max_conf, float(blk.conf_blk.max().item()))
+        while int(blk.masked.sum().item()) > 0 and t < n_steps:
+            t += 1
+            blk.pruned_step(t)
+            max_conf = max(max_conf, float(blk.conf_blk.max().item()))
+        finished.append(t + 1)
+        gen.finish_block(b)
+    # the same generation recomputing every prefix confidence at each pass
+    gen_re = SprintGeneration(x, B, "cuda", carry_conf=False)
+    gen_re.run(n_steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        gen_re.run(n_steps)
+    torch.cuda.synchronize()
+    t_re = (time.perf_counter() - t0) / reps
+    del gen_re
+    torch.cuda.synchronize()
+    T = n_steps + 1
+    m0 = Lq
+    per_step = -(-m0 // T)
+    fixed_steps = -(-m0 // per_step)
+    prefix_last = int(np.sum(gen.lens[-1]))
+    return {
+        "blocks": B, "steps_budget_T": T,
+        "prefix_first": int(x.layout.total_L), "prefix_last": prefix_last,
+        "sprint": {"ms": round(t_sp * 1e3, 3), "blocks_per_s": round(B / t_sp, 2),
+                   "tokens_per_s": round(B * Lq * nseq / t_sp, 1),
+                   "block_steps_per_s": round(B * T * nseq / t_sp, 1)},
+        "full_prefix": {"ms": round(t_full * 1e3, 3), "blocks_per_s": round(B / t_full, 2),
+                        "tokens_per_s": round(B * Lq * nseq / t_full, 1)},
+        "sprint_recomputed_conf": {"ms": round(t_re * 1e3, 3),
+                                   "blocks_per_s": round(B / t_re, 2),
+                                   "note": "every pass runs the LM head over the whole prefix"},
+        "speedup": round(t_full / t_sp, 4),
+        "adaptive_steps_per_block": finished,
+        "fixed_schedule_steps_per_block": fixed_steps,
+        "max_block_confidence": round(max_conf, 6), "tau": gen.blk.tau,
+        "note": "timed runs launch all T steps of every block (pass + T-1 pruned); the "
+                "steps a block needs are counted separately with a host check per step"
+                + ("; no confidence exceeds tau with these random weights, so the adaptive "
+                   "schedule accepts only its minimum ceil(m/(T-t)) per step"
+                   if max_conf <= gen.blk.tau else ""),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the SPRINT block step runs on a single MI355X here).", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
     from sparse_prefix_kv_amd import synth
     from sparse_prefix_kv_amd.block import SprintBlock
@@ -361,6 +440,14 @@ def main():
     step_pr = att_pr + calls["lmhead_block"]["us"] + calls["unmask"]["us"]
     step_full = att_full + calls["lmhead_block"]["us"] + calls["unmask"]["us"]
 
+    # ---------------------------------------------------------------- generation
+    generation = None
+    if args.gen_blocks > 0:
+        generation = measure_generation(args, x, wl, n_steps, torch)
+        log(f"[bench] generation of {args.gen_blocks} blocks: "
+            f"{generation['sprint']['blocks_per_s']:.1f} blocks/s SPRINT, "
+            f"{generation['full_prefix']['blocks_per_s']:.1f} blocks/s full prefix")
+
     # ---------------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -405,6 +492,7 @@ def main():
                                    "block": round(t_full / t_sprint, 4),
                                    "pages_claim_context": "up to 1.6x end to end (model, "
                                                           "hardware and workload not given)"},
+        "generation": generation,
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,

@@ -120,10 +120,12 @@ class SprintBlock:
                         torch.tensor(keep, dtype=i32, device=dev),
                         torch.tensor(cu_kept, dtype=i32, device=dev), cu_kept)
 
-    def set_prefix(self, K, V, hidden, modality, cu_len, lens, keep, cu_kept, cu_kept_host):
+    def set_prefix(self, K, V, hidden, modality, cu_len, lens, keep, cu_kept, cu_kept_host,
+                   conf=None):
         """Point the block at a (possibly grown) prefix: device K, V, hidden,
         modality and cu_len; host `lens` per sequence; device keep/cu_kept and
-        the host copy of cu_kept (from sprint_plan_keep)."""
+        the host copy of cu_kept (from sprint_plan_keep).  `conf`, if given, is
+        a device array already holding the prefix confidences."""
         tl = int(K.shape[0])
         if tl > self._cap_L:
             raise ValueError(f"prefix of {tl} rows exceeds the {self._cap_L} sized for")
@@ -134,7 +136,7 @@ class SprintBlock:
         self.cu_kept_host = list(cu_kept_host)
         self.total_kept = int(cu_kept_host[-1])
         self.max_kept = int(np.max(np.diff(cu_kept_host)))
-        self.conf_prefix = self.conf_prefix_buf[:tl]
+        self.conf_prefix = self.conf_prefix_buf[:tl] if conf is None else conf
         self.argmax_prefix = self.argmax_prefix_buf[:tl]
         self.ibar = self.ibar_buf[:tl]
         self.score = self.score_buf[:tl]
@@ -204,9 +206,12 @@ class SprintBlock:
         self.unmask(t)
 
     # ------------------------------------------------------------------ block
-    def pruning_pass(self):
-        """t = 0: full pass over the prefix, scoring and pruning, first unmask."""
-        self.prefix_confidence()
+    def pruning_pass(self, prefix_conf: bool = True):
+        """t = 0: full pass over the prefix, scoring and pruning, first unmask.
+        `prefix_conf=False` takes conf_prefix as already filled (a generation
+        loop that carries earlier blocks' confidences forward)."""
+        if prefix_conf:
+            self.prefix_confidence()
         self.score_and_prune()
         self.attend(pruned=False)
         self.confidence_and_unmask(0)
@@ -215,9 +220,9 @@ class SprintBlock:
         self.attend(pruned=True)
         self.confidence_and_unmask(t)
 
-    def run_block(self, n_steps: int):
+    def run_block(self, n_steps: int, prefix_conf: bool = True):
         self.reset()
-        self.pruning_pass()
+        self.pruning_pass(prefix_conf)
         for t in range(1, n_steps + 1):
             self.pruned_step(t)
 

@@ -86,11 +86,11 @@ def _kept_sets_agree(kept, res, cu, modality):
     return False
 
 
-def _gen_case(name, B, n_steps, oracle_steps, o_tol, conf_rtol):
+def _gen_case(name, B, n_steps, oracle_steps, o_tol, conf_rtol, carry_conf=True):
     wl = synth.WORKLOADS[name]
     x = synth.make_inputs(wl, 0)
     lay = x.layout
-    gen = SprintGeneration(x, B, DEV)
+    gen = SprintGeneration(x, B, DEV, carry_conf=carry_conf)
     seen = []
 
     def grab(b):
@@ -115,9 +115,10 @@ def _gen_case(name, B, n_steps, oracle_steps, o_tol, conf_rtol):
             tail = g["modality"][lays[b][s + 1] - b * wl.Lq:lays[b][s + 1]]
             assert np.all(tail == wl.gen_modality)
         # rows of the original prefix see the same hidden states on both sides;
-        # rows appended by finished blocks hold those blocks' outputs, which
-        # agree with the oracle's only to the attention tolerance (bf16
-        # probabilities in the P V product), so their confidences get 1e-2
+        # rows appended by finished blocks hold those blocks' outputs (carried
+        # confidences: the last step's block confidences), which agree with
+        # the oracle's only to the attention tolerance (bf16 probabilities in
+        # the P V product), so their confidences get 1e-2
         grown = np.zeros(len(g["conf"]), dtype=bool)
         for s in range(lay.nseq):
             grown[lays[b][s] + lay.lens[s]:lays[b][s + 1]] = True
@@ -134,8 +135,9 @@ def _gen_case(name, B, n_steps, oracle_steps, o_tol, conf_rtol):
     return gen, seen, res
 
 
-def test_generation_tiny_three_blocks():
-    gen, seen, res = _gen_case("tiny", 3, 31, 31, 1e-5, 1e-4)
+@pytest.mark.parametrize("carry_conf", [True, False])
+def test_generation_tiny_three_blocks(carry_conf):
+    gen, seen, res = _gen_case("tiny", 3, 31, 31, 1e-5, 1e-4, carry_conf)
     # one acceptance per step: where the oracle's first-step choice is unique,
     # the position taken with the full-prefix prediction and hence every
     # token agree (pruned steps all predict the same tokens)
