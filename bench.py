@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--cpu-blocks", type=int, default=8)
     ap.add_argument("--gen-blocks", type=int, default=8,
                     help="blocks of the generation measurement (0: skip it)")
+    ap.add_argument("--layers", type=int, default=16,
+                    help="layers of the several-layer measurement (0: skip it)")
     ap.add_argument("--profile-call", default=None,
                     help="only launch this call --steps times (for rocprofv3 counter runs); "
                          "'copy' launches a 256 MiB device-to-device copy for calibration")
@@ -255,6 +257,48 @@ def measure_generation(args, x, wl, n_steps, torch, reps=5):
     }
 
 
+def measure_layers(args, x, n_steps, torch, reps=5):
+    """A block of an n-layer stand-in (every layer its own prefix cache and
+    block inputs; LM head on the last layer): one kept set shared by all
+    layers, a set per layer, and the unpruned baseline."""
+    from sparse_prefix_kv_amd.layers import SprintLayers
+
+    def med(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[len(ts) // 2]
+
+    out = {"n_layers": args.layers,
+           "note": "layers run in order, one attention launch each; the LM head reads the "
+                   "last layer; layer inputs are independent draws (no layer weights)"}
+    blk = SprintLayers(x, args.layers, "cuda", mode="shared")
+    t_full = med(lambda: blk.run_full_block(n_steps))
+    blk.run_block(n_steps)
+    step_full = med(lambda: [blk.attend_layers(False), blk.confidence_and_unmask(1)])
+    step_pr = med(lambda: [blk.attend_layers(True), blk.confidence_and_unmask(1)])
+    for mode in ("shared", "per_layer"):
+        if mode != blk.mode:
+            del blk
+            torch.cuda.synchronize()
+            blk = SprintLayers(x, args.layers, "cuda", mode=mode)
+        t = med(lambda: blk.run_block(n_steps))
+        t_pass = med(lambda: [blk.prefix_confidence(), blk.score_and_prune()])
+        out[mode] = {"block_ms": round(t * 1e3, 4), "pruning_pass_ms": round(t_pass * 1e3, 4),
+                     "speedup_vs_full": round(t_full / t, 4)}
+    out["full_prefix"] = {"block_ms": round(t_full * 1e3, 4)}
+    out["step_ms"] = {"pruned": round(step_pr * 1e3, 4), "full": round(step_full * 1e3, 4),
+                      "speedup": round(step_full / step_pr, 4)}
+    del blk
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -448,6 +492,14 @@ def main():
             f"{generation['sprint']['blocks_per_s']:.1f} blocks/s SPRINT, "
             f"{generation['full_prefix']['blocks_per_s']:.1f} blocks/s full prefix")
 
+    # ---------------------------------------------------------------- several layers
+    layers = None
+    if args.layers > 0:
+        layers = measure_layers(args, x, n_steps, torch)
+        log(f"[bench] {args.layers} layers: block {layers['shared']['block_ms']:.3f} ms shared set, "
+            f"{layers['per_layer']['block_ms']:.3f} ms per-layer sets, "
+            f"{layers['full_prefix']['block_ms']:.3f} ms full prefix")
+
     # ---------------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -493,6 +545,7 @@ def main():
                                    "pages_claim_context": "up to 1.6x end to end (model, "
                                                           "hardware and workload not given)"},
         "generation": generation,
+        "layers": layers,
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,

@@ -131,6 +131,33 @@ int sprint_prune_kv(const float* score, const uint8_t* modality, const int32_t* 
                     size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Several layers sharing one kept set (Sparse Prefix Retention applied to a
+ * model whose every layer holds a prefix KV cache; the page scores positions,
+ * not layers, so one set serves every layer).  The key-norm importance is
+ * the mean over layers of each layer's mean-normalised key norm:
+ *   I_i = (1/n_layers) sum_l n_i^l / ((1/L) sum_{j in seq} n_j^l),
+ *   s_i = alpha * I_i + (1 - alpha) * c_i,
+ * and the kept set selected from s is compacted in every layer's cache.
+ *   K, V    [n_layers, total_L, Hkv, D] dtype (layer-major)
+ *   K_out, V_out [n_layers, total_kept, Hkv, D] dtype out
+ *   kept_idx [total_kept] int32 out (one set for all layers)
+ * Other arguments as for sprint_score / sprint_prune_kv; n_layers = 1 gives
+ * exactly their results.  1 <= n_layers <= 65535.  The prune's workspace is
+ * sprint_prune_kv_ws(total_L, nseq) for any number of layers.
+ * ------------------------------------------------------------------------ */
+size_t sprint_score_layers_ws(int64_t total_L, int32_t nseq, int32_t n_layers);
+int sprint_score_layers(const void* K, int32_t n_layers, const float* conf, const int32_t* cu_len,
+                        int32_t nseq, int64_t total_L, int32_t Hkv, int32_t D, int32_t dtype,
+                        float alpha, float* ibar, float* score, void* ws, size_t ws_bytes,
+                        void* stream);
+int sprint_prune_kv_layers(const float* score, const uint8_t* modality, const int32_t* cu_len,
+                           const int32_t* keep, const int32_t* cu_kept, int32_t nseq,
+                           int64_t total_L, int64_t total_kept, const void* K, const void* V,
+                           int32_t n_layers, int32_t Hkv, int32_t D, int32_t dtype, void* K_out,
+                           void* V_out, int32_t* kept_idx, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
  * Block attention of a denoising step: the block's queries attend, without a
  * mask, to [prefix cache ; the block's own keys] (the block is predicted from
  * the clean prefix and its own noisy tokens).  With GQA, query head h reads

@@ -8,4 +8,5 @@ from .sprint_oracle import (attention, compact, composite_score, fixed_schedule_
                             keep_count, key_norm_importance, key_norms, lmhead_confidence,
                             lmhead_top2_gap, min_acceptances, run_block, select_kept,
                             unmask_select, BlockResult, append_block, store_as,
-                            run_generation)
+                            run_generation, key_norm_importance_layers,
+                            run_block_layers, LayersResult)

@@ -401,3 +401,86 @@ def run_generation(blocks, K, V, hidden, W, cu_len, modality, gen_modality: int,
         modality, cu = append_block(modality, cu,
                                     np.full((nseq, Lq), gen_modality, dtype=modality.dtype))
     return results, layouts
+
+
+# --------------------------------------------------------------------------
+# Several layers: one kept set shared by every layer, or one set per layer
+# --------------------------------------------------------------------------
+
+def key_norm_importance_layers(K_layers, cu_len) -> np.ndarray:
+    """Layer-mean key-norm importance: I_i = (1/n_layers) sum_l I_i^l, where
+    I^l is the mean-normalised key norm of layer l's cache (Sparse Prefix
+    Retention scores positions; with several layers the per-layer importances
+    are averaged so that one kept set serves every layer)."""
+    return np.mean([key_norm_importance(K, cu_len) for K in K_layers], axis=0)
+
+
+@dataclass
+class LayersResult:
+    conf_prefix: np.ndarray
+    ibars: List[np.ndarray]          # one per layer, or one (the layer mean) when shared
+    scores: List[np.ndarray]
+    kept: List[np.ndarray]           # kept rows per layer (all equal when shared)
+    cu_kept: np.ndarray
+    outputs: List[List[np.ndarray]] = field(default_factory=list)   # per step, per layer
+    confs: List[np.ndarray] = field(default_factory=list)
+    masks: List[np.ndarray] = field(default_factory=list)
+    tokens: List[np.ndarray] = field(default_factory=list)
+
+
+def run_block_layers(layers, hidden, W, cu_len, modality, r_text, r_img, tau,
+                     T: Optional[int], n_steps: int, shared: bool = True,
+                     alpha: float = 0.5) -> LayersResult:
+    """One SPRINT block of a model with several layers, each with its own
+    prefix cache and its own block queries and K/V.
+
+    layers: list of (Q, K, V, Kb, Vb) per layer.  The prefix confidences come
+    from the LM head over `hidden` (one per position, for every layer).
+    shared: one kept set from the layer-mean importance, compacted in every
+    layer's cache; otherwise each layer keeps the top positions of its own
+    score.  Every step attends layer by layer; the LM head reads the last
+    layer's output (the layers' inputs are independent draws here, standing
+    in for the layers of one model).
+    """
+    cu = np.asarray(cu_len, dtype=np.int64)
+    nseq = len(cu) - 1
+    conf_prefix, _, _ = lmhead_confidence(hidden, W)
+    keep = np.zeros((nseq, 2), dtype=np.int64)
+    for s in range(nseq):
+        seg = np.asarray(modality)[cu[s]:cu[s + 1]]
+        keep[s, 0] = keep_count(r_text, int(np.sum(seg == 0)))
+        keep[s, 1] = keep_count(r_img, int(np.sum(seg == 1)))
+    cu_kept = np.zeros(nseq + 1, dtype=np.int64)
+    cu_kept[1:] = np.cumsum(keep.sum(axis=1))
+    if shared:
+        ibars = [key_norm_importance_layers([l[1] for l in layers], cu)]
+    else:
+        ibars = [key_norm_importance(l[1], cu) for l in layers]
+    scores = [composite_score(ib, conf_prefix, alpha) for ib in ibars]
+    kept_sets = [select_kept(sc, modality, cu, keep) for sc in scores]
+    if shared:
+        kept_sets = kept_sets * len(layers)
+    pruned = [compact(l[1], l[2], k) for l, k in zip(layers, kept_sets)]
+    res = LayersResult(conf_prefix, ibars, scores, kept_sets, cu_kept)
+    Q_last = np.asarray(layers[-1][0])
+    _, Lq, Hq, D = Q_last.shape
+    masked = np.ones((nseq, Lq), dtype=np.uint8)
+    tokens = np.full((nseq, Lq), -1, dtype=np.int64)
+    big = 1 << 30
+    for t in range(n_steps + 1):
+        outs = []
+        for (Q, K, V, Kb, Vb), (Kp, Vp) in zip(layers, pruned):
+            if t == 0:
+                outs.append(attention(Q, K, V, cu, Kb, Vb))
+            else:
+                outs.append(attention(Q, Kp, Vp, cu_kept, Kb, Vb))
+        conf, amax, _ = lmhead_confidence(outs[-1].reshape(nseq * Lq, Hq * D), W)
+        conf = conf.reshape(nseq, Lq)
+        amax = amax.reshape(nseq, Lq)
+        steps_left = big if T is None else T - t
+        masked, tokens, _ = unmask_select(conf, amax, masked, tokens, tau, steps_left)
+        res.outputs.append(outs)
+        res.confs.append(conf)
+        res.masks.append(masked.copy())
+        res.tokens.append(tokens.copy())
+    return res

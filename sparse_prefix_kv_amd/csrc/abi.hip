@@ -95,27 +95,70 @@ int lmhead_confidence(const void* hidden, int64_t M, int32_t H, const void* W, i
 }
 
 // ---------------------------------------------------------------- score
+static int score_impl(const void* K, int32_t n_layers, const float* conf, const int32_t* cu_len,
+                      int32_t nseq, int64_t total_L, int32_t Hkv, int32_t D, int32_t dtype,
+                      float alpha, float* ibar, float* score, void* ws, size_t ws_bytes,
+                      void* stream) {
+  if (!dtype_ok(dtype) || nseq < 1 || total_L < 0 || total_L > INT32_MAX || Hkv < 1)
+    return SPRINT_EINVAL;
+  if (n_layers < 1 || n_layers > 65535) return SPRINT_EINVAL;
+  if (!dev4(cu_len) || !isfinite(alpha)) return SPRINT_EINVAL;
+  if (!head_dim_ok(D)) return SPRINT_EUNSUPPORTED;
+  if (total_L > 0 && (!dev16(K) || !dev4(conf) || !dev4(ibar) || !dev4(score)))
+    return SPRINT_EINVAL;
+  const int st = check_ws(ws, ws_bytes, score_ws_bytes(total_L, nseq, n_layers));
+  if (st != SPRINT_OK) return st;
+  return status_of(launch_score(K, n_layers, conf, cu_len, nseq, total_L, Hkv, D, dtype, alpha,
+                                ibar, score, ws, as_stream(stream)));
+}
+
 size_t sprint_score_ws(int64_t total_L, int32_t nseq) {
   if (total_L < 0 || nseq < 1) return 0;
-  return score_ws_bytes(total_L, nseq);
+  return score_ws_bytes(total_L, nseq, 1);
 }
 
 int sprint_score(const void* K, const float* conf, const int32_t* cu_len, int32_t nseq,
                  int64_t total_L, int32_t Hkv, int32_t D, int32_t dtype, float alpha, float* ibar,
                  float* score, void* ws, size_t ws_bytes, void* stream) {
-  if (!dtype_ok(dtype) || nseq < 1 || total_L < 0 || total_L > INT32_MAX || Hkv < 1)
-    return SPRINT_EINVAL;
-  if (!dev4(cu_len) || !isfinite(alpha)) return SPRINT_EINVAL;
-  if (!head_dim_ok(D)) return SPRINT_EUNSUPPORTED;
-  if (total_L > 0 && (!dev16(K) || !dev4(conf) || !dev4(ibar) || !dev4(score)))
-    return SPRINT_EINVAL;
-  const int st = check_ws(ws, ws_bytes, score_ws_bytes(total_L, nseq));
-  if (st != SPRINT_OK) return st;
-  return status_of(launch_score(K, conf, cu_len, nseq, total_L, Hkv, D, dtype, alpha, ibar, score,
-                                ws, as_stream(stream)));
+  return score_impl(K, 1, conf, cu_len, nseq, total_L, Hkv, D, dtype, alpha, ibar, score, ws,
+                    ws_bytes, stream);
+}
+
+size_t sprint_score_layers_ws(int64_t total_L, int32_t nseq, int32_t n_layers) {
+  if (total_L < 0 || nseq < 1 || n_layers < 1) return 0;
+  return score_ws_bytes(total_L, nseq, n_layers);
+}
+
+int sprint_score_layers(const void* K, int32_t n_layers, const float* conf, const int32_t* cu_len,
+                        int32_t nseq, int64_t total_L, int32_t Hkv, int32_t D, int32_t dtype,
+                        float alpha, float* ibar, float* score, void* ws, size_t ws_bytes,
+                        void* stream) {
+  return score_impl(K, n_layers, conf, cu_len, nseq, total_L, Hkv, D, dtype, alpha, ibar, score,
+                    ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- prune
+static int prune_impl(const float* score, const uint8_t* modality, const int32_t* cu_len,
+                      const int32_t* keep, const int32_t* cu_kept, int32_t nseq, int64_t total_L,
+                      int64_t total_kept, const void* K, const void* V, int32_t n_layers,
+                      int32_t Hkv, int32_t D, int32_t dtype, void* K_out, void* V_out,
+                      int32_t* kept_idx, void* ws, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || nseq < 1 || total_L < 0 || total_L > INT32_MAX || Hkv < 1)
+    return SPRINT_EINVAL;
+  if (n_layers < 1 || n_layers > 65535) return SPRINT_EINVAL;
+  if (total_kept < 0 || total_kept > total_L) return SPRINT_EINVAL;
+  if (!dev4(cu_len) || !dev4(keep) || !dev4(cu_kept)) return SPRINT_EINVAL;
+  if (!head_dim_ok(D)) return SPRINT_EUNSUPPORTED;
+  if (total_L > 0 && (!dev4(score) || modality == nullptr || !dev16(K) || !dev16(V)))
+    return SPRINT_EINVAL;
+  if (total_kept > 0 && (!dev16(K_out) || !dev16(V_out) || !dev4(kept_idx))) return SPRINT_EINVAL;
+  const int st = check_ws(ws, ws_bytes, prune_ws_bytes(total_L, nseq));
+  if (st != SPRINT_OK) return st;
+  return status_of(launch_prune(score, modality, cu_len, keep, cu_kept, nseq, total_L, total_kept,
+                                K, V, n_layers, Hkv, D, dtype, K_out, V_out, kept_idx, ws,
+                                as_stream(stream)));
+}
+
 size_t sprint_prune_kv_ws(int64_t total_L, int32_t nseq) {
   if (total_L < 0 || nseq < 1) return 0;
   return prune_ws_bytes(total_L, nseq);
@@ -126,19 +169,18 @@ int sprint_prune_kv(const float* score, const uint8_t* modality, const int32_t* 
                     int64_t total_kept, const void* K, const void* V, int32_t Hkv, int32_t D,
                     int32_t dtype, void* K_out, void* V_out, int32_t* kept_idx, void* ws,
                     size_t ws_bytes, void* stream) {
-  if (!dtype_ok(dtype) || nseq < 1 || total_L < 0 || total_L > INT32_MAX || Hkv < 1)
-    return SPRINT_EINVAL;
-  if (total_kept < 0 || total_kept > total_L) return SPRINT_EINVAL;
-  if (!dev4(cu_len) || !dev4(keep) || !dev4(cu_kept)) return SPRINT_EINVAL;
-  if (!head_dim_ok(D)) return SPRINT_EUNSUPPORTED;
-  if (total_L > 0 && (!dev4(score) || modality == nullptr || !dev16(K) || !dev16(V)))
-    return SPRINT_EINVAL;
-  if (total_kept > 0 && (!dev16(K_out) || !dev16(V_out) || !dev4(kept_idx))) return SPRINT_EINVAL;
-  const int st = check_ws(ws, ws_bytes, prune_ws_bytes(total_L, nseq));
-  if (st != SPRINT_OK) return st;
-  return status_of(launch_prune(score, modality, cu_len, keep, cu_kept, nseq, total_L, total_kept,
-                                K, V, Hkv, D, dtype, K_out, V_out, kept_idx, ws,
-                                as_stream(stream)));
+  return prune_impl(score, modality, cu_len, keep, cu_kept, nseq, total_L, total_kept, K, V, 1,
+                    Hkv, D, dtype, K_out, V_out, kept_idx, ws, ws_bytes, stream);
+}
+
+int sprint_prune_kv_layers(const float* score, const uint8_t* modality, const int32_t* cu_len,
+                           const int32_t* keep, const int32_t* cu_kept, int32_t nseq,
+                           int64_t total_L, int64_t total_kept, const void* K, const void* V,
+                           int32_t n_layers, int32_t Hkv, int32_t D, int32_t dtype, void* K_out,
+                           void* V_out, int32_t* kept_idx, void* ws, size_t ws_bytes,
+                           void* stream) {
+  return prune_impl(score, modality, cu_len, keep, cu_kept, nseq, total_L, total_kept, K, V,
+                    n_layers, Hkv, D, dtype, K_out, V_out, kept_idx, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- attention

@@ -13,7 +13,9 @@
 //   2. chunk_count_kernel     kept count of every 64-position chunk;
 //   3. compact_kernel         per chunk: prefix of earlier chunk counts in the
 //                             sequence -> output slots; writes kept_idx and
-//                             copies the K and V rows (16-byte vectors).
+//                             copies the K and V rows (16-byte vectors), of
+//                             every layer (grid y) when one kept set serves
+//                             several layers' caches.
 // The copy dominates: 2 x kept x row bytes read and written, HBM-bound.
 #include <limits.h>
 
@@ -198,6 +200,12 @@ __global__ __launch_bounds__(kCopyThreads) void compact_kernel(
     int32_t* __restrict__ kept_idx) {
   SeqChunk sc;
   if (!find_seq_chunk(cu_len, nseq, kChunk, total_L, blockIdx.x, sc)) return;
+  // layer blockIdx.y: its caches; layer 0 writes kept_idx
+  const int64_t layer = blockIdx.y;
+  K += layer * total_L * row_vecs * 16;
+  V += layer * total_L * row_vecs * 16;
+  K_out += layer * total_kept * row_vecs * 16;
+  V_out += layer * total_kept * row_vecs * 16;
   __shared__ int64_t s_pos[kChunk];
   __shared__ int64_t s_slot0, s_limit;
   __shared__ int s_nk;
@@ -216,7 +224,7 @@ __global__ __launch_bounds__(kCopyThreads) void compact_kernel(
     if (f) {
       s_pos[rank] = p;
       const int64_t slot = slot0 + rank;
-      if (slot >= 0 && slot < limit) kept_idx[slot] = static_cast<int32_t>(p);
+      if (layer == 0 && slot >= 0 && slot < limit) kept_idx[slot] = static_cast<int32_t>(p);
     }
     if (lane == 0) {
       s_nk = __popcll(bal);
@@ -267,8 +275,8 @@ size_t prune_ws_bytes(int64_t total_L, int nseq) {
 
 hipError_t launch_prune(const float* score, const uint8_t* modality, const int32_t* cu_len,
                         const int32_t* keep, const int32_t* cu_kept, int nseq, int64_t total_L,
-                        int64_t total_kept, const void* K, const void* V, int Hkv, int D,
-                        int dtype, void* K_out, void* V_out, int32_t* kept_idx, void* ws,
+                        int64_t total_kept, const void* K, const void* V, int n_layers, int Hkv,
+                        int D, int dtype, void* K_out, void* V_out, int32_t* kept_idx, void* ws,
                         hipStream_t st) {
   if (total_L == 0) return hipSuccess;
   SegThresh* thr = static_cast<SegThresh*>(ws);
@@ -286,7 +294,8 @@ hipError_t launch_prune(const float* score, const uint8_t* modality, const int32
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (total_kept == 0) return hipSuccess;
-  compact_kernel<<<dim3(nchunk), dim3(kCopyThreads), 0, st>>>(
+  compact_kernel<<<dim3(static_cast<unsigned>(nchunk), static_cast<unsigned>(n_layers)),
+                   dim3(kCopyThreads), 0, st>>>(
       score, modality, cu_len, cu_kept, nseq, total_L, total_kept, thr, counts,
       static_cast<const char*>(K), static_cast<const char*>(V), row_vecs,
       static_cast<char*>(K_out), static_cast<char*>(V_out), kept_idx);

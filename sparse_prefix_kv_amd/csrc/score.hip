@@ -7,6 +7,10 @@
 //   2. score_kernel: every chunk re-derives its sequence's mean from the
 //      chunk sums in one fixed order (so all chunks agree bitwise), then
 //      writes I_i = n_i / mean and s_i = alpha*I_i + (1-alpha)*c_i in place.
+// With several layers (one kept set shared by every layer's cache), launch 1
+// runs once per layer (grid y) into per-layer norms and chunk sums, and I_i
+// is the mean over layers of each layer's I_i, summed in layer order; one
+// layer gives exactly the single-layer arithmetic.
 // HBM-bound: it reads each key row once (Hkv*D elements) and 12 bytes of
 // per-position floats.  Eight lanes share a row: one wave instruction reads
 // 128 contiguous bytes of eight rows (whole cache lines), and every lane has
@@ -58,6 +62,10 @@ __global__ __launch_bounds__(kThreads) void keynorm_kernel(const char* __restric
                                                            float* __restrict__ partial) {
   SeqChunk sc;
   if (!find_seq_chunk(cu_len, nseq, kChunk, total_L, blockIdx.x, sc)) return;
+  // layer blockIdx.y: its cache, norms and chunk sums
+  K += static_cast<int64_t>(blockIdx.y) * total_L * row_vecs * 16;
+  norms += static_cast<int64_t>(blockIdx.y) * total_L;
+  partial += static_cast<int64_t>(blockIdx.y) * gridDim.x;
   __shared__ float s_norm[kChunk];
   const int64_t p0 = sc.begin + static_cast<int64_t>(sc.c) * kChunk;
   const int64_t rem = sc.begin + sc.len - p0;
@@ -103,23 +111,30 @@ __global__ __launch_bounds__(kThreads) void keynorm_kernel(const char* __restric
   }
 }
 
-// One wave per 64-position chunk.
+// One wave per 64-position chunk.  norms: [n_layers, total_L] (may be ibar
+// itself for one layer); partial: [n_layers, n_chunks].
 __global__ __launch_bounds__(64) void score_kernel(const float* __restrict__ conf,
                                                    const int32_t* __restrict__ cu_len, int nseq,
-                                                   int64_t total_L,
+                                                   int64_t total_L, int n_layers,
+                                                   const float* norms,
                                                    const float* __restrict__ partial, float alpha,
-                                                   float* __restrict__ ibar,
-                                                   float* __restrict__ score) {
+                                                   float* ibar, float* __restrict__ score) {
   SeqChunk sc;
   if (!find_seq_chunk(cu_len, nseq, kChunk, total_L, blockIdx.x, sc)) return;
   const int lane = threadIdx.x;
-  float acc = 0.f;
-  for (int i = lane; i < sc.nchunks; i += 64) acc += partial[sc.first + i];
-  acc = wave_sum(acc);
-  const float mean = acc / static_cast<float>(sc.len);
   const int64_t p = sc.begin + static_cast<int64_t>(sc.c) * kChunk + lane;
-  if (p < sc.begin + sc.len) {
-    const float ib = mean > 0.f ? ibar[p] / mean : 1.f;
+  const bool ok = p < sc.begin + sc.len;
+  float ib = 0.f;
+  for (int l = 0; l < n_layers; ++l) {
+    const float* part = partial + static_cast<int64_t>(l) * gridDim.x;
+    float acc = 0.f;
+    for (int i = lane; i < sc.nchunks; i += 64) acc += part[sc.first + i];
+    acc = wave_sum(acc);
+    const float mean = acc / static_cast<float>(sc.len);
+    if (ok) ib += mean > 0.f ? norms[static_cast<int64_t>(l) * total_L + p] / mean : 1.f;
+  }
+  if (ok) {
+    ib /= static_cast<float>(n_layers);
     ibar[p] = ib;
     score[p] = alpha * ib + (1.f - alpha) * conf[p];
   }
@@ -127,28 +142,39 @@ __global__ __launch_bounds__(64) void score_kernel(const float* __restrict__ con
 
 }  // namespace
 
-size_t score_ws_bytes(int64_t total_L, int nseq) {
-  return align_up(static_cast<size_t>(chunk_bound(total_L, nseq, kChunk)) * sizeof(float), 256);
+size_t score_ws_bytes(int64_t total_L, int nseq, int n_layers) {
+  const size_t part = align_up(static_cast<size_t>(chunk_bound(total_L, nseq, kChunk)) *
+                                   n_layers * sizeof(float), 256);
+  const size_t norms =
+      n_layers > 1 ? align_up(static_cast<size_t>(total_L) * n_layers * sizeof(float), 256) : 0;
+  return part + norms;
 }
 
-hipError_t launch_score(const void* K, const float* conf, const int32_t* cu_len, int nseq,
-                        int64_t total_L, int Hkv, int D, int dtype, float alpha, float* ibar,
-                        float* score, void* ws, hipStream_t st) {
+hipError_t launch_score(const void* K, int n_layers, const float* conf, const int32_t* cu_len,
+                        int nseq, int64_t total_L, int Hkv, int D, int dtype, float alpha,
+                        float* ibar, float* score, void* ws, hipStream_t st) {
   if (total_L == 0) return hipSuccess;
   const int es = dtype == 1 ? 2 : 4;
   const int row_vecs = Hkv * D * es / 16;
   const int64_t nblk = chunk_bound(total_L, nseq, kChunk);
   float* partial = static_cast<float*>(ws);
+  // one layer keeps its norms in ibar; several need their own array
+  float* norms = n_layers > 1
+                     ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                                align_up(static_cast<size_t>(nblk) * n_layers *
+                                                             sizeof(float), 256))
+                     : ibar;
+  const dim3 grid(static_cast<unsigned>(nblk), static_cast<unsigned>(n_layers));
   if (dtype == 1)
-    keynorm_kernel<BF16><<<dim3(nblk), dim3(kThreads), 0, st>>>(
-        static_cast<const char*>(K), cu_len, nseq, total_L, row_vecs, ibar, partial);
+    keynorm_kernel<BF16><<<grid, dim3(kThreads), 0, st>>>(
+        static_cast<const char*>(K), cu_len, nseq, total_L, row_vecs, norms, partial);
   else
-    keynorm_kernel<F32><<<dim3(nblk), dim3(kThreads), 0, st>>>(
-        static_cast<const char*>(K), cu_len, nseq, total_L, row_vecs, ibar, partial);
+    keynorm_kernel<F32><<<grid, dim3(kThreads), 0, st>>>(
+        static_cast<const char*>(K), cu_len, nseq, total_L, row_vecs, norms, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  score_kernel<<<dim3(nblk), dim3(64), 0, st>>>(conf, cu_len, nseq, total_L, partial, alpha, ibar,
-                                                score);
+  score_kernel<<<dim3(nblk), dim3(64), 0, st>>>(conf, cu_len, nseq, total_L, n_layers, norms,
+                                                partial, alpha, ibar, score);
   return hipGetLastError();
 }
 

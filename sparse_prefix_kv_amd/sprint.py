@@ -50,6 +50,14 @@ _SIGS = {
                                     _c_void_p, _c_void_p, _size, _c_void_p]),
     "unmask_select": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _f32, _i32, _c_void_p,
                                      _c_void_p, _c_void_p, _c_void_p]),
+    "sprint_score_layers_ws": (_size, [_i64, _i32, _i32]),
+    "sprint_score_layers": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i64, _i32,
+                                           _i32, _i32, _f32, _c_void_p, _c_void_p, _c_void_p,
+                                           _size, _c_void_p]),
+    "sprint_prune_kv_layers": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                              _c_void_p, _i32, _i64, _i64, _c_void_p, _c_void_p,
+                                              _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
+                                              _c_void_p, _c_void_p, _size, _c_void_p]),
     "sprint_append_rows": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i64, _c_void_p, _i32, _i64,
                                           _c_void_p, _c_void_p, _c_void_p]),
 }
@@ -282,3 +290,49 @@ def sprint_append_rows(old, cu_old, blk, out=None, cu_out=None, stream=None):
         _ptr(blk) if n_blk else None, n_blk, row_bytes, _ptr(out) if total else None,
         _ptr(cu_out), _stream(stream)))
     return out, cu_out
+
+
+def sprint_score_layers_ws(total_L: int, nseq: int, n_layers: int) -> int:
+    return int(lib().sprint_score_layers_ws(total_L, nseq, n_layers))
+
+
+def sprint_score_layers(K, conf, cu_len, alpha: float = 0.5, ibar=None, score=None, ws=None,
+                        stream=None):
+    """Layer-mean key-norm importance and composite score.  K [n_layers, total_L, Hkv, D]."""
+    _dev(K, "K")
+    n_layers, total_L, Hkv, D = K.shape
+    nseq = cu_len.numel() - 1
+    dev = K.device
+    ibar = torch.empty(total_L, dtype=torch.float32, device=dev) if ibar is None else ibar
+    score = torch.empty(total_L, dtype=torch.float32, device=dev) if score is None else score
+    ws = _ws(sprint_score_layers_ws(total_L, nseq, n_layers), dev, ws)
+    _check("sprint_score_layers", lib().sprint_score_layers(
+        _ptr(K), n_layers, _ptr(conf), _ptr(cu_len), nseq, total_L, Hkv, D, _dt(K),
+        float(alpha), _ptr(ibar), _ptr(score), _ptr(ws), ws.numel(), _stream(stream)))
+    return ibar, score
+
+
+def sprint_prune_kv_layers(score, modality, cu_len, keep, cu_kept, total_kept: int, K, V,
+                           K_out=None, V_out=None, kept_idx=None, ws=None, stream=None):
+    """One kept set compacted in every layer's cache.  K, V [n_layers, total_L, Hkv, D]."""
+    _dev(K, "K")
+    _dev(V, "V")
+    n_layers, total_L, Hkv, D = K.shape
+    nseq = cu_len.numel() - 1
+    dev = K.device
+    shape = (n_layers, max(total_kept, 1), Hkv, D)
+    if K_out is None:
+        K_out = torch.empty(shape, dtype=K.dtype, device=dev)[:, :total_kept]
+    if V_out is None:
+        V_out = torch.empty(shape, dtype=V.dtype, device=dev)[:, :total_kept]
+    for t, name in ((K_out, "K_out"), (V_out, "V_out")):
+        if total_kept and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [n_layers, total_kept, Hkv, D]")
+    if kept_idx is None:
+        kept_idx = torch.empty(max(total_kept, 1), dtype=torch.int32, device=dev)[:total_kept]
+    ws = _ws(sprint_prune_kv_ws(total_L, nseq), dev, ws)
+    _check("sprint_prune_kv_layers", lib().sprint_prune_kv_layers(
+        _ptr(score), _ptr(modality), _ptr(cu_len), _ptr(keep), _ptr(cu_kept), nseq, total_L,
+        int(total_kept), _ptr(K), _ptr(V), n_layers, Hkv, D, _dt(K), _ptr(K_out), _ptr(V_out),
+        _ptr(kept_idx), _ptr(ws), ws.numel(), _stream(stream)))
+    return K_out, V_out, kept_idx

@@ -26,6 +26,10 @@ Generation over several blocks: block 0 uses the draws above; block b >= 1
 draws its own Q, Kb, Vb (same shapes and laws, in that order) from
 ``default_rng([seed, b])``.  The rows a finished block adds to the prefix
 are not drawn: they are that block's own K/V and outputs.
+
+Several layers: layer 0 uses the draws above; layer l >= 1 draws its own
+Q, K (with its own key scales), V, Kb, Vb from ``default_rng([seed, 2**20,
+l])``.  The prefix hidden states and the LM head are shared.
 """
 from __future__ import annotations
 
@@ -224,6 +228,28 @@ def make_block_inputs(wl: Workload, nseq: int, b: int, seed: int = 0):
     if wl.dtype == "bf16":
         Q, Kb, Vb = (bf16_round(a) for a in (Q, Kb, Vb))
     return Q, Kb, Vb
+
+
+def make_layer_inputs(wl: Workload, layout: "Layout", l: int, seed: int = 0,
+                      prefix_scale: float = 1.0):
+    """Q, K, V, Kb, Vb of layer l >= 1 of a several-layer stand-in (layer 0
+    uses make_inputs's draws): the same laws, drawn from
+    default_rng([seed, 1 << 20, l]) in the order Q, K, key scale, V, Kb, Vb."""
+    if l < 1:
+        raise ValueError("layer 0 takes its inputs from make_inputs")
+    rng = np.random.default_rng([seed, 1 << 20, l])
+    f32 = np.float32
+    nseq, tl = layout.nseq, layout.total_L
+    Q = rng.standard_normal((nseq, wl.Lq, wl.Hq, wl.D), dtype=f32)
+    K = rng.standard_normal((tl, wl.Hkv, wl.D), dtype=f32)
+    ks = rng.lognormal(0.0, 0.5, size=tl).astype(f32) * f32(prefix_scale)
+    K *= ks[:, None, None]
+    V = rng.standard_normal((tl, wl.Hkv, wl.D), dtype=f32)
+    Kb = rng.standard_normal((nseq, wl.Lq, wl.Hkv, wl.D), dtype=f32)
+    Vb = rng.standard_normal((nseq, wl.Lq, wl.Hkv, wl.D), dtype=f32)
+    if wl.dtype == "bf16":
+        Q, K, V, Kb, Vb = (bf16_round(a) for a in (Q, K, V, Kb, Vb))
+    return Q, K, V, Kb, Vb
 
 
 # ---------------------------------------------------------------------------

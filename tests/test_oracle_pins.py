@@ -529,3 +529,77 @@ def test_generation_prefix_grows_by_finished_blocks(gen_modality):
         rows = np.arange(cu1[s + 1] - wl.Lq, cu1[s + 1])
         np.testing.assert_allclose(res[1].conf_prefix[rows], c[s * wl.Lq:(s + 1) * wl.Lq],
                                    rtol=1e-12)
+
+
+# -------------------------------------------------------------- several layers
+
+def _layer_stack(n_layers, seed=0):
+    wl, x = _tiny_inputs(seed)
+    layers = [(x.Q, x.K, x.V, x.Kb, x.Vb)] + [synth.make_layer_inputs(wl, x.layout, l, seed)
+                                              for l in range(1, n_layers)]
+    return wl, x, layers
+
+
+def test_layer_mean_importance_is_per_layer_scale_free():
+    # each layer is normalised by its own mean: scaling one layer's keys (by a
+    # power of two, exactly) does not move the mean importance (a norm over
+    # the layers' concatenated keys would), and every sequence's importances
+    # still average to one
+    wl, x, layers = _layer_stack(3, seed=1)
+    cu = x.layout.cu_len
+    Ks = [l[1] for l in layers]
+    ib = oracle.key_norm_importance_layers(Ks, cu)
+    ib_scaled = oracle.key_norm_importance_layers([Ks[0], 8.0 * Ks[1], Ks[2]], cu)
+    np.testing.assert_allclose(ib_scaled, ib, rtol=1e-12)
+    concat = oracle.key_norm_importance(np.concatenate([Ks[0], 8.0 * Ks[1], Ks[2]], axis=1), cu)
+    assert np.max(np.abs(concat - ib)) > 1e-3
+    assert abs(ib.sum() - x.layout.total_L) < 1e-9
+    # one layer, or identical layers, reduce to the single-layer importance
+    np.testing.assert_array_equal(oracle.key_norm_importance_layers(Ks[:1], cu),
+                                  oracle.key_norm_importance(Ks[0], cu))
+    np.testing.assert_allclose(oracle.key_norm_importance_layers([Ks[2]] * 4, cu),
+                               oracle.key_norm_importance(Ks[2], cu), rtol=1e-14)
+
+
+def test_layers_one_layer_is_run_block():
+    wl, x, layers = _layer_stack(1)
+    lay = x.layout
+    for shared in (True, False):
+        r = oracle.run_block_layers(layers, x.hidden, x.W, lay.cu_len, lay.modality, 1.0, 0.5,
+                                    0.9, 4, 3, shared=shared)
+        one = oracle.run_block(x.Q, x.K, x.V, x.Kb, x.Vb, x.hidden, x.W, lay.cu_len,
+                               lay.modality, 1.0, 0.5, 0.9, 4, 3)
+        np.testing.assert_array_equal(r.kept[0], one.kept_idx)
+        for t in range(4):
+            np.testing.assert_array_equal(r.outputs[t][0], one.outputs[t])
+            np.testing.assert_array_equal(r.tokens[t], one.tokens[t])
+
+
+def test_layers_shared_and_per_layer_sets():
+    wl, x, layers = _layer_stack(3, seed=2)
+    lay = x.layout
+    sh = oracle.run_block_layers(layers, x.hidden, x.W, lay.cu_len, lay.modality, 1.0, 0.5, 0.9,
+                                 4, 2, shared=True)
+    pl = oracle.run_block_layers(layers, x.hidden, x.W, lay.cu_len, lay.modality, 1.0, 0.5, 0.9,
+                                 4, 2, shared=False)
+    # the shared set is one set; per-layer sets follow each layer's own keys
+    assert all(np.array_equal(k, sh.kept[0]) for k in sh.kept)
+    for l in range(3):
+        own = oracle.select_kept(oracle.composite_score(
+            oracle.key_norm_importance(layers[l][1], lay.cu_len), pl.conf_prefix),
+            lay.modality, lay.cu_len, [[24, 4]])
+        np.testing.assert_array_equal(pl.kept[l], own)
+    assert not all(np.array_equal(pl.kept[0], k) for k in pl.kept[1:])
+    # every set keeps the same counts; step 0 (full prefix) does not depend on
+    # the sets, so both modes agree there
+    assert all(len(k) == 28 for k in sh.kept + pl.kept)
+    for l in range(3):
+        np.testing.assert_array_equal(sh.outputs[0][l], pl.outputs[0][l])
+    # identical layers make every mode the same selection
+    same = [layers[0]] * 3
+    a = oracle.run_block_layers(same, x.hidden, x.W, lay.cu_len, lay.modality, 1.0, 0.5, 0.9, 4,
+                                1, shared=True)
+    b = oracle.run_block_layers(same, x.hidden, x.W, lay.cu_len, lay.modality, 1.0, 0.5, 0.9, 4,
+                                1, shared=False)
+    for k in a.kept + b.kept:
+        np.testing.assert_array_equal(k, a.kept[0])
