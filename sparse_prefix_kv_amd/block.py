@@ -80,12 +80,16 @@ class SprintBlock:
         M = self.nseq * self.Lq
         self.conf_blk = torch.empty(M, dtype=f32, device=dev)
         self.argmax_blk = torch.empty(M, dtype=i32, device=dev)
-        self.masked = torch.ones((self.nseq, self.Lq), dtype=u8, device=dev)
-        self.tokens = torch.full((self.nseq, self.Lq), -1, dtype=i32, device=dev)
-        # block-start state (all masked), restored by a device copy so that a
-        # captured graph holds no memset node
-        self.masked0 = self.masked.clone()
-        self.tokens0 = self.tokens.clone()
+        # tokens (int32) and mask (uint8) share one buffer, so the block-start
+        # state (all masked) comes back with one device copy; a copy rather
+        # than a fill keeps memset nodes out of captured graphs
+        n = self.nseq * self.Lq
+        self._state = torch.empty(5 * n, dtype=u8, device=dev)
+        self.tokens = self._state[:4 * n].view(i32).view(self.nseq, self.Lq)
+        self.masked = self._state[4 * n:].view(self.nseq, self.Lq)
+        self.tokens.fill_(-1)
+        self.masked.fill_(1)
+        self._state0 = self._state.clone()
         self.timer = None
         self.n_acc = torch.empty(self.nseq, dtype=i32, device=dev)
         dti = sprint.BF16 if dt == "bf16" else sprint.F32
@@ -149,8 +153,7 @@ class SprintBlock:
         return BIG_STEPS if self.T is None else self.T - t
 
     def reset(self):
-        self.masked.copy_(self.masked0)
-        self.tokens.copy_(self.tokens0)
+        self._state.copy_(self._state0)
 
     def _t(self, name):
         """Event-timed region around one library call when a timer is set."""

@@ -80,10 +80,13 @@ class SprintLayers:
         M = self.nseq * self.Lq
         self.conf_blk = torch.empty(M, dtype=f32, device=dev)
         self.argmax_blk = torch.empty(M, dtype=i32, device=dev)
-        self.masked = torch.ones((self.nseq, self.Lq), dtype=u8, device=dev)
-        self.tokens = torch.full((self.nseq, self.Lq), -1, dtype=i32, device=dev)
-        self.masked0 = self.masked.clone()
-        self.tokens0 = self.tokens.clone()
+        n = self.nseq * self.Lq
+        self._state = torch.empty(5 * n, dtype=u8, device=dev)   # tokens, then mask
+        self.tokens = self._state[:4 * n].view(i32).view(self.nseq, self.Lq)
+        self.masked = self._state[4 * n:].view(self.nseq, self.Lq)
+        self.tokens.fill_(-1)
+        self.masked.fill_(1)
+        self._state0 = self._state.clone()
         self.n_acc = torch.empty(self.nseq, dtype=i32, device=dev)
         dti = sprint.BF16 if dt == "bf16" else sprint.F32
 
@@ -100,8 +103,7 @@ class SprintLayers:
 
     # ------------------------------------------------------------------ pieces
     def reset(self):
-        self.masked.copy_(self.masked0)
-        self.tokens.copy_(self.tokens0)
+        self._state.copy_(self._state0)
 
     def steps_left(self, t: int) -> int:
         return BIG_STEPS if self.T is None else self.T - t
