@@ -9,4 +9,5 @@ from .sprint_oracle import (attention, compact, composite_score, fixed_schedule_
                             lmhead_top2_gap, min_acceptances, run_block, select_kept,
                             unmask_select, BlockResult, append_block, store_as,
                             run_generation, key_norm_importance_layers,
-                            run_block_layers, LayersResult)
+                            run_block_layers, LayersResult, silu, moe_route,
+                            expert_ffn, moe_ffn)

@@ -484,3 +484,62 @@ def run_block_layers(layers, hidden, W, cu_len, modality, r_text, r_img, tau,
         res.masks.append(masked.copy())
         res.tokens.append(tokens.copy())
     return res
+
+
+# --------------------------------------------------------------------------
+# An MoE FFN on synthetic weights (the backbone's expert layer)
+# --------------------------------------------------------------------------
+
+def silu(z):
+    """z * sigmoid(z)."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def moe_route(x, w_router, bias, top_k: int, route_scale: float = 2.5):
+    """Routing of each token (LLaDA2.0-Uni, "Load Balancing Strategy").
+
+    Affinity s_e = sigmoid(x . r_e) per expert.  The auxiliary-loss-free
+    balancing bias b only steers selection: the top_k experts by s_e + b_e
+    are chosen (the lower expert index wins a tie), and their gates are the
+    affinities normalised over the chosen experts and scaled by route_scale
+    (2.5 on the page).  Returns (expert ids [M, top_k] in selection order,
+    gates [M, top_k], affinities [M, E]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    logits = x @ np.asarray(w_router, dtype=np.float64).T
+    s = 1.0 / (1.0 + np.exp(-logits))
+    sel_score = s + np.asarray(bias, dtype=np.float64)[None, :]
+    M, E = s.shape
+    ids = np.zeros((M, top_k), dtype=np.int64)
+    gates = np.zeros((M, top_k))
+    for t in range(M):
+        order = np.lexsort((np.arange(E), -sel_score[t]))
+        ids[t] = order[:top_k]
+        gates[t] = route_scale * s[t, ids[t]] / s[t, ids[t]].sum()
+    return ids, gates, s
+
+
+def expert_ffn(x, w_gate, w_up, w_down):
+    """SwiGLU expert: W_down (silu(W_gate x) * (W_up x)).  x [n, H];
+    w_gate, w_up [I, H]; w_down [H, I]."""
+    x = np.asarray(x, dtype=np.float64)
+    g = x @ np.asarray(w_gate, dtype=np.float64).T
+    u = x @ np.asarray(w_up, dtype=np.float64).T
+    return (silu(g) * u) @ np.asarray(w_down, dtype=np.float64).T
+
+
+def moe_ffn(x, w_router, bias, w_gate, w_up, w_down, top_k: int, route_scale: float = 2.5,
+            residual=None):
+    """y_t = residual_t + sum_j gate_{t,j} * FFN_{e_{t,j}}(x_t)  (residual
+    optional).  w_gate, w_up [E, I, H]; w_down [E, H, I].  Returns (y, ids,
+    gates)."""
+    ids, gates, _ = moe_route(x, w_router, bias, top_k, route_scale)
+    x = np.asarray(x, dtype=np.float64)
+    M, H = x.shape
+    y = np.zeros((M, H)) if residual is None else np.asarray(residual, dtype=np.float64).copy()
+    for t in range(M):
+        for j in range(top_k):
+            e = ids[t, j]
+            y[t] += gates[t, j] * expert_ffn(x[t:t + 1], w_gate[e], w_up[e], w_down[e])[0]
+    return y, ids, gates

@@ -603,3 +603,84 @@ def test_layers_shared_and_per_layer_sets():
                                 1, shared=False)
     for k in a.kept + b.kept:
         np.testing.assert_array_equal(k, a.kept[0])
+
+
+# -------------------------------------------------------------- MoE FFN
+
+def test_silu_identities():
+    z = np.linspace(-9, 9, 181)
+    np.testing.assert_allclose(oracle.silu(z) - oracle.silu(-z), z, atol=1e-12)
+    assert oracle.silu(0.0) == 0.0
+    # sigmoid(z) = (1 + tanh(z/2)) / 2
+    np.testing.assert_allclose(oracle.silu(z), z * (1 + np.tanh(z / 2)) / 2, rtol=1e-12)
+
+
+def test_moe_hand_example():
+    # H = 2, I = 1, two experts, one chosen: affinities 1/2 and 3/4, so
+    # expert 1 wins with gate 2.5; its FFN gives silu(2) * 3 on row one of
+    # W_down = (1, -1)
+    x = np.array([[1.0, 0.0]])
+    wr = np.array([[0.0, 0.0], [np.log(3.0), 0.0]])
+    wg = np.zeros((2, 1, 2)); wu = np.zeros((2, 1, 2)); wd = np.zeros((2, 2, 1))
+    wg[1, 0] = [2.0, 0.0]; wu[1, 0] = [3.0, 0.0]; wd[1, :, 0] = [1.0, -1.0]
+    y, ids, g = oracle.moe_ffn(x, wr, np.zeros(2), wg, wu, wd, 1)
+    silu2 = 2.0 * (1 + np.tanh(1.0)) / 2
+    assert ids.tolist() == [[1]] and g.tolist() == [[2.5]]
+    np.testing.assert_allclose(y, [[7.5 * silu2, -7.5 * silu2]], rtol=1e-14)
+    _, _, s = oracle.moe_route(x, wr, np.zeros(2), 1)
+    np.testing.assert_allclose(s, [[0.5, 0.75]], rtol=1e-14)
+
+
+def _moe_case(seed, M=5, H=16, I=8, E=7):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((M, H)), r.standard_normal((E, H)) / 4, r.uniform(-0.1, 0.1, E),
+            r.standard_normal((E, I, H)) / 4, r.standard_normal((E, I, H)) / 4,
+            r.standard_normal((E, H, I)) / 3)
+
+
+@pytest.mark.parametrize("k", [1, 3, 7])
+def test_moe_selection_is_the_best_subset(k):
+    x, wr, b, *_ = _moe_case(1)
+    ids, gates, s = oracle.moe_route(x, wr, b, k)
+    sel = s + b[None, :]
+    for t in range(len(x)):
+        best = max(itertools.combinations(range(7), k), key=lambda c: sel[t, list(c)].sum())
+        assert sorted(ids[t].tolist()) == sorted(best)
+        np.testing.assert_allclose(gates[t].sum(), 2.5, rtol=1e-14)
+
+
+def test_moe_bias_steers_selection_only_and_ties_go_low():
+    x, wr, b, wg, wu, wd = _moe_case(2)
+    y0, ids0, g0 = oracle.moe_ffn(x, wr, b, wg, wu, wd, 3)
+    y1, ids1, g1 = oracle.moe_ffn(x, wr, b + 5.0, wg, wu, wd, 3)   # a common shift
+    np.testing.assert_array_equal(ids0, ids1)
+    np.testing.assert_allclose(y0, y1, rtol=1e-14)
+    # a large bias forces expert 6 in; its gate still follows its affinity:
+    # the ratio of two chosen experts' gates is the ratio of their affinities
+    big = b.copy(); big[6] = 10.0
+    ids2, g2, s2 = oracle.moe_route(x, wr, big, 3)
+    for t in range(len(x)):
+        assert ids2[t, 0] == 6
+        np.testing.assert_allclose(g2[t, 0] / g2[t, 1], s2[t, 6] / s2[t, ids2[t, 1]], rtol=1e-12)
+    # all-equal affinities and biases: the lowest experts, equal gates
+    ids3, g3, _ = oracle.moe_route(x, np.zeros_like(wr), np.zeros(7), 4)
+    assert ids3.tolist() == [[0, 1, 2, 3]] * len(x)
+    np.testing.assert_allclose(g3, 2.5 / 4, rtol=1e-14)
+
+
+def test_moe_expert_permutation_and_linearity():
+    x, wr, b, wg, wu, wd = _moe_case(3)
+    p = np.array([3, 0, 6, 1, 5, 2, 4])
+    y, ids, g = oracle.moe_ffn(x, wr, b, wg, wu, wd, 2)
+    yp, idsp, gp = oracle.moe_ffn(x, wr[p], b[p], wg[p], wu[p], wd[p], 2)
+    np.testing.assert_allclose(yp, y, rtol=1e-12)
+    np.testing.assert_array_equal(p[idsp], ids)
+    y3, _, _ = oracle.moe_ffn(x, wr, b, wg, wu, 3.0 * wd, 2)
+    np.testing.assert_allclose(y3, 3.0 * y, rtol=1e-12)
+    # every expert with equal affinity and scale 1 is the plain mean of the experts
+    ym, _, _ = oracle.moe_ffn(x, np.zeros_like(wr), np.zeros(7), wg, wu, wd, 7, 1.0)
+    mean = np.mean([oracle.expert_ffn(x, wg[e], wu[e], wd[e]) for e in range(7)], axis=0)
+    np.testing.assert_allclose(ym, mean, rtol=1e-12)
+    # the residual adds
+    yr, _, _ = oracle.moe_ffn(x, wr, b, wg, wu, wd, 2, residual=x[:, :16])
+    np.testing.assert_allclose(yr, y + x, rtol=1e-12)
