@@ -218,6 +218,32 @@ int sprint_append_rows(const void* old, const int32_t* cu_old, int32_t nseq, int
                        const void* blk, int32_t n_blk, int64_t row_bytes, void* out,
                        int32_t* cu_out, void* stream);
 
+/* ------------------------------------------------------------------------
+ * MoE FFN on synthetic weights (the backbone's expert layer; LLaDA2.0-Uni,
+ * "Load Balancing Strategy": an auxiliary-loss-free bias steers expert
+ * selection, and routing gates are scaled by 2.5).  Per token t:
+ *   s_e  = sigmoid(x_t . w_router[e]),
+ *   the top_k experts by s_e + bias[e] (lower expert index on ties), in
+ *   selection order e_{t,0..top_k-1},
+ *   g_j  = route_scale * s_{e_j} / sum_j s_{e_j},
+ *   y_t  = residual_t + sum_j g_j * w_down[e_j] (silu(w_gate[e_j] x_t) * (w_up[e_j] x_t)).
+ *   x        [M, H] dtype;  w_router [E, H] dtype;  bias [E] float
+ *   w_gate, w_up [E, inter, H] dtype;  w_down [E, H, inter] dtype
+ *   residual [M, H] dtype or NULL;  y [M, H] dtype out (may equal residual)
+ *   expert_ids [M, top_k] int32 out;  gates [M, top_k] float out
+ * Every chosen expert's weights are read once per call (a grouped
+ * matrix-vector product for the few tokens of a denoising step).
+ * Supported: H a multiple of 512 (bf16) or 256 (fp32) up to 2048 / 1024,
+ * inter a multiple of 512 / 256 up to 1024 / 512, E <= 1024, top_k <= 16,
+ * M * top_k <= 8192.
+ * ------------------------------------------------------------------------ */
+size_t moe_ffn_ws(int32_t M, int32_t H, int32_t n_experts, int32_t top_k, int32_t inter);
+int moe_ffn(const void* x, int32_t M, int32_t H, const void* w_router, const float* bias,
+            int32_t n_experts, int32_t top_k, float route_scale, const void* w_gate,
+            const void* w_up, const void* w_down, int32_t inter, int32_t dtype,
+            const void* residual, void* y, int32_t* expert_ids, float* gates, void* ws,
+            size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

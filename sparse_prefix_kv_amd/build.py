@@ -34,7 +34,7 @@ COMMON = [
 ]
 
 SOURCES = ["abi.hip", "score.hip", "prune.hip", "attend.hip", "lmhead.hip", "unmask.hip",
-           "append.hip"]
+           "append.hip", "moe.hip"]
 
 
 def _compile(src: str) -> str:

@@ -264,4 +264,30 @@ int sprint_append_rows(const void* old, const int32_t* cu_old, int32_t nseq, int
                                       cu_out, as_stream(stream)));
 }
 
+// ---------------------------------------------------------------- MoE FFN
+size_t moe_ffn_ws(int32_t M, int32_t H, int32_t n_experts, int32_t top_k, int32_t inter) {
+  if (M < 1 || H < 1 || n_experts < 1 || top_k < 1 || inter < 1) return 0;
+  return moe_ws_bytes(M, H, n_experts, top_k, inter);
+}
+
+int moe_ffn(const void* x, int32_t M, int32_t H, const void* w_router, const float* bias,
+            int32_t n_experts, int32_t top_k, float route_scale, const void* w_gate,
+            const void* w_up, const void* w_down, int32_t inter, int32_t dtype,
+            const void* residual, void* y, int32_t* expert_ids, float* gates, void* ws,
+            size_t ws_bytes, void* stream) {
+  if (!dtype_ok(dtype) || M < 1 || H < 1 || n_experts < 1 || top_k < 1 || inter < 1)
+    return SPRINT_EINVAL;
+  if (top_k > n_experts || !isfinite(route_scale)) return SPRINT_EINVAL;
+  if (!dev16(x) || !dev16(w_router) || !dev4(bias) || !dev16(w_gate) || !dev16(w_up) ||
+      !dev16(w_down) || !dev16(y) || !dev4(expert_ids) || !dev4(gates))
+    return SPRINT_EINVAL;
+  if (residual != nullptr && !dev16(residual)) return SPRINT_EINVAL;
+  if (!moe_shape_supported(H, inter, n_experts, top_k, M, dtype)) return SPRINT_EUNSUPPORTED;
+  const int st = check_ws(ws, ws_bytes, moe_ws_bytes(M, H, n_experts, top_k, inter));
+  if (st != SPRINT_OK) return st;
+  return status_of(launch_moe(x, M, H, w_router, bias, n_experts, top_k, route_scale, w_gate,
+                              w_up, w_down, inter, dtype, residual, y, expert_ids, gates, ws,
+                              as_stream(stream)));
+}
+
 }  // extern "C"

@@ -1,0 +1,424 @@
+// MoE FFN of the backbone's expert layers on synthetic weights
+// (LLaDA2.0-Uni: a mixture-of-experts diffusion backbone; "Load Balancing
+// Strategy": an auxiliary-loss-free bias steers expert selection and the
+// routing gates are scaled by 2.5).
+//
+//   s_e   = sigmoid(x . r_e)                      affinity of each expert
+//   chosen = top_k experts by s_e + b_e            (lower index wins a tie)
+//   g_j   = scale * s_{e_j} / sum_chosen s         gates (bias-free)
+//   y     = residual + sum_j g_j * W_down_j (silu(W_gate_j x) * (W_up_j x))
+//
+// A denoising step has few tokens (32 per block), so each chosen expert
+// sees a handful of them: the work is streaming the chosen experts' weights
+// (3*I*H elements each) from HBM once, a grouped matrix-vector product.  The
+// vector ALUs keep up with that (a weight element meets at most M tokens),
+// so the expert kernels stream weights with coalesced non-temporal loads and
+// keep the expert's tokens in LDS; no MFMA.
+//
+// Launches (no host synchronisation: every expert's blocks are launched and
+// those of experts nobody chose exit at once):
+//   1. moe_router_kernel   logits [M, E]: a wave holds one router row in
+//                          registers and dots it with every token;
+//   2. moe_select_kernel   one block: sigmoid, biased top-k by wave arg-max
+//                          rounds, gates; then, per expert, its slots in slot
+//                          order (slot = token * top_k + j), so the grouping is
+//                          deterministic;
+//   3. moe_up_kernel       (I tile, expert): silu(gate) * up of each of the
+//                          expert's slots, fp32;
+//   4. moe_down_kernel     (H tile, expert): g * (W_down act) per slot, fp32;
+//   5. moe_combine_kernel  y = residual + sum_j out[t*top_k + j] in order j.
+// Every sum has a fixed order, so results are bitwise reproducible.
+#include <math.h>
+
+#include "sprint_device.hpp"
+#include "sprint_internal.hpp"
+
+namespace sprint {
+namespace {
+
+constexpr int kMoeThreads = 256;
+constexpr int kRouterExpertsPerBlock = 8;   // two per wave
+constexpr int kUpRows = 32;                 // I rows per up block
+constexpr int kDownRows = 64;               // H rows per down block
+constexpr int kStageBytes = 64 * 1024;      // LDS for an expert's token rows
+
+template <typename T>
+struct Vec {
+  static constexpr int kE = 16 / T::bytes;    // elements per 16-byte vector
+};
+
+template <typename T>
+__device__ __forceinline__ void unpack(u32x4 v, float* out);
+template <>
+__device__ __forceinline__ void unpack<BF16>(u32x4 v, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(v[i] << 16);
+    out[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void unpack<F32>(u32x4 v, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(v[i]);
+}
+
+// ---------------------------------------------------------------- 1. router
+// Lane l of a wave holds elements [16*(l + 64*v), +16 bytes) of a row for
+// v < NV (NV = H / (64 * elements per vector)).
+template <typename T, int NV>
+__global__ __launch_bounds__(kMoeThreads) void moe_router_kernel(
+    const char* __restrict__ x, int M, int H, const char* __restrict__ wr, int E,
+    float* __restrict__ logits) {
+  constexpr int EV = Vec<T>::kE;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row_bytes = static_cast<int64_t>(H) * T::bytes;
+  const int e0 = blockIdx.x * kRouterExpertsPerBlock + 2 * wave;
+  float r[2][NV * EV];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int e = e0 + k < E ? e0 + k : E - 1;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      unpack<T>(ld16_nt(wr + e * row_bytes + (lane + 64 * v) * 16), &r[k][v * EV]);
+  }
+  for (int t = 0; t < M; ++t) {
+    float xv[NV * EV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) unpack<T>(ld16(x + t * row_bytes + (lane + 64 * v) * 16), &xv[v * EV]);
+    float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV * EV; ++i) {
+      d0 = fmaf(r[0][i], xv[i], d0);
+      d1 = fmaf(r[1][i], xv[i], d1);
+    }
+    d0 = wave_sum(d0);
+    d1 = wave_sum(d1);
+    if (lane == 0) {
+      if (e0 < E) logits[static_cast<int64_t>(t) * E + e0] = d0;
+      if (e0 + 1 < E) logits[static_cast<int64_t>(t) * E + e0 + 1] = d1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 2. select
+constexpr int kSelWaves = 16;
+constexpr int kMaxExpertsPerLane = 16;      // E <= 1024
+constexpr int kMaxSlots = 8192;             // M * top_k
+
+__global__ __launch_bounds__(64 * kSelWaves) void moe_select_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias, int M, int E, int top_k,
+    float scale, int32_t* __restrict__ ids, float* __restrict__ gates,
+    int32_t* __restrict__ counts, int32_t* __restrict__ lists) {
+  __shared__ int32_t s_ids[kMaxSlots];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ne = (E + 63) / 64;
+  for (int t = wave; t < M; t += kSelWaves) {
+    float aff[kMaxExpertsPerLane], sel[kMaxExpertsPerLane];
+#pragma unroll
+    for (int i = 0; i < kMaxExpertsPerLane; ++i) {
+      const int e = lane + 64 * i;
+      const bool ok = i < ne && e < E;
+      const float z = ok ? logits[static_cast<int64_t>(t) * E + e] : 0.f;
+      aff[i] = 1.f / (1.f + expf(-z));
+      sel[i] = ok ? aff[i] + bias[e] : -INFINITY;
+    }
+    float chosen_aff[16];
+    float ssum = 0.f;
+    for (int j = 0; j < top_k; ++j) {
+      // this lane's best (largest selection score, lowest expert on ties)
+      float bv = -INFINITY;
+      int be = INT_MAX;
+#pragma unroll
+      for (int i = 0; i < kMaxExpertsPerLane; ++i)
+        if (sel[i] > bv) {     // ascending i: the first maximum is the lowest expert
+          bv = sel[i];
+          be = lane + 64 * i;
+        }
+      // wave arg-max, ties to the lowest expert
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const float ov = shfl_xor_f(bv, m);
+        const int oe = shfl_xor_i(be, m);
+        if (ov > bv || (ov == bv && oe < be)) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      // the owner lane removes it and broadcasts its affinity
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < kMaxExpertsPerLane; ++i)
+        if (lane + 64 * i == be) {
+          a = aff[i];
+          sel[i] = -INFINITY;
+        }
+      a = __shfl(a, be & 63, 64);
+      chosen_aff[j & 15] = a;
+      ssum += a;
+      if (lane == 0) {
+        ids[static_cast<int64_t>(t) * top_k + j] = be;
+        s_ids[t * top_k + j] = be;
+      }
+    }
+    if (lane < top_k) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j == lane) a = chosen_aff[j];
+      gates[static_cast<int64_t>(t) * top_k + lane] = scale * a / ssum;
+    }
+  }
+  __syncthreads();
+  // each expert's slots, in slot order
+  const int n_slots = M * top_k;
+  for (int e = threadIdx.x; e < E; e += 64 * kSelWaves) {
+    int c = 0;
+    for (int sl = 0; sl < n_slots; ++sl)
+      if (s_ids[sl] == e) lists[static_cast<int64_t>(e) * M + c++] = sl;
+    counts[e] = c;
+  }
+}
+
+// Stage rows of the expert's slots into LDS (as raw elements); row of slot
+// c of the chunk comes from src_row(c).  row_bytes is a multiple of 16.
+template <typename F>
+__device__ __forceinline__ void stage_rows_lds(char* lds, int n, int64_t row_bytes, F src_row) {
+  const int vecs = static_cast<int>(row_bytes / 16);
+  for (int u = threadIdx.x; u < n * vecs; u += kMoeThreads) {
+    const int c = u / vecs, v = u - c * vecs;
+    st16(lds + c * row_bytes + v * 16, ld16(src_row(c) + v * 16));
+  }
+}
+
+// ---------------------------------------------------------------- 3. gate/up
+template <typename T, int NV>
+__global__ __launch_bounds__(kMoeThreads) void moe_up_kernel(
+    const char* __restrict__ x, int H, int top_k, int M, const char* __restrict__ wg,
+    const char* __restrict__ wu, int I, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ lists, float* __restrict__ act) {
+  constexpr int EV = Vec<T>::kE;
+  __shared__ __align__(16) char xs[kStageBytes];
+  const int e = blockIdx.y;
+  const int n = counts[e];
+  if (n == 0) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row_bytes = static_cast<int64_t>(H) * T::bytes;
+  const int chunk = static_cast<int>(kStageBytes / row_bytes);
+  const char* g_e = wg + static_cast<int64_t>(e) * I * row_bytes;
+  const char* u_e = wu + static_cast<int64_t>(e) * I * row_bytes;
+  const int32_t* list = lists + static_cast<int64_t>(e) * M;
+  const int r0 = blockIdx.x * kUpRows + wave * (kUpRows / 4);
+  for (int c0 = 0; c0 < n; c0 += chunk) {
+    const int nc = min(chunk, n - c0);
+    __syncthreads();
+    stage_rows_lds(xs, nc, row_bytes, [&](int c) { return x + (list[c0 + c] / top_k) * row_bytes; });
+    __syncthreads();
+    // two rows at a time: both rows' gate and up loads in flight together
+    for (int rr = 0; rr < kUpRows / 4; rr += 2) {
+      float gw[2][NV * EV], uw[2][NV * EV];
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          const int64_t off = (r0 + rr + k) * row_bytes + (lane + 64 * v) * 16;
+          unpack<T>(ld16_nt(g_e + off), &gw[k][v * EV]);
+          unpack<T>(ld16_nt(u_e + off), &uw[k][v * EV]);
+        }
+      for (int c = 0; c < nc; ++c) {
+        float xv[NV * EV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          unpack<T>(ld16(xs + c * row_bytes + (lane + 64 * v) * 16), &xv[v * EV]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          float g = 0.f, u = 0.f;
+#pragma unroll
+          for (int i = 0; i < NV * EV; ++i) {
+            g = fmaf(gw[k][i], xv[i], g);
+            u = fmaf(uw[k][i], xv[i], u);
+          }
+          g = wave_sum(g);
+          u = wave_sum(u);
+          if (lane == 0) {
+            const float sg = g / (1.f + expf(-g));
+            act[static_cast<int64_t>(list[c0 + c]) * I + r0 + rr + k] = sg * u;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 4. down
+template <typename T, int NV>
+__global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(
+    const float* __restrict__ act, int I, const char* __restrict__ wd, int H,
+    const float* __restrict__ gates, int M, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ lists, float* __restrict__ out) {
+  constexpr int EV = Vec<T>::kE;
+  constexpr int kR = 4;                       // rows in flight per wave
+  __shared__ __align__(16) char as[kStageBytes];
+  const int e = blockIdx.y;
+  const int n = counts[e];
+  if (n == 0) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w_row_bytes = static_cast<int64_t>(I) * T::bytes;
+  const int64_t a_row_bytes = static_cast<int64_t>(I) * 4;
+  const int chunk = static_cast<int>(kStageBytes / a_row_bytes);
+  const char* d_e = wd + static_cast<int64_t>(e) * H * w_row_bytes;
+  const int32_t* list = lists + static_cast<int64_t>(e) * M;
+  const int h0 = blockIdx.x * kDownRows + wave * (kDownRows / 4);
+  for (int c0 = 0; c0 < n; c0 += chunk) {
+    const int nc = min(chunk, n - c0);
+    __syncthreads();
+    stage_rows_lds(as, nc, a_row_bytes, [&](int c) {
+      return reinterpret_cast<const char*>(act + static_cast<int64_t>(list[c0 + c]) * I);
+    });
+    __syncthreads();
+    for (int hh = 0; hh < kDownRows / 4; hh += kR) {
+      float w[kR][NV * EV];
+#pragma unroll
+      for (int k = 0; k < kR; ++k)
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          unpack<T>(ld16_nt(d_e + (h0 + hh + k) * w_row_bytes + (lane + 64 * v) * 16),
+                    &w[k][v * EV]);
+      for (int c = 0; c < nc; ++c) {
+        // act slice matching the weight elements: element (lane + 64 v)*EV + i
+        float av[NV * EV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+          for (int q = 0; q < EV / 4; ++q) {
+            const u32x4 a = ld16(as + c * a_row_bytes + ((lane + 64 * v) * EV + 4 * q) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) av[v * EV + 4 * q + i] = __uint_as_float(a[i]);
+          }
+        const int slot = list[c0 + c];
+        const float gate = gates[slot];
+#pragma unroll
+        for (int k = 0; k < kR; ++k) {
+          float d = 0.f;
+#pragma unroll
+          for (int i = 0; i < NV * EV; ++i) d = fmaf(w[k][i], av[i], d);
+          d = wave_sum(d);
+          if (lane == 0) out[static_cast<int64_t>(slot) * H + h0 + hh + k] = gate * d;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 5. combine
+template <typename T>
+__global__ __launch_bounds__(kMoeThreads) void moe_combine_kernel(
+    const float* __restrict__ out, int M, int H, int top_k,
+    const typename T::storage* residual, typename T::storage* y) {   // y may be residual
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kMoeThreads + threadIdx.x;
+  if (i >= static_cast<int64_t>(M) * H) return;
+  const int64_t t = i / H, h = i - t * H;
+  float acc = residual != nullptr ? T::to_f32(residual[i]) : 0.f;
+  for (int j = 0; j < top_k; ++j) acc += out[(t * top_k + j) * H + h];
+  y[i] = T::from_f32(acc);
+}
+
+struct MoeWs {
+  float* logits;
+  int32_t* counts;
+  int32_t* lists;
+  float* act;
+  float* out;
+};
+
+MoeWs moe_ws_layout(void* ws, int M, int H, int E, int top_k, int I) {
+  char* p = static_cast<char*>(ws);
+  MoeWs w;
+  w.logits = reinterpret_cast<float*>(p);
+  p += align_up(static_cast<size_t>(M) * E * 4, 256);
+  w.counts = reinterpret_cast<int32_t*>(p);
+  p += align_up(static_cast<size_t>(E) * 4, 256);
+  w.lists = reinterpret_cast<int32_t*>(p);
+  p += align_up(static_cast<size_t>(E) * M * 4, 256);
+  w.act = reinterpret_cast<float*>(p);
+  p += align_up(static_cast<size_t>(M) * top_k * I * 4, 256);
+  w.out = reinterpret_cast<float*>(p);
+  return w;
+}
+
+template <typename T, int NVH, int NVI>
+hipError_t launch_moe_typed(const void* x, int M, int H, const void* wr, const float* bias, int E,
+                            int top_k, float scale, const void* wg, const void* wu,
+                            const void* wd, int I, const void* residual, void* y, int32_t* ids,
+                            float* gates, void* ws, hipStream_t st) {
+  const MoeWs w = moe_ws_layout(ws, M, H, E, top_k, I);
+  const auto* xc = static_cast<const char*>(x);
+  moe_router_kernel<T, NVH><<<dim3((E + kRouterExpertsPerBlock - 1) / kRouterExpertsPerBlock),
+                              dim3(kMoeThreads), 0, st>>>(xc, M, H, static_cast<const char*>(wr),
+                                                          E, w.logits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  moe_select_kernel<<<dim3(1), dim3(64 * kSelWaves), 0, st>>>(w.logits, bias, M, E, top_k, scale,
+                                                              ids, gates, w.counts, w.lists);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  moe_up_kernel<T, NVH><<<dim3(I / kUpRows, E), dim3(kMoeThreads), 0, st>>>(
+      xc, H, top_k, M, static_cast<const char*>(wg), static_cast<const char*>(wu), I, w.counts,
+      w.lists, w.act);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  moe_down_kernel<T, NVI><<<dim3(H / kDownRows, E), dim3(kMoeThreads), 0, st>>>(
+      w.act, I, static_cast<const char*>(wd), H, gates, M, w.counts, w.lists, w.out);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  using S = typename T::storage;
+  const int64_t n = static_cast<int64_t>(M) * H;
+  moe_combine_kernel<T><<<dim3(static_cast<unsigned>((n + kMoeThreads - 1) / kMoeThreads)),
+                          dim3(kMoeThreads), 0, st>>>(w.out, M, H, top_k,
+                                                      static_cast<const S*>(residual),
+                                                      static_cast<S*>(y));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t moe_ws_bytes(int M, int H, int E, int top_k, int I) {
+  return align_up(static_cast<size_t>(M) * E * 4, 256) + align_up(static_cast<size_t>(E) * 4, 256) +
+         align_up(static_cast<size_t>(E) * M * 4, 256) +
+         align_up(static_cast<size_t>(M) * top_k * I * 4, 256) +
+         align_up(static_cast<size_t>(M) * top_k * H * 4, 256);
+}
+
+bool moe_shape_supported(int H, int I, int E, int top_k, int M, int dtype) {
+  const int ev = dtype == 1 ? 8 : 4;
+  const int nvh = H / (64 * ev), nvi = I / (64 * ev);
+  if (H % (64 * ev) != 0 || I % (64 * ev) != 0) return false;
+  if (nvh < 1 || nvh > 4 || nvi < 1 || nvi > 2) return false;
+  if (H % kDownRows != 0 || I % kUpRows != 0) return false;
+  if (E < 1 || E > 64 * kMaxExpertsPerLane || top_k < 1 || top_k > 16 || top_k > E) return false;
+  if (static_cast<int64_t>(M) * top_k > kMaxSlots) return false;
+  // one token row (and one fp32 activation row) must fit the LDS stage
+  if (static_cast<int64_t>(H) * (dtype == 1 ? 2 : 4) > kStageBytes) return false;
+  if (static_cast<int64_t>(I) * 4 > kStageBytes) return false;
+  return true;
+}
+
+hipError_t launch_moe(const void* x, int M, int H, const void* wr, const float* bias, int E,
+                      int top_k, float scale, const void* wg, const void* wu, const void* wd,
+                      int I, int dtype, const void* residual, void* y, int32_t* ids,
+                      float* gates, void* ws, hipStream_t st) {
+  const int ev = dtype == 1 ? 8 : 4;
+  const int nvh = H / (64 * ev), nvi = I / (64 * ev);
+#define SPRINT_MOE(T, A, B)                                                                   \
+  if (nvh == A && nvi == B)                                                                   \
+    return launch_moe_typed<T, A, B>(x, M, H, wr, bias, E, top_k, scale, wg, wu, wd, I,       \
+                                     residual, y, ids, gates, ws, st);
+  if (dtype == 1) {
+    SPRINT_MOE(BF16, 1, 1) SPRINT_MOE(BF16, 2, 1) SPRINT_MOE(BF16, 4, 1)
+    SPRINT_MOE(BF16, 1, 2) SPRINT_MOE(BF16, 2, 2) SPRINT_MOE(BF16, 4, 2)
+  } else {
+    SPRINT_MOE(F32, 1, 1) SPRINT_MOE(F32, 2, 1) SPRINT_MOE(F32, 4, 1)
+    SPRINT_MOE(F32, 1, 2) SPRINT_MOE(F32, 2, 2) SPRINT_MOE(F32, 4, 2)
+  }
+#undef SPRINT_MOE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sprint

@@ -55,4 +55,12 @@ hipError_t launch_append_rows(const void* old, const int32_t* cu_old, int nseq, 
                               const void* blk, int n_blk, int64_t row_bytes, void* out,
                               int32_t* cu_out, hipStream_t st);
 
+// ---- MoE FFN on synthetic weights
+size_t moe_ws_bytes(int M, int H, int E, int top_k, int I);
+bool moe_shape_supported(int H, int I, int E, int top_k, int M, int dtype);
+hipError_t launch_moe(const void* x, int M, int H, const void* wr, const float* bias, int E,
+                      int top_k, float scale, const void* wg, const void* wu, const void* wd,
+                      int I, int dtype, const void* residual, void* y, int32_t* ids,
+                      float* gates, void* ws, hipStream_t st);
+
 }  // namespace sprint

@@ -58,6 +58,10 @@ _SIGS = {
                                               _c_void_p, _i32, _i64, _i64, _c_void_p, _c_void_p,
                                               _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
                                               _c_void_p, _c_void_p, _size, _c_void_p]),
+    "moe_ffn_ws": (_size, [_i32, _i32, _i32, _i32, _i32]),
+    "moe_ffn": (ctypes.c_int, [_c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i32, _f32,
+                               _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _c_void_p,
+                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
     "sprint_append_rows": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i64, _c_void_p, _i32, _i64,
                                           _c_void_p, _c_void_p, _c_void_p]),
 }
@@ -336,3 +340,31 @@ def sprint_prune_kv_layers(score, modality, cu_len, keep, cu_kept, total_kept: i
         int(total_kept), _ptr(K), _ptr(V), n_layers, Hkv, D, _dt(K), _ptr(K_out), _ptr(V_out),
         _ptr(kept_idx), _ptr(ws), ws.numel(), _stream(stream)))
     return K_out, V_out, kept_idx
+
+
+def moe_ffn_ws(M: int, H: int, n_experts: int, top_k: int, inter: int) -> int:
+    return int(lib().moe_ffn_ws(M, H, n_experts, top_k, inter))
+
+
+def moe_ffn(x, w_router, bias, w_gate, w_up, w_down, top_k: int, route_scale: float = 2.5,
+            residual=None, y=None, expert_ids=None, gates=None, ws=None, stream=None):
+    """MoE FFN with sigmoid routing, bias-steered top-k and SwiGLU experts.
+    x [M, H]; w_router [E, H]; bias [E] float32; w_gate, w_up [E, I, H];
+    w_down [E, H, I].  Returns (y, expert_ids, gates)."""
+    for t, n in ((x, "x"), (w_router, "w_router"), (bias, "bias"), (w_gate, "w_gate"),
+                 (w_up, "w_up"), (w_down, "w_down")):
+        _dev(t, n)
+    M, H = x.shape
+    E, inter = w_gate.shape[0], w_gate.shape[1]
+    dev = x.device
+    y = torch.empty_like(x) if y is None else y
+    if expert_ids is None:
+        expert_ids = torch.empty((M, top_k), dtype=torch.int32, device=dev)
+    if gates is None:
+        gates = torch.empty((M, top_k), dtype=torch.float32, device=dev)
+    ws = _ws(moe_ffn_ws(M, H, E, top_k, inter), dev, ws)
+    _check("moe_ffn", lib().moe_ffn(
+        _ptr(x), M, H, _ptr(w_router), _ptr(bias), E, top_k, float(route_scale), _ptr(w_gate),
+        _ptr(w_up), _ptr(w_down), inter, _dt(x), _ptr(residual), _ptr(y), _ptr(expert_ids),
+        _ptr(gates), _ptr(ws), ws.numel(), _stream(stream)))
+    return y, expert_ids, gates

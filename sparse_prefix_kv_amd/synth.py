@@ -27,6 +27,9 @@ draws its own Q, Kb, Vb (same shapes and laws, in that order) from
 ``default_rng([seed, b])``.  The rows a finished block adds to the prefix
 are not drawn: they are that block's own K/V and outputs.
 
+MoE FFN weights (``make_moe_weights``) come from ``default_rng([seed,
+2**21])``.
+
 Several layers: layer 0 uses the draws above; layer l >= 1 draws its own
 Q, K (with its own key scales), V, Kb, Vb from ``default_rng([seed, 2**20,
 l])``.  The prefix hidden states and the LM head are shared.
@@ -250,6 +253,23 @@ def make_layer_inputs(wl: Workload, layout: "Layout", l: int, seed: int = 0,
     if wl.dtype == "bf16":
         Q, K, V, Kb, Vb = (bf16_round(a) for a in (Q, K, V, Kb, Vb))
     return Q, K, V, Kb, Vb
+
+
+def make_moe_weights(H: int, E: int, inter: int, dtype: str, seed: int = 0):
+    """Synthetic MoE FFN weights, from default_rng([seed, 2**21]) in the order
+    router [E, H] ~ N(0, 1/H), bias [E] ~ U(-0.05, 0.05), gate and up
+    [E, inter, H] ~ N(0, 1/H), down [E, H, inter] ~ N(0, 1/inter); rounded to
+    bf16 for bf16 (the bias stays float32)."""
+    rng = np.random.default_rng([seed, 1 << 21])
+    f32 = np.float32
+    wr = rng.standard_normal((E, H), dtype=f32) * f32(H ** -0.5)
+    bias = rng.uniform(-0.05, 0.05, E).astype(f32)
+    wg = rng.standard_normal((E, inter, H), dtype=f32) * f32(H ** -0.5)
+    wu = rng.standard_normal((E, inter, H), dtype=f32) * f32(H ** -0.5)
+    wd = rng.standard_normal((E, H, inter), dtype=f32) * f32(inter ** -0.5)
+    if dtype == "bf16":
+        wr, wg, wu, wd = (bf16_round(a) for a in (wr, wg, wu, wd))
+    return wr, bias, wg, wu, wd
 
 
 # ---------------------------------------------------------------------------

@@ -25,7 +25,7 @@ def _header_functions():
 def test_library_exports_every_declared_function():
     lib = sprint.lib()
     declared = _header_functions()
-    assert len(declared) >= 17
+    assert len(declared) >= 19
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(sprint.EXPORTS)
