@@ -56,6 +56,8 @@ def parse():
                     help="blocks of the generation measurement (0: skip it)")
     ap.add_argument("--layers", type=int, default=16,
                     help="layers of the several-layer measurement (0: skip it)")
+    ap.add_argument("--moe-experts", type=int, default=256,
+                    help="experts of the MoE FFN measurement (0: skip it)")
     ap.add_argument("--profile-call", default=None,
                     help="only launch this call --steps times (for rocprofv3 counter runs); "
                          "'copy' launches a 256 MiB device-to-device copy for calibration")
@@ -299,6 +301,73 @@ def measure_layers(args, x, n_steps, torch, reps=5):
     return out
 
 
+def measure_moe(args, blk, wl, torch, reps=20):
+    """The MoE FFN on the block's attention outputs (M = 32 tokens), with
+    synthetic weights drawn on the GPU (the laws of synth.make_moe_weights,
+    bf16): 20 back-to-back calls captured in a graph, HIP events around the
+    replay.  Algorithmic bytes: every chosen expert's three matrices once,
+    the router, and x, the residual and y."""
+    from sparse_prefix_kv_amd import sprint as sp
+    E, K, I, H = args.moe_experts, 8, 512, wl.H
+    g = torch.Generator(device="cuda").manual_seed(0)
+    bf = torch.bfloat16
+
+    def normal(shape, std):
+        return (torch.randn(shape, generator=g, device="cuda", dtype=torch.float32) * std).to(bf)
+    wr = normal((E, H), H ** -0.5)
+    bias = (torch.rand(E, generator=g, device="cuda") - 0.5) * 0.1
+    wg = torch.empty((E, I, H), dtype=bf, device="cuda")
+    wu = torch.empty_like(wg)
+    wd = torch.empty((E, H, I), dtype=bf, device="cuda")
+    for e in range(E):            # per expert, to bound the fp32 temporaries
+        wg[e] = normal((I, H), H ** -0.5)
+        wu[e] = normal((I, H), H ** -0.5)
+        wd[e] = normal((H, I), I ** -0.5)
+    M = blk.nseq * blk.Lq
+    x = blk.O.view(M, H)
+    y = torch.empty_like(x)
+    ids = torch.empty((M, K), dtype=torch.int32, device="cuda")
+    gates = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sp.moe_ffn_ws(M, H, E, K, I), dtype=torch.uint8, device="cuda")
+
+    def call():
+        sp.moe_ffn(x, wr, bias, wg, wu, wd, K, residual=x, y=y, expert_ids=ids, gates=gates,
+                   ws=ws)
+    call()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            call()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(5):
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+    us = sorted(ts)[len(ts) // 2]
+    distinct = int(torch.unique(ids).numel())
+    alg = distinct * 3 * I * H * 2 + E * H * 2 + 3 * M * H * 2
+    del graph, wg, wu, wd
+    torch.cuda.synchronize()
+    return {"config": f"E {E}, top-{K}, inter {I}, H {H}, M {M} tokens, bf16",
+            "us": round(us, 2), "distinct_experts": distinct, "alg_bytes": alg,
+            "gbs": round(alg / us / 1e3, 1), "hbm_frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4),
+            "bound": "hbm",
+            "note": "weights are synthetic (N(0,1/H), N(0,1/I)); the page gives no expert sizes"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -500,6 +569,13 @@ def main():
             f"{layers['per_layer']['block_ms']:.3f} ms per-layer sets, "
             f"{layers['full_prefix']['block_ms']:.3f} ms full prefix")
 
+    # ---------------------------------------------------------------- MoE FFN
+    moe = None
+    if args.moe_experts > 0 and bf16:
+        moe = measure_moe(args, blk, wl, torch)
+        log(f"[bench] MoE FFN ({moe['config']}): {moe['us']:.1f} us, {moe['gbs']:.0f} GB/s over "
+            f"{moe['distinct_experts']} chosen experts")
+
     # ---------------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -546,6 +622,7 @@ def main():
                                                           "hardware and workload not given)"},
         "generation": generation,
         "layers": layers,
+        "moe": moe,
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,

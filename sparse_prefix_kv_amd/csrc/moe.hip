@@ -19,12 +19,12 @@
 // those of experts nobody chose exit at once):
 //   1. moe_router_kernel   logits [M, E]: a wave holds one router row in
 //                          registers and dots it with every token;
-//   2. moe_select_kernel   one block: sigmoid, biased top-k by wave arg-max
-//                          rounds, gates; then, per expert, its slots in slot
-//                          order (slot = token * top_k + j), so the grouping is
-//                          deterministic;
-//   3. moe_up_kernel       (I tile, expert): silu(gate) * up of each of the
-//                          expert's slots, fp32;
+//   2. moe_select_kernel   a wave per token: sigmoid, biased top-k by wave
+//                          arg-max rounds, gates;
+//   3. moe_up_kernel       (I tile, expert): the block first lists the slots
+//                          (token * top_k + j) that chose its expert, in slot
+//                          order (ballots), so the grouping is deterministic;
+//                          then silu(gate) * up of each of them, fp32;
 //   4. moe_down_kernel     (H tile, expert): g * (W_down act) per slot, fp32;
 //   5. moe_combine_kernel  y = residual + sum_j out[t*top_k + j] in order j.
 // Every sum has a fixed order, so results are bitwise reproducible.
@@ -65,12 +65,16 @@ __device__ __forceinline__ void unpack<F32>(u32x4 v, float* out) {
 
 // ---------------------------------------------------------------- 1. router
 // Lane l of a wave holds elements [16*(l + 64*v), +16 bytes) of a row for
-// v < NV (NV = H / (64 * elements per vector)).
+// v < NV (NV = H / (64 * elements per vector)).  Block (g, b): experts
+// 8g .. 8g+7 (two per wave, rows held in registers) against tokens
+// 8b .. 8b+7, four tokens' rows loaded at a time.
+constexpr int kRouterTokens = 8;
 template <typename T, int NV>
 __global__ __launch_bounds__(kMoeThreads) void moe_router_kernel(
     const char* __restrict__ x, int M, int H, const char* __restrict__ wr, int E,
     float* __restrict__ logits) {
   constexpr int EV = Vec<T>::kE;
+  constexpr int kTG = 4;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row_bytes = static_cast<int64_t>(H) * T::bytes;
   const int e0 = blockIdx.x * kRouterExpertsPerBlock + 2 * wave;
@@ -82,102 +86,113 @@ __global__ __launch_bounds__(kMoeThreads) void moe_router_kernel(
     for (int v = 0; v < NV; ++v)
       unpack<T>(ld16_nt(wr + e * row_bytes + (lane + 64 * v) * 16), &r[k][v * EV]);
   }
-  for (int t = 0; t < M; ++t) {
-    float xv[NV * EV];
+  const int tb = blockIdx.y * kRouterTokens;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) unpack<T>(ld16(x + t * row_bytes + (lane + 64 * v) * 16), &xv[v * EV]);
-    float d0 = 0.f, d1 = 0.f;
+  for (int g = 0; g < kRouterTokens; g += kTG) {
+    float xv[kTG][NV * EV];
 #pragma unroll
-    for (int i = 0; i < NV * EV; ++i) {
-      d0 = fmaf(r[0][i], xv[i], d0);
-      d1 = fmaf(r[1][i], xv[i], d1);
+    for (int u = 0; u < kTG; ++u) {
+      const int t = min(tb + g + u, M - 1);
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+        unpack<T>(ld16(x + t * row_bytes + (lane + 64 * v) * 16), &xv[u][v * EV]);
     }
-    d0 = wave_sum(d0);
-    d1 = wave_sum(d1);
-    if (lane == 0) {
-      if (e0 < E) logits[static_cast<int64_t>(t) * E + e0] = d0;
-      if (e0 + 1 < E) logits[static_cast<int64_t>(t) * E + e0 + 1] = d1;
+#pragma unroll
+    for (int u = 0; u < kTG; ++u) {
+      const int t = tb + g + u;
+      float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < NV * EV; ++i) {
+        d0 = fmaf(r[0][i], xv[u][i], d0);
+        d1 = fmaf(r[1][i], xv[u][i], d1);
+      }
+      d0 = wave_sum(d0);
+      d1 = wave_sum(d1);
+      if (lane == 0 && t < M) {
+        if (e0 < E) logits[static_cast<int64_t>(t) * E + e0] = d0;
+        if (e0 + 1 < E) logits[static_cast<int64_t>(t) * E + e0 + 1] = d1;
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------- 2. select
-constexpr int kSelWaves = 16;
-constexpr int kMaxExpertsPerLane = 16;      // E <= 1024
+// One wave per token; lane l holds experts l, l + 64, ... (NE of them).  Each
+// of the top_k rounds takes the lane's best, then a wave arg-max (ties to the
+// lowest expert); lane j keeps the affinity of the j-th choice.
 constexpr int kMaxSlots = 8192;             // M * top_k
+constexpr int kMaxTokens = 1024;            // an expert's slot list (LDS)
 
-__global__ __launch_bounds__(64 * kSelWaves) void moe_select_kernel(
+template <int NE>
+__global__ __launch_bounds__(kMoeThreads) void moe_select_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int M, int E, int top_k,
-    float scale, int32_t* __restrict__ ids, float* __restrict__ gates,
-    int32_t* __restrict__ counts, int32_t* __restrict__ lists) {
-  __shared__ int32_t s_ids[kMaxSlots];
+    float scale, int32_t* __restrict__ ids, float* __restrict__ gates) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ne = (E + 63) / 64;
-  for (int t = wave; t < M; t += kSelWaves) {
-    float aff[kMaxExpertsPerLane], sel[kMaxExpertsPerLane];
+  const int t = blockIdx.x * (kMoeThreads / 64) + wave;
+  if (t >= M) return;
+  float aff[NE], sel[NE];
 #pragma unroll
-    for (int i = 0; i < kMaxExpertsPerLane; ++i) {
-      const int e = lane + 64 * i;
-      const bool ok = i < ne && e < E;
-      const float z = ok ? logits[static_cast<int64_t>(t) * E + e] : 0.f;
-      aff[i] = 1.f / (1.f + expf(-z));
-      sel[i] = ok ? aff[i] + bias[e] : -INFINITY;
-    }
-    float chosen_aff[16];
-    float ssum = 0.f;
-    for (int j = 0; j < top_k; ++j) {
-      // this lane's best (largest selection score, lowest expert on ties)
-      float bv = -INFINITY;
-      int be = INT_MAX;
+  for (int i = 0; i < NE; ++i) {
+    const int e = lane + 64 * i;
+    const bool ok = e < E;
+    const float z = ok ? logits[static_cast<int64_t>(t) * E + e] : 0.f;
+    aff[i] = 1.f / (1.f + expf(-z));
+    sel[i] = ok ? aff[i] + bias[e] : -INFINITY;
+  }
+  float my_aff = 0.f, ssum = 0.f;
+  for (int j = 0; j < top_k; ++j) {
+    float bv = -INFINITY;
+    int be = INT_MAX;
 #pragma unroll
-      for (int i = 0; i < kMaxExpertsPerLane; ++i)
-        if (sel[i] > bv) {     // ascending i: the first maximum is the lowest expert
-          bv = sel[i];
-          be = lane + 64 * i;
-        }
-      // wave arg-max, ties to the lowest expert
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float ov = shfl_xor_f(bv, m);
-        const int oe = shfl_xor_i(be, m);
-        if (ov > bv || (ov == bv && oe < be)) {
-          bv = ov;
-          be = oe;
-        }
+    for (int i = 0; i < NE; ++i)
+      if (sel[i] > bv) {       // ascending i: the first maximum is the lowest expert
+        bv = sel[i];
+        be = lane + 64 * i;
       }
-      // the owner lane removes it and broadcasts its affinity
-      float a = 0.f;
 #pragma unroll
-      for (int i = 0; i < kMaxExpertsPerLane; ++i)
-        if (lane + 64 * i == be) {
-          a = aff[i];
-          sel[i] = -INFINITY;
-        }
-      a = __shfl(a, be & 63, 64);
-      chosen_aff[j & 15] = a;
-      ssum += a;
-      if (lane == 0) {
-        ids[static_cast<int64_t>(t) * top_k + j] = be;
-        s_ids[t * top_k + j] = be;
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ov = shfl_xor_f(bv, m);
+      const int oe = shfl_xor_i(be, m);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
       }
     }
-    if (lane < top_k) {
-      float a = 0.f;
+    float a = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j == lane) a = chosen_aff[j];
-      gates[static_cast<int64_t>(t) * top_k + lane] = scale * a / ssum;
-    }
+    for (int i = 0; i < NE; ++i)
+      if (lane + 64 * i == be) {
+        a = aff[i];
+        sel[i] = -INFINITY;
+      }
+    a = __shfl(a, be & 63, 64);
+    if (lane == j) my_aff = a;
+    ssum += a;
+    if (lane == 0) ids[static_cast<int64_t>(t) * top_k + j] = be;
   }
-  __syncthreads();
-  // each expert's slots, in slot order
-  const int n_slots = M * top_k;
-  for (int e = threadIdx.x; e < E; e += 64 * kSelWaves) {
-    int c = 0;
-    for (int sl = 0; sl < n_slots; ++sl)
-      if (s_ids[sl] == e) lists[static_cast<int64_t>(e) * M + c++] = sl;
-    counts[e] = c;
+  if (lane < top_k) gates[static_cast<int64_t>(t) * top_k + lane] = scale * my_aff / ssum;
+}
+
+// The slots (token * top_k + j) that chose expert e, in slot order, into LDS:
+// 256 ids per round, a ballot per wave and the waves' counts in order.
+// Returns the count (block-uniform).
+__device__ __forceinline__ int build_slot_list(const int32_t* __restrict__ ids, int n_slots,
+                                               int e, int32_t* list, int* s_wave) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int total = 0;
+  for (int base = 0; base < n_slots; base += kMoeThreads) {
+    const int sl = base + threadIdx.x;
+    const bool f = sl < n_slots && ids[sl] == e;
+    const uint64_t bal = __ballot(f);
+    if (lane == 0) s_wave[wave] = __popcll(bal);
+    __syncthreads();
+    int before = total;
+    for (int w = 0; w < wave; ++w) before += s_wave[w];
+    if (f) list[before + __popcll(bal & ((1ull << lane) - 1ull))] = sl;
+    for (int w = 0; w < kMoeThreads / 64; ++w) total += s_wave[w];
+    __syncthreads();
   }
+  return total;
 }
 
 // Stage rows of the expert's slots into LDS (as raw elements); row of slot
@@ -192,29 +207,33 @@ __device__ __forceinline__ void stage_rows_lds(char* lds, int n, int64_t row_byt
 }
 
 // ---------------------------------------------------------------- 3. gate/up
+// Block (tile, e): rows [32 tile, +32) of expert e's gate and up matrices
+// (8 per wave, two at a time, both matrices' loads in flight together)
+// against the expert's token rows staged in LDS.  (Holding the rows packed
+// and four at a time under a 128-register cap made the compiler spill.)
 template <typename T, int NV>
 __global__ __launch_bounds__(kMoeThreads) void moe_up_kernel(
-    const char* __restrict__ x, int H, int top_k, int M, const char* __restrict__ wg,
-    const char* __restrict__ wu, int I, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ lists, float* __restrict__ act) {
+    const char* __restrict__ x, int H, int top_k, int n_slots, const char* __restrict__ wg,
+    const char* __restrict__ wu, int I, const int32_t* __restrict__ ids,
+    float* __restrict__ act) {
   constexpr int EV = Vec<T>::kE;
   __shared__ __align__(16) char xs[kStageBytes];
+  __shared__ int32_t list[kMaxTokens];
+  __shared__ int s_wave[kMoeThreads / 64];
   const int e = blockIdx.y;
-  const int n = counts[e];
+  const int n = build_slot_list(ids, n_slots, e, list, s_wave);
   if (n == 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row_bytes = static_cast<int64_t>(H) * T::bytes;
   const int chunk = static_cast<int>(kStageBytes / row_bytes);
   const char* g_e = wg + static_cast<int64_t>(e) * I * row_bytes;
   const char* u_e = wu + static_cast<int64_t>(e) * I * row_bytes;
-  const int32_t* list = lists + static_cast<int64_t>(e) * M;
   const int r0 = blockIdx.x * kUpRows + wave * (kUpRows / 4);
   for (int c0 = 0; c0 < n; c0 += chunk) {
     const int nc = min(chunk, n - c0);
     __syncthreads();
     stage_rows_lds(xs, nc, row_bytes, [&](int c) { return x + (list[c0 + c] / top_k) * row_bytes; });
     __syncthreads();
-    // two rows at a time: both rows' gate and up loads in flight together
     for (int rr = 0; rr < kUpRows / 4; rr += 2) {
       float gw[2][NV * EV], uw[2][NV * EV];
 #pragma unroll
@@ -251,59 +270,71 @@ __global__ __launch_bounds__(kMoeThreads) void moe_up_kernel(
 }
 
 // ---------------------------------------------------------------- 4. down
-template <typename T, int NV>
+// Block (tile, e): rows [64 tile, +64) of expert e's down matrix, 16 per
+// wave.  Eight lanes share a row (lane l: row l/8 of a group of eight, 16-byte
+// vectors l%8, l%8 + 8, ...), so one load instruction covers eight rows of
+// 128 contiguous bytes and a row's dot product needs a 3-step reduction
+// among its eight lanes.  A wave holds G groups of eight rows in registers,
+// their loads issued before the expert's activations are staged in LDS.
+template <typename T, int VPL>
 __global__ __launch_bounds__(kMoeThreads) void moe_down_kernel(
     const float* __restrict__ act, int I, const char* __restrict__ wd, int H,
-    const float* __restrict__ gates, int M, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ lists, float* __restrict__ out) {
+    const float* __restrict__ gates, int n_slots, const int32_t* __restrict__ ids,
+    float* __restrict__ out) {
   constexpr int EV = Vec<T>::kE;
-  constexpr int kR = 4;                       // rows in flight per wave
+  constexpr int kRW = kDownRows / 4;          // rows per wave
+  constexpr int kG = VPL * EV <= 64 ? 2 : 1;  // groups of eight rows in flight
   __shared__ __align__(16) char as[kStageBytes];
+  __shared__ int32_t list[kMaxTokens];
+  __shared__ int s_wave[kMoeThreads / 64];
   const int e = blockIdx.y;
-  const int n = counts[e];
+  const int n = build_slot_list(ids, n_slots, e, list, s_wave);
   if (n == 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rl = lane >> 3, sub = lane & 7;
   const int64_t w_row_bytes = static_cast<int64_t>(I) * T::bytes;
   const int64_t a_row_bytes = static_cast<int64_t>(I) * 4;
   const int chunk = static_cast<int>(kStageBytes / a_row_bytes);
   const char* d_e = wd + static_cast<int64_t>(e) * H * w_row_bytes;
-  const int32_t* list = lists + static_cast<int64_t>(e) * M;
-  const int h0 = blockIdx.x * kDownRows + wave * (kDownRows / 4);
-  for (int c0 = 0; c0 < n; c0 += chunk) {
-    const int nc = min(chunk, n - c0);
-    __syncthreads();
-    stage_rows_lds(as, nc, a_row_bytes, [&](int c) {
-      return reinterpret_cast<const char*>(act + static_cast<int64_t>(list[c0 + c]) * I);
-    });
-    __syncthreads();
-    for (int hh = 0; hh < kDownRows / 4; hh += kR) {
-      float w[kR][NV * EV];
+  const int h0 = blockIdx.x * kDownRows + wave * kRW;
+  for (int g0 = 0; g0 < kRW / 8; g0 += kG) {
+    float w[kG][VPL * EV];
 #pragma unroll
-      for (int k = 0; k < kR; ++k)
+    for (int gi = 0; gi < kG; ++gi)
 #pragma unroll
-        for (int v = 0; v < NV; ++v)
-          unpack<T>(ld16_nt(d_e + (h0 + hh + k) * w_row_bytes + (lane + 64 * v) * 16),
-                    &w[k][v * EV]);
+      for (int v = 0; v < VPL; ++v)
+        unpack<T>(ld16_nt(d_e + (h0 + 8 * (g0 + gi) + rl) * w_row_bytes + (sub + 8 * v) * 16),
+                  &w[gi][v * EV]);
+    for (int c0 = 0; c0 < n; c0 += chunk) {
+      const int nc = min(chunk, n - c0);
+      __syncthreads();
+      stage_rows_lds(as, nc, a_row_bytes, [&](int c) {
+        return reinterpret_cast<const char*>(act + static_cast<int64_t>(list[c0 + c]) * I);
+      });
+      __syncthreads();
       for (int c = 0; c < nc; ++c) {
-        // act slice matching the weight elements: element (lane + 64 v)*EV + i
-        float av[NV * EV];
+        // activations matching this lane's weight elements (sub + 8 v)*EV + i
+        float av[VPL * EV];
 #pragma unroll
-        for (int v = 0; v < NV; ++v)
+        for (int v = 0; v < VPL; ++v)
 #pragma unroll
           for (int q = 0; q < EV / 4; ++q) {
-            const u32x4 a = ld16(as + c * a_row_bytes + ((lane + 64 * v) * EV + 4 * q) * 4);
+            const u32x4 a4 = ld16(as + c * a_row_bytes + ((sub + 8 * v) * EV + 4 * q) * 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) av[v * EV + 4 * q + i] = __uint_as_float(a[i]);
+            for (int i = 0; i < 4; ++i) av[v * EV + 4 * q + i] = __uint_as_float(a4[i]);
           }
         const int slot = list[c0 + c];
         const float gate = gates[slot];
 #pragma unroll
-        for (int k = 0; k < kR; ++k) {
+        for (int gi = 0; gi < kG; ++gi) {
           float d = 0.f;
 #pragma unroll
-          for (int i = 0; i < NV * EV; ++i) d = fmaf(w[k][i], av[i], d);
-          d = wave_sum(d);
-          if (lane == 0) out[static_cast<int64_t>(slot) * H + h0 + hh + k] = gate * d;
+          for (int i = 0; i < VPL * EV; ++i) d = fmaf(w[gi][i], av[i], d);
+          d += shfl_xor_f(d, 1);
+          d += shfl_xor_f(d, 2);
+          d += shfl_xor_f(d, 4);
+          if (sub == 0)
+            out[static_cast<int64_t>(slot) * H + h0 + 8 * (g0 + gi) + rl] = gate * d;
         }
       }
     }
@@ -325,8 +356,6 @@ __global__ __launch_bounds__(kMoeThreads) void moe_combine_kernel(
 
 struct MoeWs {
   float* logits;
-  int32_t* counts;
-  int32_t* lists;
   float* act;
   float* out;
 };
@@ -336,10 +365,6 @@ MoeWs moe_ws_layout(void* ws, int M, int H, int E, int top_k, int I) {
   MoeWs w;
   w.logits = reinterpret_cast<float*>(p);
   p += align_up(static_cast<size_t>(M) * E * 4, 256);
-  w.counts = reinterpret_cast<int32_t*>(p);
-  p += align_up(static_cast<size_t>(E) * 4, 256);
-  w.lists = reinterpret_cast<int32_t*>(p);
-  p += align_up(static_cast<size_t>(E) * M * 4, 256);
   w.act = reinterpret_cast<float*>(p);
   p += align_up(static_cast<size_t>(M) * top_k * I * 4, 256);
   w.out = reinterpret_cast<float*>(p);
@@ -353,20 +378,31 @@ hipError_t launch_moe_typed(const void* x, int M, int H, const void* wr, const f
                             float* gates, void* ws, hipStream_t st) {
   const MoeWs w = moe_ws_layout(ws, M, H, E, top_k, I);
   const auto* xc = static_cast<const char*>(x);
-  moe_router_kernel<T, NVH><<<dim3((E + kRouterExpertsPerBlock - 1) / kRouterExpertsPerBlock),
+  moe_router_kernel<T, NVH><<<dim3((E + kRouterExpertsPerBlock - 1) / kRouterExpertsPerBlock,
+                                   (M + kRouterTokens - 1) / kRouterTokens),
                               dim3(kMoeThreads), 0, st>>>(xc, M, H, static_cast<const char*>(wr),
                                                           E, w.logits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  moe_select_kernel<<<dim3(1), dim3(64 * kSelWaves), 0, st>>>(w.logits, bias, M, E, top_k, scale,
-                                                              ids, gates, w.counts, w.lists);
+  const int n_slots = M * top_k;
+  const dim3 sgrid((M + 3) / 4);
+  if (E <= 64)
+    moe_select_kernel<1><<<sgrid, dim3(kMoeThreads), 0, st>>>(w.logits, bias, M, E, top_k, scale,
+                                                              ids, gates);
+  else if (E <= 256)
+    moe_select_kernel<4><<<sgrid, dim3(kMoeThreads), 0, st>>>(w.logits, bias, M, E, top_k, scale,
+                                                              ids, gates);
+  else
+    moe_select_kernel<16><<<sgrid, dim3(kMoeThreads), 0, st>>>(w.logits, bias, M, E, top_k,
+                                                               scale, ids, gates);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   moe_up_kernel<T, NVH><<<dim3(I / kUpRows, E), dim3(kMoeThreads), 0, st>>>(
-      xc, H, top_k, M, static_cast<const char*>(wg), static_cast<const char*>(wu), I, w.counts,
-      w.lists, w.act);
+      xc, H, top_k, n_slots, static_cast<const char*>(wg), static_cast<const char*>(wu), I, ids,
+      w.act);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  moe_down_kernel<T, NVI><<<dim3(H / kDownRows, E), dim3(kMoeThreads), 0, st>>>(
-      w.act, I, static_cast<const char*>(wd), H, gates, M, w.counts, w.lists, w.out);
+  // vectors per lane per down row: I / (8 lanes * elements per vector)
+  moe_down_kernel<T, NVI * 8><<<dim3(H / kDownRows, E), dim3(kMoeThreads), 0, st>>>(
+      w.act, I, static_cast<const char*>(wd), H, gates, n_slots, ids, w.out);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   using S = typename T::storage;
   const int64_t n = static_cast<int64_t>(M) * H;
@@ -380,8 +416,7 @@ hipError_t launch_moe_typed(const void* x, int M, int H, const void* wr, const f
 }  // namespace
 
 size_t moe_ws_bytes(int M, int H, int E, int top_k, int I) {
-  return align_up(static_cast<size_t>(M) * E * 4, 256) + align_up(static_cast<size_t>(E) * 4, 256) +
-         align_up(static_cast<size_t>(E) * M * 4, 256) +
+  return align_up(static_cast<size_t>(M) * E * 4, 256) +
          align_up(static_cast<size_t>(M) * top_k * I * 4, 256) +
          align_up(static_cast<size_t>(M) * top_k * H * 4, 256);
 }
@@ -392,8 +427,8 @@ bool moe_shape_supported(int H, int I, int E, int top_k, int M, int dtype) {
   if (H % (64 * ev) != 0 || I % (64 * ev) != 0) return false;
   if (nvh < 1 || nvh > 4 || nvi < 1 || nvi > 2) return false;
   if (H % kDownRows != 0 || I % kUpRows != 0) return false;
-  if (E < 1 || E > 64 * kMaxExpertsPerLane || top_k < 1 || top_k > 16 || top_k > E) return false;
-  if (static_cast<int64_t>(M) * top_k > kMaxSlots) return false;
+  if (E < 1 || E > 1024 || top_k < 1 || top_k > 16 || top_k > E) return false;
+  if (static_cast<int64_t>(M) * top_k > kMaxSlots || M > kMaxTokens) return false;
   // one token row (and one fp32 activation row) must fit the LDS stage
   if (static_cast<int64_t>(H) * (dtype == 1 ? 2 : 4) > kStageBytes) return false;
   if (static_cast<int64_t>(I) * 4 > kStageBytes) return false;
