@@ -301,7 +301,7 @@ def measure_layers(args, x, n_steps, torch, reps=5):
     return out
 
 
-def measure_moe(args, blk, wl, torch, reps=20):
+def measure_moe(args, blk, x_in, wl, n_steps, torch, reps=20):
     """The MoE FFN on the block's attention outputs (M = 32 tokens), with
     synthetic weights drawn on the GPU (the laws of synth.make_moe_weights,
     bf16): 20 back-to-back calls captured in a graph, HIP events around the
@@ -359,12 +359,44 @@ def measure_moe(args, blk, wl, torch, reps=20):
     us = sorted(ts)[len(ts) // 2]
     distinct = int(torch.unique(ids).numel())
     alg = distinct * 3 * I * H * 2 + E * H * 2 + 3 * M * H * 2
-    del graph, wg, wu, wd
+    del graph
+
+    # a pruned denoising step with the MoE FFN between attention and the LM
+    # head, against the same step without it (8 steps captured in a graph)
+    from sparse_prefix_kv_amd.block import SprintBlock
+
+    def step_us(b):
+        b.run_block(n_steps)
+        torch.cuda.synchronize()
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gs):
+            for t in range(1, n_steps + 1):
+                b.pruned_step(t)
+        torch.cuda.current_stream().wait_stream(gs)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for t in range(1, n_steps + 1):
+                b.pruned_step(t)
+        gr.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (10 * n_steps)
+    blk_moe = SprintBlock(x_in, "cuda", moe=(wr, bias, wg, wu, wd, K, 2.5))
+    t_moe = step_us(blk_moe)
+    t_plain = step_us(blk)
+    del blk_moe, wg, wu, wd
     torch.cuda.synchronize()
     return {"config": f"E {E}, top-{K}, inter {I}, H {H}, M {M} tokens, bf16",
             "us": round(us, 2), "distinct_experts": distinct, "alg_bytes": alg,
             "gbs": round(alg / us / 1e3, 1), "hbm_frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4),
             "bound": "hbm",
+            "pruned_step_us": {"with_moe": round(t_moe, 2), "without": round(t_plain, 2)},
             "note": "weights are synthetic (N(0,1/H), N(0,1/I)); the page gives no expert sizes"}
 
 
@@ -572,7 +604,7 @@ def main():
     # ---------------------------------------------------------------- MoE FFN
     moe = None
     if args.moe_experts > 0 and bf16:
-        moe = measure_moe(args, blk, wl, torch)
+        moe = measure_moe(args, blk, x, wl, n_steps, torch)
         log(f"[bench] MoE FFN ({moe['config']}): {moe['us']:.1f} us, {moe['gbs']:.0f} GB/s over "
             f"{moe['distinct_experts']} chosen experts")
 

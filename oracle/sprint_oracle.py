@@ -267,6 +267,7 @@ class BlockResult:
     kept_idx: np.ndarray
     cu_kept: np.ndarray
     outputs: List[np.ndarray] = field(default_factory=list)    # O per step
+    moe_ids: List[np.ndarray] = field(default_factory=list)    # experts per step (with an MoE)
     confs: List[np.ndarray] = field(default_factory=list)      # block conf per step
     argmaxes: List[np.ndarray] = field(default_factory=list)
     masks: List[np.ndarray] = field(default_factory=list)      # mask after each step
@@ -276,7 +277,8 @@ class BlockResult:
 
 def run_block(Q, K, V, Kb, Vb, hidden, W, cu_len, modality, r_text, r_img,
               tau, T: Optional[int], n_steps: int, alpha: float = 0.5,
-              pass_rows: Optional[np.ndarray] = None) -> BlockResult:
+              pass_rows: Optional[np.ndarray] = None, moe=None,
+              store_dtype: Optional[str] = None) -> BlockResult:
     """The SPRINT block as one composition (Sparse Prefix Retention +
     Non-uniform Token Unmasking).
 
@@ -287,6 +289,10 @@ def run_block(Q, K, V, Kb, Vb, hidden, W, cu_len, modality, r_text, r_img,
     not part of this path).  T = None means at least one acceptance per step.
     `pass_rows` restricts the prefix LM head to those rows (others get conf 0)
     for large sizes; None computes all of them.
+    `moe` = (w_router, bias, w_gate, w_up, w_down, top_k, route_scale) puts an
+    MoE FFN between attention and the LM head: the LM head reads
+    O + moe_ffn(O), with O stored in `store_dtype` first (the workload's
+    dtype) as the FFN's input.
     """
     nseq, Lq, Hq, D = np.asarray(Q).shape
     cu = np.asarray(cu_len, dtype=np.int64)
@@ -316,7 +322,13 @@ def run_block(Q, K, V, Kb, Vb, hidden, W, cu_len, modality, r_text, r_img,
             O = attention(Q, K, V, cu, Kb, Vb)
         else:
             O = attention(Q, Kp, Vp, cu_kept, Kb, Vb)
-        conf, amax, _ = lmhead_confidence(O.reshape(nseq * Lq, Hq * D), W)
+        h = O.reshape(nseq * Lq, Hq * D)
+        if moe is not None:
+            wr, mb, wg, wu, wd, k, sc = moe
+            hs = store_as(h, store_dtype) if store_dtype else h
+            h, ids, _ = moe_ffn(hs, wr, mb, wg, wu, wd, k, sc, residual=hs)
+            res.moe_ids.append(ids)
+        conf, amax, _ = lmhead_confidence(h, W)
         conf = conf.reshape(nseq, Lq)
         amax = amax.reshape(nseq, Lq)
         steps_left = big if T is None else T - t

@@ -41,9 +41,13 @@ class SprintBlock:
 
     def __init__(self, x: synth.Inputs, device="cuda", r_text: Optional[float] = None,
                  r_img: Optional[float] = None, tau: Optional[float] = None,
-                 T: Optional[int] = "wl", alpha: Optional[float] = None, grow: int = 0):
+                 T: Optional[int] = "wl", alpha: Optional[float] = None, grow: int = 0,
+                 moe=None):
         """`grow`: rows per sequence the prefix may gain later (blocks appended
-        by a generation loop); buffers and workspaces are sized for it once."""
+        by a generation loop); buffers and workspaces are sized for it once.
+        `moe` = (w_router, bias, w_gate, w_up, w_down, top_k, route_scale) as
+        device tensors puts an MoE FFN between attention and the LM head: the
+        LM head then reads O + moe_ffn(O)."""
         wl = x.wl
         lay = x.layout
         self.wl, self.layout = wl, lay
@@ -94,6 +98,15 @@ class SprintBlock:
         self.n_acc = torch.empty(self.nseq, dtype=i32, device=dev)
         dti = sprint.BF16 if dt == "bf16" else sprint.F32
         H, Vv = wl.H, wl.vocab
+        self.moe = moe
+        if moe is not None:
+            wr, _, wg, _, _, k, _ = moe
+            E, inter = wg.shape[0], wg.shape[1]
+            self.moe_y = torch.empty((M, H), dtype=self.Q.dtype, device=dev)
+            self.moe_ids = torch.empty((M, k), dtype=i32, device=dev)
+            self.moe_gates = torch.empty((M, k), dtype=f32, device=dev)
+            self.ws_moe = torch.empty(max(sprint.moe_ffn_ws(M, H, E, k, inter), 256), dtype=u8,
+                                      device=dev)
         max_len_max = int(lens_max.max())
         max_kept_max = int(np.max(np.diff(cu_kept_max)))
 
@@ -190,11 +203,23 @@ class SprintBlock:
                 sprint.block_attend(self.Q, self.K, self.V, self.cu_len, self.max_len, self.Kb,
                                     self.Vb, O=self.O, ws=self.ws_att_full)
 
+    def moe_ffn(self):
+        """y = O + moe_ffn(O), the LM head's input when an MoE FFN is set."""
+        M = self.nseq * self.Lq
+        wr, bias, wg, wu, wd, k, sc = self.moe
+        O = self.O.view(M, self.Hq * self.D)
+        with self._t("moe_ffn"):
+            sprint.moe_ffn(O, wr, bias, wg, wu, wd, k, sc, residual=O, y=self.moe_y,
+                           expert_ids=self.moe_ids, gates=self.moe_gates, ws=self.ws_moe)
+
     def block_confidence(self):
         M = self.nseq * self.Lq
+        h = self.O.view(M, self.Hq * self.D)
+        if self.moe is not None:
+            self.moe_ffn()
+            h = self.moe_y
         with self._t("lmhead_block"):
-            sprint.lmhead_confidence(self.O.view(M, self.Hq * self.D), self.W,
-                                     conf=self.conf_blk, argmax=self.argmax_blk,
+            sprint.lmhead_confidence(h, self.W, conf=self.conf_blk, argmax=self.argmax_blk,
                                      ws=self.ws_lm_blk)
 
     def unmask(self, t: int):

@@ -88,3 +88,33 @@ def test_moe_bitwise_reproducible():
     b = sprint.moe_ffn(*args)
     torch.cuda.synchronize()
     assert all(torch.equal(p, q) for p, q in zip(a, b))
+
+
+def test_block_with_moe_between_attention_and_lm_head():
+    from sparse_prefix_kv_amd.block import SprintBlock
+    wl = synth.WORKLOADS["tiny"]
+    x = synth.make_inputs(wl, 0)
+    lay = x.layout
+    E, K, inter = 16, 4, 256
+    wr, bias, wg, wu, wd = synth.make_moe_weights(wl.H, E, inter, "f32", 3)
+    # W_down scaled up so that the experts visibly move the LM head's input
+    wd = wd * np.float32(8.0)
+    dev_moe = tuple(torch.from_numpy(a).to(DEV) for a in (wr, bias, wg, wu, wd)) + (K, 2.5)
+    blk = SprintBlock(x, DEV, moe=dev_moe)
+    blk.reset()
+    blk.pruning_pass()
+    torch.cuda.synchronize()
+    c0, ids0 = blk.conf_blk.cpu().numpy(), blk.moe_ids.cpu().numpy()
+    blk.pruned_step(1)
+    torch.cuda.synchronize()
+    c1, ids1 = blk.conf_blk.cpu().numpy(), blk.moe_ids.cpu().numpy()
+    res = oracle.run_block(x.Q, x.K, x.V, x.Kb, x.Vb, x.hidden, x.W, lay.cu_len, lay.modality,
+                           wl.r_text, wl.r_img, np.float32(wl.tau), wl.T, 1,
+                           moe=(wr, bias, wg, wu, wd, K, 2.5), store_dtype="f32")
+    same_kept = np.array_equal(blk.kept_idx.cpu().numpy(), res.kept_idx)
+    for t, (c, ids) in enumerate(((c0, ids0), (c1, ids1))):
+        if t == 1 and not same_kept:
+            break
+        agree = np.all(ids == res.moe_ids[t], axis=1)
+        assert agree.sum() >= len(agree) - 1
+        np.testing.assert_allclose(c[agree], res.confs[t][0][agree], rtol=1e-4)

@@ -684,3 +684,25 @@ def test_moe_expert_permutation_and_linearity():
     # the residual adds
     yr, _, _ = oracle.moe_ffn(x, wr, b, wg, wu, wd, 2, residual=x[:, :16])
     np.testing.assert_allclose(yr, y + x, rtol=1e-12)
+
+
+def test_block_with_moe_of_zero_down_is_the_plain_block():
+    # W_down = 0 makes the MoE contribute nothing: y = O, so the block's
+    # confidences and tokens are those without it; a non-zero MoE moves them
+    wl, x = _tiny_inputs(seed=5)
+    lay = x.layout
+    H = wl.H
+    wr, b, wg, wu, wd = synth.make_moe_weights(H, 6, 8, "f32", 1)
+    plain = oracle.run_block(x.Q, x.K, x.V, x.Kb, x.Vb, x.hidden, x.W, lay.cu_len,
+                             lay.modality, 1.0, 0.5, 0.9, 4, 2)
+    zero = oracle.run_block(x.Q, x.K, x.V, x.Kb, x.Vb, x.hidden, x.W, lay.cu_len,
+                            lay.modality, 1.0, 0.5, 0.9, 4, 2,
+                            moe=(wr, b, wg, wu, np.zeros_like(wd), 2, 2.5))
+    for t in range(3):
+        np.testing.assert_allclose(zero.confs[t], plain.confs[t], rtol=1e-14)
+        np.testing.assert_array_equal(zero.tokens[t], plain.tokens[t])
+        assert zero.moe_ids[t].shape == (6, 2)
+    live = oracle.run_block(x.Q, x.K, x.V, x.Kb, x.Vb, x.hidden, x.W, lay.cu_len,
+                            lay.modality, 1.0, 0.5, 0.9, 4, 2,
+                            moe=(wr, b, wg, wu, 50.0 * wd, 2, 2.5))
+    assert np.max(np.abs(live.confs[0] - plain.confs[0])) > 1e-6
