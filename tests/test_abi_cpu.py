@@ -149,3 +149,45 @@ def test_append_rejects_before_hip():
     assert _call("sprint_append_rows", *a) == 1                     # NULL old with rows
     a = list(ap); a[1] = FAKE + 2
     assert _call("sprint_append_rows", *a) == 1                     # misaligned cu_old
+
+
+def test_layers_entry_points_reject_before_hip():
+    # K, n_layers, conf, cu_len, nseq, total_L, Hkv, D, dtype, alpha, ibar, score, ws, ws_bytes
+    sc = [FAKE, 4, FAKE, FAKE, 1, 4096, 4, 128, sprint.BF16, 0.5, FAKE, FAKE, FAKE, 1 << 30, None]
+    a = list(sc); a[1] = 0
+    assert _call("sprint_score_layers", *a) == 1                    # no layers
+    a = list(sc); a[7] = 96
+    assert _call("sprint_score_layers", *a) == 2                    # head dim
+    a = list(sc); a[13] = 8
+    assert _call("sprint_score_layers", *a) == 3                    # workspace
+    assert sprint.sprint_score_layers_ws(4096, 1, 4) > sprint.sprint_score_ws(4096, 1)
+    pr = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 3481, FAKE, FAKE, 4, 4, 128, sprint.BF16,
+          FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+    a = list(pr); a[10] = 0
+    assert _call("sprint_prune_kv_layers", *a) == 1                 # no layers
+    a = list(pr); a[7] = 5000
+    assert _call("sprint_prune_kv_layers", *a) == 1                 # kept > total
+    a = list(pr); a[15] = None
+    assert _call("sprint_prune_kv_layers", *a) == 1                 # NULL V_out
+
+
+def test_moe_rejects_before_hip():
+    # x, M, H, w_router, bias, E, top_k, scale, w_gate, w_up, w_down, inter, dtype,
+    # residual, y, ids, gates, ws, ws_bytes, stream
+    ok = [FAKE, 32, 2048, FAKE, FAKE, 256, 8, 2.5, FAKE, FAKE, FAKE, 512, sprint.BF16, None,
+          FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+    a = list(ok); a[6] = 257
+    assert _call("moe_ffn", *a) == 1                                # top_k > E
+    a = list(ok); a[7] = float("inf")
+    assert _call("moe_ffn", *a) == 1                                # scale not finite
+    a = list(ok); a[2] = 2304
+    assert _call("moe_ffn", *a) == 2                                # H not supported
+    a = list(ok); a[11] = 500
+    assert _call("moe_ffn", *a) == 2                                # inter not supported
+    a = list(ok); a[6] = 17
+    assert _call("moe_ffn", *a) == 2                                # top_k > 16
+    a = list(ok); a[13] = FAKE + 4
+    assert _call("moe_ffn", *a) == 1                                # misaligned residual
+    a = list(ok); a[18] = 64
+    assert _call("moe_ffn", *a) == 3                                # workspace
+    assert sprint.moe_ffn_ws(32, 2048, 256, 8, 512) >= 32 * 8 * (512 + 2048) * 4
