@@ -9,7 +9,9 @@
 // kept iff key > T, or key == T and p <= tie_cut (the first ties by position).
 //
 // Launches:
-//   1. topk_threshold_kernel  one 1024-thread block per segment;
+//   1. topk_threshold_kernel  one 1024-thread block per segment (the keys of
+//                             a sequence of up to 32768 positions read from
+//                             HBM once, into LDS);
 //   2. chunk_count_kernel     kept count of every 64-position chunk;
 //   3. compact_kernel         per chunk: prefix of earlier chunk counts in the
 //                             sequence -> output slots; writes kept_idx and
@@ -26,6 +28,7 @@ namespace sprint {
 namespace {
 
 constexpr int kSelThreads = 1024;
+constexpr int kLdsKeys = 32768;    // a sequence's keys kept in LDS (128 KB)
 constexpr int kChunk = 64;
 constexpr int kCopyThreads = 256;
 
@@ -87,7 +90,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
   const int k = keep[seg];
   __shared__ int hist[256];
   __shared__ int s_wave[kSelThreads / 64];
-  __shared__ int s_bucket, s_above, s_total, s_found;
+  __shared__ int s_bucket, s_above, s_total, s_found, s_nkeys;
+  __shared__ uint32_t s_keys[kLdsKeys];
   if (k <= 0) {
     if (threadIdx.x == 0) thr[seg] = SegThresh{0xFFFFFFFFu, -1};
     return;
@@ -95,14 +99,51 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
   uint32_t prefix = 0, pmask = 0;
   int krem = k;
   int ties = 0;
+  // A sequence of up to kLdsKeys positions has its modality's keys read from
+  // HBM once, during the first pass, into LDS (in any order: the histograms
+  // only count); the later passes read them there.  Longer sequences read
+  // the scores again in every pass.
+  const bool in_lds = e - a <= kLdsKeys;
+  if (threadIdx.x == 0) s_nkeys = 0;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     if (threadIdx.x < 256) hist[threadIdx.x] = 0;
     __syncthreads();
-    for (int64_t p = a + threadIdx.x; p < e; p += kSelThreads) {
-      if (modality[p] != mod) continue;
-      const uint32_t key = order_key(score[p]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    if (in_lds && pass > 0) {
+      const int nk = s_nkeys;
+      for (int i = threadIdx.x; i < nk; i += kSelThreads) {
+        const uint32_t key = s_keys[i];
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+      }
+    } else {
+      // eight chunks of the sequence per round, all their loads in flight
+      // before any is used
+      const int lane = threadIdx.x & 63;
+      constexpr int kU = 8;
+      for (int64_t p0 = a; p0 < e; p0 += kU * kSelThreads) {
+        uint8_t md[kU];
+        float sc[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int64_t p = p0 + u * kSelThreads + threadIdx.x;
+          md[u] = p < e ? modality[p] : static_cast<uint8_t>(mod ^ 1);
+          sc[u] = p < e ? score[p] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const bool mine = md[u] == mod;
+          const uint32_t key = mine ? order_key(sc[u]) : 0u;
+          if (mine && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+          if (in_lds) {
+            // one LDS slot reservation per wave
+            const uint64_t bal = __ballot(mine);
+            int slot0 = 0;
+            if (lane == 0 && bal) slot0 = atomicAdd(&s_nkeys, __popcll(bal));
+            slot0 = __shfl(slot0, 0, 64);
+            if (mine) s_keys[slot0 + __popcll(bal & ((1ull << lane) - 1ull))] = key;
+          }
+        }
+      }
     }
     __syncthreads();
     // Suffix sums over the 256 digits (threads 0..255 = waves 0..3).  Every
