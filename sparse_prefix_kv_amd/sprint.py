@@ -121,6 +121,29 @@ def _dev(t: torch.Tensor, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _arg(t, name: str, dtype=None, numel: Optional[int] = None, shape=None):
+    """Check a tensor argument's dtype and size (or exact shape), so that a
+    wrong buffer raises here instead of being read or written out of range by
+    a kernel.  Device and contiguity are checked afterwards, for all
+    arguments together (_gpu)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
+    return t
+
+
+def _gpu(**tensors):
+    """Device and contiguity of every tensor argument given (None skipped)."""
+    for name, t in tensors.items():
+        if t is not None:
+            _dev(t, name)
+
+
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
@@ -175,18 +198,21 @@ def block_attend_ws(nseq, Lq, Hq, Hkv, D, max_kv, has_block) -> int:
 def lmhead_confidence(hidden: torch.Tensor, W: torch.Tensor, conf=None, argmax=None, lse=None,
                       want_lse: bool = False, ws=None, stream=None):
     """Top-1 softmax confidence and argmax of hidden @ W^T.  hidden [M, H], W [V, H]."""
-    _dev(hidden, "hidden")
-    _dev(W, "W")
     M, H = hidden.shape
     V = W.shape[0]
-    if W.shape[1] != H or W.dtype != hidden.dtype:
-        raise ValueError("hidden/W shape or dtype mismatch")
     dt = _dt(hidden)
+    _arg(hidden, "hidden")
+    _arg(W, "W", hidden.dtype, shape=(V, H))
     dev = hidden.device
-    conf = torch.empty(M, dtype=torch.float32, device=dev) if conf is None else conf
-    argmax = torch.empty(M, dtype=torch.int32, device=dev) if argmax is None else argmax
+    f32, i32 = torch.float32, torch.int32
+    conf = torch.empty(M, dtype=f32, device=dev) if conf is None else _arg(conf, "conf", f32, M)
+    argmax = (torch.empty(M, dtype=i32, device=dev) if argmax is None
+              else _arg(argmax, "argmax", i32, M))
     if want_lse and lse is None:
-        lse = torch.empty(M, dtype=torch.float32, device=dev)
+        lse = torch.empty(M, dtype=f32, device=dev)
+    if lse is not None:
+        _arg(lse, "lse", f32, M)
+    _gpu(hidden=hidden, W=W, conf=conf, argmax=argmax, lse=lse)
     ws = _ws(lmhead_confidence_ws(M, H, V, dt), dev, ws)
     _check("lmhead_confidence", lib().lmhead_confidence(
         _ptr(hidden), M, H, _ptr(W), V, dt, _ptr(conf), _ptr(argmax), _ptr(lse), _ptr(ws),
@@ -197,12 +223,18 @@ def lmhead_confidence(hidden: torch.Tensor, W: torch.Tensor, conf=None, argmax=N
 def sprint_score(K: torch.Tensor, conf: torch.Tensor, cu_len: torch.Tensor, alpha: float = 0.5,
                  ibar=None, score=None, ws=None, stream=None):
     """Mean-normalised key norm and composite score.  K [total_L, Hkv, D]."""
-    _dev(K, "K")
     total_L, Hkv, D = K.shape
+    _dt(K)
+    _arg(K, "K")
+    f32 = torch.float32
+    _arg(conf, "conf", f32, total_L)
+    _arg(cu_len, "cu_len", torch.int32)
     nseq = cu_len.numel() - 1
     dev = K.device
-    ibar = torch.empty(total_L, dtype=torch.float32, device=dev) if ibar is None else ibar
-    score = torch.empty(total_L, dtype=torch.float32, device=dev) if score is None else score
+    ibar = torch.empty(total_L, dtype=f32, device=dev) if ibar is None else _arg(ibar, "ibar", f32, total_L)
+    score = (torch.empty(total_L, dtype=f32, device=dev) if score is None
+             else _arg(score, "score", f32, total_L))
+    _gpu(K=K, conf=conf, cu_len=cu_len, ibar=ibar, score=score)
     ws = _ws(sprint_score_ws(total_L, nseq), dev, ws)
     _check("sprint_score", lib().sprint_score(
         _ptr(K), _ptr(conf), _ptr(cu_len), nseq, total_L, Hkv, D, _dt(K), float(alpha),
@@ -213,17 +245,32 @@ def sprint_score(K: torch.Tensor, conf: torch.Tensor, cu_len: torch.Tensor, alph
 def sprint_prune_kv(score, modality, cu_len, keep, cu_kept, total_kept: int, K, V,
                     K_out=None, V_out=None, kept_idx=None, ws=None, stream=None):
     """Per-modality top-k selection and compaction into a contiguous pruned cache."""
-    _dev(K, "K")
-    _dev(V, "V")
     total_L, Hkv, D = K.shape
+    _dt(K)
+    _arg(K, "K")
+    _arg(V, "V", K.dtype, shape=K.shape)
+    i32 = torch.int32
+    _arg(cu_len, "cu_len", i32)
     nseq = cu_len.numel() - 1
+    _arg(score, "score", torch.float32, total_L)
+    _arg(modality, "modality", torch.uint8, total_L)
+    _arg(keep, "keep", i32, 2 * nseq)
+    _arg(cu_kept, "cu_kept", i32, nseq + 1)
+    if not 0 <= total_kept <= total_L:
+        raise ValueError("total_kept must lie in [0, total_L]")
     dev = K.device
     if K_out is None:
         K_out = torch.empty((max(total_kept, 1), Hkv, D), dtype=K.dtype, device=dev)[:total_kept]
     if V_out is None:
         V_out = torch.empty((max(total_kept, 1), Hkv, D), dtype=V.dtype, device=dev)[:total_kept]
     if kept_idx is None:
-        kept_idx = torch.empty(max(total_kept, 1), dtype=torch.int32, device=dev)[:total_kept]
+        kept_idx = torch.empty(max(total_kept, 1), dtype=i32, device=dev)[:total_kept]
+    if total_kept:
+        _arg(K_out, "K_out", K.dtype, total_kept * Hkv * D)
+        _arg(V_out, "V_out", K.dtype, total_kept * Hkv * D)
+        _arg(kept_idx, "kept_idx", i32, total_kept)
+    _gpu(score=score, modality=modality, cu_len=cu_len, keep=keep, cu_kept=cu_kept, K=K, V=V,
+         K_out=K_out, V_out=V_out, kept_idx=kept_idx)
     ws = _ws(sprint_prune_kv_ws(total_L, nseq), dev, ws)
     _check("sprint_prune_kv", lib().sprint_prune_kv(
         _ptr(score), _ptr(modality), _ptr(cu_len), _ptr(keep), _ptr(cu_kept), nseq, total_L,
@@ -235,14 +282,23 @@ def sprint_prune_kv(score, modality, cu_len, keep, cu_kept, total_kept: int, K, 
 def block_attend(Q, Kp, Vp, cu_kv, max_kv: int, Kb=None, Vb=None, scale: Optional[float] = None,
                  O=None, ws=None, stream=None):
     """softmax(Q K^T * scale) V over [prefix ; block] with GQA.  Q [nseq, Lq, Hq, D]."""
-    _dev(Q, "Q")
     nseq, Lq, Hq, D = Q.shape
-    Hkv = Kp.shape[1]
-    total_kv = Kp.shape[0]
+    _dt(Q)
+    _arg(Q, "Q")
+    total_kv, Hkv = Kp.shape[0], Kp.shape[1]
+    _arg(Kp, "Kp", Q.dtype, shape=(total_kv, Hkv, D))
+    _arg(Vp, "Vp", Q.dtype, shape=(total_kv, Hkv, D))
+    _arg(cu_kv, "cu_kv", torch.int32, shape=(nseq + 1,))
+    if (Kb is None) != (Vb is None):
+        raise ValueError("Kb and Vb go together")
+    if Kb is not None:
+        _arg(Kb, "Kb", Q.dtype, shape=(nseq, Lq, Hkv, D))
+        _arg(Vb, "Vb", Q.dtype, shape=(nseq, Lq, Hkv, D))
     if scale is None:
         scale = D ** -0.5
     dev = Q.device
-    O = torch.empty_like(Q) if O is None else O
+    O = torch.empty_like(Q) if O is None else _arg(O, "O", Q.dtype, Q.numel())
+    _gpu(Q=Q, Kp=Kp, Vp=Vp, cu_kv=cu_kv, Kb=Kb, Vb=Vb, O=O)
     ws = _ws(block_attend_ws(nseq, Lq, Hq, Hkv, D, max_kv, Kb is not None), dev, ws)
     _check("block_attend", lib().block_attend(
         _ptr(Q), nseq, Lq, Hq, _ptr(Kp) if total_kv else None, _ptr(Vp) if total_kv else None,
@@ -255,8 +311,14 @@ def unmask_select(conf, argmax, masked, tokens, tau: float, steps_left: int, n_a
                   stream=None):
     """One confidence-adaptive unmasking step; updates masked and tokens in place."""
     nseq, Lq = conf.shape
+    _arg(conf, "conf", torch.float32)
+    _arg(argmax, "argmax", torch.int32, shape=(nseq, Lq))
+    _arg(masked, "masked", torch.uint8, shape=(nseq, Lq))
+    _arg(tokens, "tokens", torch.int32, shape=(nseq, Lq))
     if n_accepted is None:
         n_accepted = torch.empty(nseq, dtype=torch.int32, device=conf.device)
+    _arg(n_accepted, "n_accepted", torch.int32, nseq)
+    _gpu(conf=conf, argmax=argmax, masked=masked, tokens=tokens, n_accepted=n_accepted)
     _check("unmask_select", lib().unmask_select(
         _ptr(conf), _ptr(argmax), nseq, Lq, float(tau), int(steps_left), _ptr(masked),
         _ptr(tokens), _ptr(n_accepted), _stream(stream)))
@@ -269,10 +331,9 @@ def sprint_append_rows(old, cu_old, blk, out=None, cu_out=None, stream=None):
     old [total_old, ...] packed by cu_old [nseq+1]; blk [nseq, n_blk, ...] or
     [nseq*n_blk, ...] with the same row shape and dtype.  Returns (out, cu_out).
     """
-    _dev(old, "old")
-    _dev(blk, "blk")
-    if old.dtype != blk.dtype:
-        raise TypeError("old and blk must share a dtype")
+    _arg(old, "old")
+    _arg(blk, "blk", old.dtype)
+    _arg(cu_old, "cu_old", torch.int32)
     nseq = cu_old.numel() - 1
     row_shape = tuple(old.shape[1:])
     row_elems = math.prod(row_shape)
@@ -283,12 +344,13 @@ def sprint_append_rows(old, cu_old, blk, out=None, cu_out=None, stream=None):
     row_bytes = old.element_size() * row_elems
     total = total_old + nseq * n_blk
     dev = old.device
-    out = torch.empty((total, *row_shape), dtype=old.dtype, device=dev) if out is None else out
-    _dev(out, "out")
-    if out.shape[0] < total:
-        raise ValueError("out has fewer rows than old + block rows")
+    if out is None:
+        out = torch.empty((total, *row_shape), dtype=old.dtype, device=dev)
+    _arg(out, "out", old.dtype, total * row_elems)
     if cu_out is None:
         cu_out = torch.empty(nseq + 1, dtype=torch.int32, device=dev)
+    _arg(cu_out, "cu_out", torch.int32, nseq + 1)
+    _gpu(old=old, blk=blk, cu_old=cu_old, out=out, cu_out=cu_out)
     _check("sprint_append_rows", lib().sprint_append_rows(
         _ptr(old) if total_old else None, _ptr(cu_old), nseq, total_old,
         _ptr(blk) if n_blk else None, n_blk, row_bytes, _ptr(out) if total else None,
@@ -303,12 +365,18 @@ def sprint_score_layers_ws(total_L: int, nseq: int, n_layers: int) -> int:
 def sprint_score_layers(K, conf, cu_len, alpha: float = 0.5, ibar=None, score=None, ws=None,
                         stream=None):
     """Layer-mean key-norm importance and composite score.  K [n_layers, total_L, Hkv, D]."""
-    _dev(K, "K")
     n_layers, total_L, Hkv, D = K.shape
+    _dt(K)
+    _arg(K, "K")
+    f32 = torch.float32
+    _arg(conf, "conf", f32, total_L)
+    _arg(cu_len, "cu_len", torch.int32)
     nseq = cu_len.numel() - 1
     dev = K.device
-    ibar = torch.empty(total_L, dtype=torch.float32, device=dev) if ibar is None else ibar
-    score = torch.empty(total_L, dtype=torch.float32, device=dev) if score is None else score
+    ibar = torch.empty(total_L, dtype=f32, device=dev) if ibar is None else _arg(ibar, "ibar", f32, total_L)
+    score = (torch.empty(total_L, dtype=f32, device=dev) if score is None
+             else _arg(score, "score", f32, total_L))
+    _gpu(K=K, conf=conf, cu_len=cu_len, ibar=ibar, score=score)
     ws = _ws(sprint_score_layers_ws(total_L, nseq, n_layers), dev, ws)
     _check("sprint_score_layers", lib().sprint_score_layers(
         _ptr(K), n_layers, _ptr(conf), _ptr(cu_len), nseq, total_L, Hkv, D, _dt(K),
@@ -319,21 +387,33 @@ def sprint_score_layers(K, conf, cu_len, alpha: float = 0.5, ibar=None, score=No
 def sprint_prune_kv_layers(score, modality, cu_len, keep, cu_kept, total_kept: int, K, V,
                            K_out=None, V_out=None, kept_idx=None, ws=None, stream=None):
     """One kept set compacted in every layer's cache.  K, V [n_layers, total_L, Hkv, D]."""
-    _dev(K, "K")
-    _dev(V, "V")
     n_layers, total_L, Hkv, D = K.shape
+    _dt(K)
+    _arg(K, "K")
+    _arg(V, "V", K.dtype, shape=K.shape)
+    i32 = torch.int32
+    _arg(cu_len, "cu_len", i32)
     nseq = cu_len.numel() - 1
+    _arg(score, "score", torch.float32, total_L)
+    _arg(modality, "modality", torch.uint8, total_L)
+    _arg(keep, "keep", i32, 2 * nseq)
+    _arg(cu_kept, "cu_kept", i32, nseq + 1)
+    if not 0 <= total_kept <= total_L:
+        raise ValueError("total_kept must lie in [0, total_L]")
     dev = K.device
     shape = (n_layers, max(total_kept, 1), Hkv, D)
     if K_out is None:
         K_out = torch.empty(shape, dtype=K.dtype, device=dev)[:, :total_kept]
     if V_out is None:
         V_out = torch.empty(shape, dtype=V.dtype, device=dev)[:, :total_kept]
-    for t, name in ((K_out, "K_out"), (V_out, "V_out")):
-        if total_kept and not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous [n_layers, total_kept, Hkv, D]")
     if kept_idx is None:
-        kept_idx = torch.empty(max(total_kept, 1), dtype=torch.int32, device=dev)[:total_kept]
+        kept_idx = torch.empty(max(total_kept, 1), dtype=i32, device=dev)[:total_kept]
+    if total_kept:
+        _arg(K_out, "K_out", K.dtype, shape=(n_layers, total_kept, Hkv, D))
+        _arg(V_out, "V_out", K.dtype, shape=(n_layers, total_kept, Hkv, D))
+        _arg(kept_idx, "kept_idx", i32, total_kept)
+    _gpu(score=score, modality=modality, cu_len=cu_len, keep=keep, cu_kept=cu_kept, K=K, V=V,
+         K_out=K_out, V_out=V_out, kept_idx=kept_idx)
     ws = _ws(sprint_prune_kv_ws(total_L, nseq), dev, ws)
     _check("sprint_prune_kv_layers", lib().sprint_prune_kv_layers(
         _ptr(score), _ptr(modality), _ptr(cu_len), _ptr(keep), _ptr(cu_kept), nseq, total_L,
@@ -351,17 +431,27 @@ def moe_ffn(x, w_router, bias, w_gate, w_up, w_down, top_k: int, route_scale: fl
     """MoE FFN with sigmoid routing, bias-steered top-k and SwiGLU experts.
     x [M, H]; w_router [E, H]; bias [E] float32; w_gate, w_up [E, I, H];
     w_down [E, H, I].  Returns (y, expert_ids, gates)."""
-    for t, n in ((x, "x"), (w_router, "w_router"), (bias, "bias"), (w_gate, "w_gate"),
-                 (w_up, "w_up"), (w_down, "w_down")):
-        _dev(t, n)
     M, H = x.shape
     E, inter = w_gate.shape[0], w_gate.shape[1]
+    _dt(x)
+    _arg(x, "x")
+    _arg(w_router, "w_router", x.dtype, shape=(E, H))
+    _arg(bias, "bias", torch.float32, shape=(E,))
+    _arg(w_gate, "w_gate", x.dtype, shape=(E, inter, H))
+    _arg(w_up, "w_up", x.dtype, shape=(E, inter, H))
+    _arg(w_down, "w_down", x.dtype, shape=(E, H, inter))
+    if residual is not None:
+        _arg(residual, "residual", x.dtype, shape=(M, H))
     dev = x.device
-    y = torch.empty_like(x) if y is None else y
+    y = torch.empty_like(x) if y is None else _arg(y, "y", x.dtype, shape=(M, H))
     if expert_ids is None:
         expert_ids = torch.empty((M, top_k), dtype=torch.int32, device=dev)
     if gates is None:
         gates = torch.empty((M, top_k), dtype=torch.float32, device=dev)
+    _arg(expert_ids, "expert_ids", torch.int32, M * top_k)
+    _arg(gates, "gates", torch.float32, M * top_k)
+    _gpu(x=x, w_router=w_router, bias=bias, w_gate=w_gate, w_up=w_up, w_down=w_down,
+         residual=residual, y=y, expert_ids=expert_ids, gates=gates)
     ws = _ws(moe_ffn_ws(M, H, E, top_k, inter), dev, ws)
     _check("moe_ffn", lib().moe_ffn(
         _ptr(x), M, H, _ptr(w_router), _ptr(bias), E, top_k, float(route_scale), _ptr(w_gate),

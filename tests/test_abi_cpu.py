@@ -191,3 +191,38 @@ def test_moe_rejects_before_hip():
     a = list(ok); a[18] = 64
     assert _call("moe_ffn", *a) == 3                                # workspace
     assert sprint.moe_ffn_ws(32, 2048, 256, 8, 512) >= 32 * 8 * (512 + 2048) * 4
+
+
+def test_binding_checks_dtypes_and_sizes_before_the_device():
+    # CPU tensors with a wrong dtype or size are rejected before the device
+    # check, so a mismatched buffer never reaches a kernel
+    import torch
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    Q = torch.zeros(1, 4, 4, 64, dtype=bf)
+    K = torch.zeros(10, 2, 64, dtype=f32)
+    with pytest.raises(TypeError):
+        sprint.block_attend(Q, K, K, torch.zeros(2, dtype=i32), 10)
+    X = torch.zeros(8, 64, dtype=bf)
+    with pytest.raises(ValueError):
+        sprint.lmhead_confidence(X, torch.zeros(16, 32, dtype=bf))          # H mismatch
+    with pytest.raises(ValueError):
+        sprint.lmhead_confidence(X, torch.zeros(16, 64, dtype=bf),
+                                 conf=torch.zeros(4, dtype=f32))             # conf too small
+    conf = torch.zeros(2, 8, dtype=f32)
+    with pytest.raises(TypeError):
+        sprint.unmask_select(conf, torch.zeros(2, 8, dtype=torch.int64),
+                             torch.zeros(2, 8, dtype=torch.uint8), torch.zeros(2, 8, dtype=i32),
+                             0.9, 4)
+    Kl = torch.zeros(2, 10, 2, 64, dtype=bf)
+    with pytest.raises(ValueError):
+        sprint.sprint_prune_kv_layers(torch.zeros(10, dtype=f32), torch.zeros(10, dtype=torch.uint8),
+                                      torch.zeros(2, dtype=i32), torch.zeros(2, dtype=i32),
+                                      torch.zeros(2, dtype=i32), 11, Kl, Kl)  # kept > total
+    with pytest.raises(TypeError):
+        sprint.moe_ffn(X, torch.zeros(4, 64, dtype=bf), torch.zeros(4, dtype=bf),  # bias dtype
+                       torch.zeros(4, 32, 64, dtype=bf), torch.zeros(4, 32, 64, dtype=bf),
+                       torch.zeros(4, 64, 32, dtype=bf), 2)
+    with pytest.raises(ValueError):
+        sprint.sprint_append_rows(torch.zeros(5, 3, dtype=f32), torch.tensor([0, 5], dtype=i32),
+                                  torch.zeros(1, 2, 3, dtype=f32),
+                                  out=torch.zeros(6, 3, dtype=f32))          # out too small
