@@ -209,10 +209,6 @@ template <>
 __device__ __forceinline__ half_t out_cvt<half_t>(float x) {
   return static_cast<half_t>(x);
 }
-template <>
-__device__ __forceinline__ float out_cvt<float>(float x) {
-  return x;
-}
 
 template <typename E, int D>
 struct RowGeo {
