@@ -556,6 +556,12 @@ def main():
                "alg_bytes": w["bytes"], "alg_flops": w["flops"], "bound": w["bound"],
                "gbs": round(w["bytes"] / us / 1e3, 1),
                "tflops": round(w["flops"] / us / 1e6, 2)}
+        # fraction of the roofline the call is bound by
+        if w["bound"] == "mfma":
+            ent["frac"] = round(w["flops"] / us / 1e6 /
+                                (BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS), 4)
+        else:
+            ent["frac"] = round(w["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4)
         if name in calls_cold:
             cu = calls_cold[name]["median_us"]
             ent["cold_us"] = round(cu, 3)
