@@ -17,6 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsprint.so")
+C_CHECK = os.path.join(ROOT, "tests", "c_abi_check")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = os.environ.get("SPRINT_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -63,7 +65,24 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_c_check(verbose)
     return LIB
+
+
+def build_c_check(verbose: bool = True) -> str:
+    """Link tests/c_abi_check.cpp, a host program that calls the library
+    through include/sprint.h alone, against libsprint.so (no Python, no torch)."""
+    src = os.path.join(ROOT, "tests", "c_abi_check.cpp")
+    cmd = [shutil.which("g++") or "g++", "-O2", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROCM, "include"), src,
+           "-o", C_CHECK, "-L", PKG, "-lsprint", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../sparse_prefix_kv_amd", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"c_abi_check build failed:\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {C_CHECK}")
+    return C_CHECK
 
 
 if __name__ == "__main__":

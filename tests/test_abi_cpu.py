@@ -226,3 +226,15 @@ def test_binding_checks_dtypes_and_sizes_before_the_device():
         sprint.sprint_append_rows(torch.zeros(5, 3, dtype=f32), torch.tensor([0, 5], dtype=i32),
                                   torch.zeros(1, 2, 3, dtype=f32),
                                   out=torch.zeros(6, 3, dtype=f32))          # out too small
+
+
+def test_c_program_links_and_runs_host_checks():
+    """tests/c_abi_check.cpp includes only include/sprint.h and the HIP
+    runtime header: it compiling, linking and passing its host-side checks
+    shows the boundary is usable from C++ without Python."""
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi_check")
+    assert os.path.exists(exe), "tests/c_abi_check is missing: run python -m sparse_prefix_kv_amd.build"
+    r = subprocess.run([exe, "--host-only"], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all checks passed" in r.stdout
