@@ -14,11 +14,12 @@ Printed: one JSON line.  `value` is denoising block-steps per second
 of the whole block replayed as one HIP graph (after checking that a replay
 leaves exactly the state an eager run leaves) and the same blocks launched
 eagerly from the host; `timing` names which.  The same line carries both
-rates, the
-full-retention baseline, per-call GPU times (each call captured 20 times
-back to back in a graph, HIP events around the replay on the stream it runs
-on; and cache-flushed single calls), the roofline of the dominant call and
-the CPU oracle timed on the host.
+rates, the full-retention baseline, per-call GPU times (each call captured
+20 times back to back in a graph, HIP events around 11 replays on the stream
+it runs on: median, 10th and 90th percentile of the per-launch means; and
+cache-flushed single calls), the roofline of the dominant call, torch.mm on
+the prefix GEMM's shape as a library yardstick, and the CPU oracle timed on
+the host.
 """
 from __future__ import annotations
 
@@ -92,8 +93,15 @@ class EventTimer:
         out = {}
         for name, s, e in self.records:
             out.setdefault(name, []).append(s.elapsed_time(e) * 1e3)   # us
-        return {k: {"n": len(v), "mean_us": sum(v) / len(v), "min_us": min(v),
-                    "median_us": sorted(v)[len(v) // 2]} for k, v in out.items()}
+        return {k: dict(n=len(v), mean_us=sum(v) / len(v), min_us=min(v), **pctl(v))
+                for k, v in out.items()}
+
+
+def pctl(v):
+    """Median, 10th and 90th percentiles (nearest rank) of a list of times."""
+    v = sorted(v)
+    n = len(v)
+    return {"median_us": v[n // 2], "p10_us": v[(n - 1) // 10], "p90_us": v[n - 1 - (n - 1) // 10]}
 
 
 def work_model(blk):
@@ -515,13 +523,46 @@ def main():
     for name, fn in call_fns.items():
         blk.reset()
         g = capture(lambda: [fn() for _ in range(reps)])
-        ts = sorted(replay_rate(g, 3)[1] / reps for _ in range(5))
-        calls[name] = {"us": ts[len(ts) // 2] * 1e6, "min_us": ts[0] * 1e6}
+        # 11 samples, each the mean launch time over one replay of 20 launches
+        ts = [replay_rate(g, 1)[1] / reps * 1e6 for _ in range(11)]
+        pc = pctl(ts)
+        calls[name] = {"us": pc["median_us"], "min_us": min(ts), "p10_us": pc["p10_us"],
+                       "p90_us": pc["p90_us"]}
         del g
     launches = {"lmhead_prefix": 1, "score": 1, "prune": 1, "attend_full": 1,
                 "attend_pruned": n_steps, "lmhead_block": n_steps + 1, "unmask": n_steps + 1}
     launches_full = {"attend_full": n_steps + 1, "lmhead_block": n_steps + 1,
                      "unmask": n_steps + 1}
+
+    # ---------------------------------------------------------------- library yardstick
+    # The prefix GEMM's shape through torch.mm (hipBLASLt), for comparison
+    # only: logits^T = W . hidden^T, written out in bf16, which the fused
+    # kernel never does.  Eager launches, HIP events around 10 at a time.
+    yardstick = None
+    if wl.dtype == "bf16":
+        hT = blk.hidden.t().contiguous()
+        lg = torch.empty((wl.vocab, lay.total_L), dtype=blk.W.dtype, device="cuda")
+        for _ in range(3):
+            torch.mm(blk.W, hT, out=lg)
+        ys = []
+        for _ in range(5):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                torch.mm(blk.W, hT, out=lg)
+            e1.record()
+            torch.cuda.synchronize()
+            ys.append(e0.elapsed_time(e1) * 1e3 / 10)
+        yus = pctl(ys)["median_us"]
+        yfl = 2 * lay.total_L * wl.H * wl.vocab
+        yardstick = {"op": "torch.mm(W [V,H], hidden^T [H,L]) -> logits^T [V,L], bf16",
+                     "us": round(yus, 3), "tflops": round(yfl / yus / 1e6, 2),
+                     "frac": round(yfl / yus / 1e6 / BF16_PEAK_TFLOPS, 4),
+                     "note": "a library GEMM that writes the logits; not part of the path"}
+        log(f"[bench] torch.mm on the prefix GEMM's shape: {yus:.1f} us "
+            f"({yfl / yus / 1e6:.0f} TFLOP/s)")
+        del hT, lg
 
     # ---------------------------------------------------------------- cold per-call timings
     # cold: before each call, read a 512 MB buffer (twice the Infinity Cache)
@@ -554,6 +595,7 @@ def main():
         ent = {"us": round(us, 3), "launches_per_block": launches[name],
                "us_per_block": round(us * launches[name], 2),
                "alg_bytes": w["bytes"], "alg_flops": w["flops"], "bound": w["bound"],
+               "p10_us": round(st["p10_us"], 3), "p90_us": round(st["p90_us"], 3),
                "gbs": round(w["bytes"] / us / 1e3, 1),
                "tflops": round(w["flops"] / us / 1e6, 2)}
         # fraction of the roofline the call is bound by
@@ -565,6 +607,8 @@ def main():
         if name in calls_cold:
             cu = calls_cold[name]["median_us"]
             ent["cold_us"] = round(cu, 3)
+            ent["cold_p10_us"] = round(calls_cold[name]["p10_us"], 3)
+            ent["cold_p90_us"] = round(calls_cold[name]["p90_us"], 3)
             ent["cold_gbs"] = round(w["bytes"] / cu / 1e3, 1)
         kernels[name] = ent
     dw = work[dominant]
@@ -663,6 +707,7 @@ def main():
         "moe": moe,
         "roofline": roofline,
         "kernels": kernels,
+        "yardstick": yardstick,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
