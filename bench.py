@@ -191,6 +191,70 @@ def profile_call(args, blk, n_steps, torch):
     print(json.dumps({"profile_call": what, "launches": args.steps}), flush=True)
 
 
+def capture_graph(torch, fn):
+    """Warm fn up on a side stream, then capture it as a HIP graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def replay_median(torch, g, reps):
+    """Median GPU time (s) of one replay, HIP events around each of reps replays."""
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    return sorted(ts)[len(ts) // 2]
+
+
+def eager_median(torch, fn, reps):
+    """Median host wall time (s) of fn launched eagerly, synchronised."""
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[len(ts) // 2]
+
+
+def graph_and_eager(torch, run, state, poison, reps):
+    """(graph s, eager s, replay matches eager): run timed eagerly and as a
+    graph replay, after checking that a replay, from poisoned outputs,
+    leaves exactly the state an eager run leaves."""
+    t_e = eager_median(torch, run, reps)
+    run()
+    torch.cuda.synchronize()
+    ref = state()
+    g = capture_graph(torch, run)
+    poison()
+    g.replay()
+    torch.cuda.synchronize()
+    ok = all(torch.equal(u, v) for u, v in zip(ref, state()))
+    t_g = replay_median(torch, g, reps)
+    # the last of the timed replays must leave the same state too
+    ok = ok and all(torch.equal(u, v) for u, v in zip(ref, state()))
+    del g
+    return t_g, t_e, ok
+
+
 def measure_generation(args, x, wl, n_steps, torch, reps=5):
     """B consecutive blocks over a growing prefix (each block's rows join the
     prefix before the next pass), SPRINT vs the unpruned baseline, plus the
@@ -200,18 +264,18 @@ def measure_generation(args, x, wl, n_steps, torch, reps=5):
     gen = SprintGeneration(x, B, "cuda")
     nseq, Lq = gen.nseq, gen.Lq
 
-    def timed(full):
-        gen.run(n_steps, full=full)
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
-            t0 = time.perf_counter()
-            gen.run(n_steps, full=full)
-            torch.cuda.synchronize()
-            ts.append(time.perf_counter() - t0)
-        return sorted(ts)[len(ts) // 2]
-    t_sp = timed(False)
-    t_full = timed(True)
+    def timed(g_obj, full):
+        b = g_obj.blk
+
+        def state():
+            return [g_obj.tokens_out.clone(), b.O.clone(), b.kept_idx.clone()]
+
+        def poison():
+            g_obj.tokens_out.fill_(-7)
+            b.O.zero_()
+        return graph_and_eager(torch, lambda: g_obj.run(n_steps, full=full), state, poison, reps)
+    t_sp, t_sp_e, ok_sp = timed(gen, False)
+    t_full, t_full_e, ok_full = timed(gen, True)
     # steps until every position of the block is accepted (host-checked here,
     # outside the timed runs)
     blk = gen.blk
@@ -230,13 +294,7 @@ def measure_generation(args, x, wl, n_steps, torch, reps=5):
         gen.finish_block(b)
     # the same generation recomputing every prefix confidence at each pass
     gen_re = SprintGeneration(x, B, "cuda", carry_conf=False)
-    gen_re.run(n_steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        gen_re.run(n_steps)
-    torch.cuda.synchronize()
-    t_re = (time.perf_counter() - t0) / reps
+    t_re, t_re_e, ok_re = timed(gen_re, False)
     del gen_re
     torch.cuda.synchronize()
     T = n_steps + 1
@@ -247,13 +305,18 @@ def measure_generation(args, x, wl, n_steps, torch, reps=5):
     return {
         "blocks": B, "steps_budget_T": T,
         "prefix_first": int(x.layout.total_L), "prefix_last": prefix_last,
+        "timing": "HIP graph replay of the whole generation (eager_ms: host-launched)",
+        "replay_matches_eager": bool(ok_sp and ok_full and ok_re),
         "sprint": {"ms": round(t_sp * 1e3, 3), "blocks_per_s": round(B / t_sp, 2),
                    "tokens_per_s": round(B * Lq * nseq / t_sp, 1),
-                   "block_steps_per_s": round(B * T * nseq / t_sp, 1)},
+                   "block_steps_per_s": round(B * T * nseq / t_sp, 1),
+                   "eager_ms": round(t_sp_e * 1e3, 3)},
         "full_prefix": {"ms": round(t_full * 1e3, 3), "blocks_per_s": round(B / t_full, 2),
-                        "tokens_per_s": round(B * Lq * nseq / t_full, 1)},
+                        "tokens_per_s": round(B * Lq * nseq / t_full, 1),
+                        "eager_ms": round(t_full_e * 1e3, 3)},
         "sprint_recomputed_conf": {"ms": round(t_re * 1e3, 3),
                                    "blocks_per_s": round(B / t_re, 2),
+                                   "eager_ms": round(t_re_e * 1e3, 3),
                                    "note": "every pass runs the LM head over the whole prefix"},
         "speedup": round(t_full / t_sp, 4),
         "adaptive_steps_per_block": finished,
@@ -270,40 +333,55 @@ def measure_generation(args, x, wl, n_steps, torch, reps=5):
 def measure_layers(args, x, n_steps, torch, reps=5):
     """A block of an n-layer stand-in (every layer its own prefix cache and
     block inputs; LM head on the last layer): one kept set shared by all
-    layers, a set per layer, and the unpruned baseline."""
+    layers, a set per layer, and the unpruned baseline.  Each is timed as a
+    HIP graph replay (GPU time: at 16 attention launches per step the host
+    binding, not the GPU, would set an eager rate) after checking that a
+    replay leaves what an eager run leaves, and also eagerly from the host."""
     from sparse_prefix_kv_amd.layers import SprintLayers
 
-    def med(fn):
-        fn()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
-            t0 = time.perf_counter()
-            fn()
-            torch.cuda.synchronize()
-            ts.append(time.perf_counter() - t0)
-        return sorted(ts)[len(ts) // 2]
+    def timed_block(b, run):
+        def state():
+            return [b.tokens.clone(), b.masked.clone(), b.kept_idx.clone(), b.O.clone()]
+
+        def poison():
+            b.tokens.fill_(-7)
+            b.O.zero_()
+        return graph_and_eager(torch, run, state, poison, reps)
 
     out = {"n_layers": args.layers,
            "note": "layers run in order, one attention launch each; the LM head reads the "
-                   "last layer; layer inputs are independent draws (no layer weights)"}
+                   "last layer; layer inputs are independent draws (no layer weights); "
+                   "block_ms and step_ms are HIP graph replays, eager_* host-launched runs"}
     blk = SprintLayers(x, args.layers, "cuda", mode="shared")
-    t_full = med(lambda: blk.run_full_block(n_steps))
+    t_full, t_full_e, all_ok = timed_block(blk, lambda: blk.run_full_block(n_steps))
     blk.run_block(n_steps)
-    step_full = med(lambda: [blk.attend_layers(False), blk.confidence_and_unmask(1)])
-    step_pr = med(lambda: [blk.attend_layers(True), blk.confidence_and_unmask(1)])
+    steps = {}
+    for name, pruned in (("full", False), ("pruned", True)):
+        fn = (lambda p=pruned: [blk.attend_layers(p), blk.confidence_and_unmask(1)])
+        g = capture_graph(torch, fn)
+        steps[name] = (replay_median(torch, g, reps), eager_median(torch, fn, reps))
+        del g
     for mode in ("shared", "per_layer"):
         if mode != blk.mode:
             del blk
             torch.cuda.synchronize()
             blk = SprintLayers(x, args.layers, "cuda", mode=mode)
-        t = med(lambda: blk.run_block(n_steps))
-        t_pass = med(lambda: [blk.prefix_confidence(), blk.score_and_prune()])
+        t, t_e, ok = timed_block(blk, lambda: blk.run_block(n_steps))
+        all_ok = all_ok and ok
+        gp = capture_graph(torch, lambda: [blk.prefix_confidence(), blk.score_and_prune()])
+        t_pass = replay_median(torch, gp, reps)
+        del gp
         out[mode] = {"block_ms": round(t * 1e3, 4), "pruning_pass_ms": round(t_pass * 1e3, 4),
-                     "speedup_vs_full": round(t_full / t, 4)}
-    out["full_prefix"] = {"block_ms": round(t_full * 1e3, 4)}
-    out["step_ms"] = {"pruned": round(step_pr * 1e3, 4), "full": round(step_full * 1e3, 4),
-                      "speedup": round(step_full / step_pr, 4)}
+                     "speedup_vs_full": round(t_full / t, 4),
+                     "eager_block_ms": round(t_e * 1e3, 4)}
+    out["full_prefix"] = {"block_ms": round(t_full * 1e3, 4),
+                          "eager_block_ms": round(t_full_e * 1e3, 4)}
+    out["step_ms"] = {"pruned": round(steps["pruned"][0] * 1e3, 4),
+                      "full": round(steps["full"][0] * 1e3, 4),
+                      "speedup": round(steps["full"][0] / steps["pruned"][0], 4),
+                      "eager_pruned": round(steps["pruned"][1] * 1e3, 4),
+                      "eager_full": round(steps["full"][1] * 1e3, 4)}
+    out["replay_matches_eager"] = bool(all_ok)
     del blk
     torch.cuda.synchronize()
     return out
