@@ -130,7 +130,7 @@ def _arg(t, name: str, dtype=None, numel: Optional[int] = None, shape=None):
         raise ValueError(f"{name} is required")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if numel is not None and t.numel() < numel:
         raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
@@ -149,10 +149,12 @@ def _stream(stream=None):
     return s.cuda_stream
 
 
-def _ws(nbytes: int, device, ws: Optional[torch.Tensor]):
+def _ws(size, device, ws: Optional[torch.Tensor]):
+    """The caller's workspace, or a new one of size() bytes (the size query
+    runs only then: the library checks a given workspace's size itself)."""
     if ws is not None:
         return ws
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    return torch.empty(max(int(size()), 256), dtype=torch.uint8, device=device)
 
 
 # --------------------------------------------------------------------------- host helpers
@@ -213,7 +215,7 @@ def lmhead_confidence(hidden: torch.Tensor, W: torch.Tensor, conf=None, argmax=N
     if lse is not None:
         _arg(lse, "lse", f32, M)
     _gpu(hidden=hidden, W=W, conf=conf, argmax=argmax, lse=lse)
-    ws = _ws(lmhead_confidence_ws(M, H, V, dt), dev, ws)
+    ws = _ws(lambda: lmhead_confidence_ws(M, H, V, dt), dev, ws)
     _check("lmhead_confidence", lib().lmhead_confidence(
         _ptr(hidden), M, H, _ptr(W), V, dt, _ptr(conf), _ptr(argmax), _ptr(lse), _ptr(ws),
         ws.numel(), _stream(stream)))
@@ -235,7 +237,7 @@ def sprint_score(K: torch.Tensor, conf: torch.Tensor, cu_len: torch.Tensor, alph
     score = (torch.empty(total_L, dtype=f32, device=dev) if score is None
              else _arg(score, "score", f32, total_L))
     _gpu(K=K, conf=conf, cu_len=cu_len, ibar=ibar, score=score)
-    ws = _ws(sprint_score_ws(total_L, nseq), dev, ws)
+    ws = _ws(lambda: sprint_score_ws(total_L, nseq), dev, ws)
     _check("sprint_score", lib().sprint_score(
         _ptr(K), _ptr(conf), _ptr(cu_len), nseq, total_L, Hkv, D, _dt(K), float(alpha),
         _ptr(ibar), _ptr(score), _ptr(ws), ws.numel(), _stream(stream)))
@@ -271,7 +273,7 @@ def sprint_prune_kv(score, modality, cu_len, keep, cu_kept, total_kept: int, K, 
         _arg(kept_idx, "kept_idx", i32, total_kept)
     _gpu(score=score, modality=modality, cu_len=cu_len, keep=keep, cu_kept=cu_kept, K=K, V=V,
          K_out=K_out, V_out=V_out, kept_idx=kept_idx)
-    ws = _ws(sprint_prune_kv_ws(total_L, nseq), dev, ws)
+    ws = _ws(lambda: sprint_prune_kv_ws(total_L, nseq), dev, ws)
     _check("sprint_prune_kv", lib().sprint_prune_kv(
         _ptr(score), _ptr(modality), _ptr(cu_len), _ptr(keep), _ptr(cu_kept), nseq, total_L,
         int(total_kept), _ptr(K), _ptr(V), Hkv, D, _dt(K), _ptr(K_out), _ptr(V_out),
@@ -299,7 +301,7 @@ def block_attend(Q, Kp, Vp, cu_kv, max_kv: int, Kb=None, Vb=None, scale: Optiona
     dev = Q.device
     O = torch.empty_like(Q) if O is None else _arg(O, "O", Q.dtype, Q.numel())
     _gpu(Q=Q, Kp=Kp, Vp=Vp, cu_kv=cu_kv, Kb=Kb, Vb=Vb, O=O)
-    ws = _ws(block_attend_ws(nseq, Lq, Hq, Hkv, D, max_kv, Kb is not None), dev, ws)
+    ws = _ws(lambda: block_attend_ws(nseq, Lq, Hq, Hkv, D, max_kv, Kb is not None), dev, ws)
     _check("block_attend", lib().block_attend(
         _ptr(Q), nseq, Lq, Hq, _ptr(Kp) if total_kv else None, _ptr(Vp) if total_kv else None,
         _ptr(cu_kv), total_kv, int(max_kv), _ptr(Kb), _ptr(Vb), Hkv, D, float(scale), _dt(Q),
@@ -377,7 +379,7 @@ def sprint_score_layers(K, conf, cu_len, alpha: float = 0.5, ibar=None, score=No
     score = (torch.empty(total_L, dtype=f32, device=dev) if score is None
              else _arg(score, "score", f32, total_L))
     _gpu(K=K, conf=conf, cu_len=cu_len, ibar=ibar, score=score)
-    ws = _ws(sprint_score_layers_ws(total_L, nseq, n_layers), dev, ws)
+    ws = _ws(lambda: sprint_score_layers_ws(total_L, nseq, n_layers), dev, ws)
     _check("sprint_score_layers", lib().sprint_score_layers(
         _ptr(K), n_layers, _ptr(conf), _ptr(cu_len), nseq, total_L, Hkv, D, _dt(K),
         float(alpha), _ptr(ibar), _ptr(score), _ptr(ws), ws.numel(), _stream(stream)))
@@ -414,7 +416,7 @@ def sprint_prune_kv_layers(score, modality, cu_len, keep, cu_kept, total_kept: i
         _arg(kept_idx, "kept_idx", i32, total_kept)
     _gpu(score=score, modality=modality, cu_len=cu_len, keep=keep, cu_kept=cu_kept, K=K, V=V,
          K_out=K_out, V_out=V_out, kept_idx=kept_idx)
-    ws = _ws(sprint_prune_kv_ws(total_L, nseq), dev, ws)
+    ws = _ws(lambda: sprint_prune_kv_ws(total_L, nseq), dev, ws)
     _check("sprint_prune_kv_layers", lib().sprint_prune_kv_layers(
         _ptr(score), _ptr(modality), _ptr(cu_len), _ptr(keep), _ptr(cu_kept), nseq, total_L,
         int(total_kept), _ptr(K), _ptr(V), n_layers, Hkv, D, _dt(K), _ptr(K_out), _ptr(V_out),
@@ -452,7 +454,7 @@ def moe_ffn(x, w_router, bias, w_gate, w_up, w_down, top_k: int, route_scale: fl
     _arg(gates, "gates", torch.float32, M * top_k)
     _gpu(x=x, w_router=w_router, bias=bias, w_gate=w_gate, w_up=w_up, w_down=w_down,
          residual=residual, y=y, expert_ids=expert_ids, gates=gates)
-    ws = _ws(moe_ffn_ws(M, H, E, top_k, inter), dev, ws)
+    ws = _ws(lambda: moe_ffn_ws(M, H, E, top_k, inter), dev, ws)
     _check("moe_ffn", lib().moe_ffn(
         _ptr(x), M, H, _ptr(w_router), _ptr(bias), E, top_k, float(route_scale), _ptr(w_gate),
         _ptr(w_up), _ptr(w_down), inter, _dt(x), _ptr(residual), _ptr(y), _ptr(expert_ids),
