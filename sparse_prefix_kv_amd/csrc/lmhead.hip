@@ -876,10 +876,10 @@ inline bool bf16_buffers(int64_t M, int H, int V, int dtype) {
 inline bool ring_path(int64_t M, int H, int V, int dtype) {
   return dtype == 1 && M <= 64 && H % (kGKC * kRRing) == 0;
 }
-// Waves (32 vocabulary rows each) per ring block: two below V = 65536 so
-// the grid still holds about 512 blocks or more (two streams per CU overlap
-// each other's start and end), four above.
-inline int ring_waves(int V) { return V < 65536 ? 2 : 4; }
+// Waves (32 vocabulary rows each) per ring block.  With the staggered chunk
+// order, four-wave blocks stream faster than two-wave ones at every
+// vocabulary size measured (V = 32768 to 163840, M = 32 and 64).
+constexpr int kRingWaves = 4;
 inline bool stream_path(int64_t M, int H, int V, int dtype) {
   return bf16_buffers(M, H, V, dtype) && M <= 64 && H % kGKC == 0;
 }
@@ -887,7 +887,7 @@ inline bool gemm_path(int64_t M, int H, int V, int dtype) {
   return bf16_buffers(M, H, V, dtype) && M > 64 && H % (2 * kGKC) == 0;
 }
 inline int tile_bv(int64_t M, int H, int V, int dtype) {
-  if (ring_path(M, H, V, dtype)) return 32 * ring_waves(V);
+  if (ring_path(M, H, V, dtype)) return 32 * kRingWaves;
   return gemm_path(M, H, V, dtype) ? kGB : 128;
 }
 }  // namespace
@@ -905,15 +905,12 @@ hipError_t launch_lmhead(const void* X, int64_t M, int H, const void* W, int V, 
   if (ring_path(M, H, V, dtype)) {
     const uint16_t* x16 = static_cast<const uint16_t*>(X);
     const uint16_t* w16 = static_cast<const uint16_t*>(W);
-    const int nw = ring_waves(V);
-    if (M <= 32 && nw == 2)
-      lmhead_ring_kernel<1, 2><<<dim3(n_vt), dim3(128), 0, st>>>(x16, M, H, w16, V, part, n_vt);
-    else if (M <= 32)
-      lmhead_ring_kernel<1, 4><<<dim3(n_vt), dim3(256), 0, st>>>(x16, M, H, w16, V, part, n_vt);
-    else if (nw == 2)
-      lmhead_ring_kernel<2, 2><<<dim3(n_vt), dim3(128), 0, st>>>(x16, M, H, w16, V, part, n_vt);
+    if (M <= 32)
+      lmhead_ring_kernel<1, kRingWaves>
+          <<<dim3(n_vt), dim3(64 * kRingWaves), 0, st>>>(x16, M, H, w16, V, part, n_vt);
     else
-      lmhead_ring_kernel<2, 4><<<dim3(n_vt), dim3(256), 0, st>>>(x16, M, H, w16, V, part, n_vt);
+      lmhead_ring_kernel<2, kRingWaves>
+          <<<dim3(n_vt), dim3(64 * kRingWaves), 0, st>>>(x16, M, H, w16, V, part, n_vt);
     e = hipGetLastError();
   } else if (stream_path(M, H, V, dtype)) {
     const dim3 grid(n_vt);
