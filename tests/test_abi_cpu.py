@@ -238,3 +238,30 @@ def test_c_program_links_and_runs_host_checks():
     r = subprocess.run([exe, "--host-only"], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "all checks passed" in r.stdout
+
+
+def test_binding_raises_without_the_library():
+    """No CPU fallback: with libsprint.so absent the binding raises at once."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("from sparse_prefix_kv_amd import sprint\n"
+            "sprint.LIB_PATH = '/nonexistent/libsprint.so'\n"
+            "try:\n"
+            "    sprint.lib()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "raised:" in r.stdout and "missing" in r.stdout
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True,
+                       text=True, cwd=root, timeout=120)
+    assert r.returncode != 0
+    assert "--gpus 2" in r.stderr and "single" in r.stderr
