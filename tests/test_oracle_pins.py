@@ -561,6 +561,31 @@ def test_layer_mean_importance_is_per_layer_scale_free():
                                oracle.key_norm_importance(Ks[2], cu), rtol=1e-14)
 
 
+def test_layer_mean_importance_closed_form():
+    # Keys of equal base norm times a per-position factor f give the closed
+    # form I_i = f_i / mean_seq(f) in one layer (Sparse Prefix Retention's
+    # mean-normalised norm).  With different factors per layer the shared
+    # importance is the mean of those closed forms over the layers.
+    rng = np.random.default_rng(5)
+    cu = np.array([0, 7, 7, 19], dtype=np.int64)          # an empty sequence too
+    L, Hkv, D = int(cu[-1]), 2, 8
+    facs, Ks = [], []
+    for _ in range(3):
+        base = rng.standard_normal((L, Hkv, D))
+        base /= np.sqrt((base ** 2).sum(axis=(1, 2)))[:, None, None]   # unit norm rows
+        f = rng.uniform(0.2, 5.0, size=L)
+        facs.append(f)
+        Ks.append(base * f[:, None, None])
+    expect = np.zeros(L)
+    for f in facs:
+        for s in range(len(cu) - 1):
+            a, b = cu[s], cu[s + 1]
+            if b > a:
+                expect[a:b] += f[a:b] / f[a:b].mean()
+    expect /= len(facs)
+    np.testing.assert_allclose(oracle.key_norm_importance_layers(Ks, cu), expect, rtol=1e-12)
+
+
 def test_layers_one_layer_is_run_block():
     wl, x, layers = _layer_stack(1)
     lay = x.layout
