@@ -103,3 +103,36 @@ def test_block_graph_replays_match_eager(name):
         for a, b in zip(ref, got):
             assert torch.equal(a, b), f"replay {rep} differs"
     del g
+
+
+def test_two_blocks_on_two_streams_match_serial_runs():
+    """No hidden shared state: two independent blocks (different workloads,
+    their own buffers and workspaces) launched on two streams at once give
+    bitwise the results of running them one after the other."""
+    blks = [SprintBlock(synth.make_inputs(synth.WORKLOADS[n], s), DEV)
+            for n, s in (("single4k", 0), ("tiny", 3))]
+    steps = [(b.T - 1) if b.T is not None else 6 for b in blks]
+
+    def state(b):
+        return [b.tokens.clone(), b.masked.clone(), b.kept_idx.clone(), b.O.clone(),
+                b.conf_blk.clone(), b.score.clone()]
+    ref = []
+    for b, n in zip(blks, steps):
+        b.run_block(n)
+        torch.cuda.synchronize()
+        ref.append(state(b))
+    for b in blks:
+        b.tokens.fill_(-7)
+        b.O.zero_()
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(3):
+        for b, n, s in zip(blks, steps, streams):
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                b.run_block(n)
+        for s in streams:
+            torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for b, r in zip(blks, ref):
+            assert all(torch.equal(u, v) for u, v in zip(state(b), r))
