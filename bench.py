@@ -374,6 +374,18 @@ def measure_layers(args, x, n_steps, torch, reps=5):
         out[mode] = {"block_ms": round(t * 1e3, 4), "pruning_pass_ms": round(t_pass * 1e3, 4),
                      "speedup_vs_full": round(t_full / t, 4),
                      "eager_block_ms": round(t_e * 1e3, 4)}
+        if mode == "shared":
+            # the same block with its prefix confidences carried from earlier
+            # blocks (a generation after its first block): no prefix LM head
+            t_c, t_ce, ok = timed_block(blk, lambda: blk.run_block(n_steps, prefix_conf=False))
+            all_ok = all_ok and ok
+            gp = capture_graph(torch, blk.score_and_prune)
+            t_pc = replay_median(torch, gp, reps)
+            del gp
+            out["shared_carried_conf"] = {
+                "block_ms": round(t_c * 1e3, 4), "pruning_pass_ms": round(t_pc * 1e3, 4),
+                "speedup_vs_full": round(t_full / t_c, 4), "eager_block_ms": round(t_ce * 1e3, 4),
+                "note": "prefix confidences carried (no prefix LM head in the pass)"}
     out["full_prefix"] = {"block_ms": round(t_full * 1e3, 4),
                           "eager_block_ms": round(t_full_e * 1e3, 4)}
     out["step_ms"] = {"pruned": round(steps["pruned"][0] * 1e3, 4),
@@ -725,7 +737,8 @@ def main():
     layers = None
     if args.layers > 0:
         layers = measure_layers(args, x, n_steps, torch)
-        log(f"[bench] {args.layers} layers: block {layers['shared']['block_ms']:.3f} ms shared set, "
+        log(f"[bench] {args.layers} layers: block {layers['shared']['block_ms']:.3f} ms shared set "
+            f"({layers['shared_carried_conf']['block_ms']:.3f} ms with carried confidences), "
             f"{layers['per_layer']['block_ms']:.3f} ms per-layer sets, "
             f"{layers['full_prefix']['block_ms']:.3f} ms full prefix")
 

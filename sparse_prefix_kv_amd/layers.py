@@ -148,8 +148,13 @@ class SprintLayers:
                              self.tau, self.steps_left(t), n_accepted=self.n_acc)
 
     # ------------------------------------------------------------------ block
-    def pruning_pass(self):
-        self.prefix_confidence()
+    def pruning_pass(self, prefix_conf: bool = True):
+        """`prefix_conf=False`: the prefix confidences are already in
+        conf_prefix (carried from the blocks that produced those positions,
+        as in a generation after its first block), so the pass runs no
+        prefix LM head."""
+        if prefix_conf:
+            self.prefix_confidence()
         self.score_and_prune()
         self.attend_layers(pruned=False)
         self.confidence_and_unmask(0)
@@ -158,9 +163,9 @@ class SprintLayers:
         self.attend_layers(pruned=True)
         self.confidence_and_unmask(t)
 
-    def run_block(self, n_steps: int):
+    def run_block(self, n_steps: int, prefix_conf: bool = True):
         self.reset()
-        self.pruning_pass()
+        self.pruning_pass(prefix_conf)
         for t in range(1, n_steps + 1):
             self.pruned_step(t)
 
