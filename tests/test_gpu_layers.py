@@ -143,3 +143,26 @@ def test_block_three_layers_tiny(mode):
             assert np.max(np.abs(O1[l] - res.outputs[n_steps][l])) <= 1e-5
     # one acceptance per step (at least one per step, nothing above tau)
     assert int(_np(blk.masked).sum()) == 32 - (n_steps + 1)
+
+
+@pytest.mark.parametrize("mode", ["shared", "per_layer"])
+def test_block_with_carried_confidences_matches_a_full_pass(mode):
+    """A pass that takes its prefix confidences as given (carried from the
+    blocks that produced those positions) computes exactly what a pass that
+    recomputes them does, when the given values are those confidences."""
+    x = synth.make_inputs(synth.WORKLOADS["single4k"], 0)
+    blk = SprintLayers(x, 3, DEV, mode=mode)
+    n_steps = blk.T - 1
+
+    def state():
+        return [blk.tokens.clone(), blk.masked.clone(), blk.kept_idx.clone(), blk.O.clone(),
+                blk.conf_blk.clone(), blk.score.clone(), blk.K_pr.clone()]
+    blk.run_block(n_steps)
+    torch.cuda.synchronize()
+    ref = state()
+    blk.tokens.fill_(-7)
+    blk.O.zero_()
+    blk.K_pr.zero_()
+    blk.run_block(n_steps, prefix_conf=False)
+    torch.cuda.synchronize()
+    assert all(torch.equal(u, v) for u, v in zip(state(), ref))
