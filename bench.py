@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--workload", default="single4k")
     ap.add_argument("--cold-iters", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=8)
+    ap.add_argument("--cpu-blocks", type=int, default=10)
     ap.add_argument("--gen-blocks", type=int, default=8,
                     help="blocks of the generation measurement (0: skip it)")
     ap.add_argument("--layers", type=int, default=16,
