@@ -235,7 +235,8 @@ int sprint_append_rows(const void* old, const int32_t* cu_old, int32_t nseq, int
  * matrix-vector product for the few tokens of a denoising step).
  * Supported: H a multiple of 512 (bf16) or 256 (fp32) up to 2048 / 1024,
  * inter a multiple of 512 / 256 up to 1024 / 512, E <= 1024, top_k <= 16,
- * M * top_k <= 8192.
+ * M <= 1024, M * top_k <= 8192; other shapes return SPRINT_EUNSUPPORTED.
+ * top_k > n_experts or a non-finite route_scale is SPRINT_EINVAL.
  * ------------------------------------------------------------------------ */
 size_t moe_ffn_ws(int32_t M, int32_t H, int32_t n_experts, int32_t top_k, int32_t inter);
 int moe_ffn(const void* x, int32_t M, int32_t H, const void* w_router, const float* bias,
