@@ -158,6 +158,34 @@ int sprint_prune_kv_layers(const float* score, const uint8_t* modality, const in
                            void* stream);
 
 /* ------------------------------------------------------------------------
+ * Several layers, each with its own kept set (Sparse Prefix Retention
+ * applied layer by layer: every layer scores its own keys with the shared
+ * prefix confidences and keeps its own top positions).  One call does what
+ * n_layers calls of sprint_score, then of sprint_prune_kv, do, with the
+ * same results bit for bit:
+ *   I_i^l = n_i^l / ((1/L) sum_{j in seq} n_j^l),  s_i^l = alpha*I_i^l + (1-alpha)*c_i.
+ *   K, V     [n_layers, total_L, Hkv, D] dtype (layer-major)
+ *   ibar, score [n_layers, total_L] float out (score: in, for the prune)
+ *   K_out, V_out [n_layers, total_kept, Hkv, D] dtype out
+ *   kept_idx [n_layers, total_kept] int32 out (layer l's set in row l)
+ * keep / cu_kept / total_kept are per sequence and modality, so every layer
+ * keeps the same number of rows.  1 <= n_layers <= 65535.  The score's
+ * workspace is sprint_score_layers_ws(total_L, nseq, n_layers); the prune's
+ * is sprint_prune_kv_per_layer_ws(total_L, nseq, n_layers).
+ * ------------------------------------------------------------------------ */
+int sprint_score_per_layer(const void* K, int32_t n_layers, const float* conf,
+                           const int32_t* cu_len, int32_t nseq, int64_t total_L, int32_t Hkv,
+                           int32_t D, int32_t dtype, float alpha, float* ibar, float* score,
+                           void* ws, size_t ws_bytes, void* stream);
+size_t sprint_prune_kv_per_layer_ws(int64_t total_L, int32_t nseq, int32_t n_layers);
+int sprint_prune_kv_per_layer(const float* score, const uint8_t* modality, const int32_t* cu_len,
+                              const int32_t* keep, const int32_t* cu_kept, int32_t nseq,
+                              int64_t total_L, int64_t total_kept, const void* K, const void* V,
+                              int32_t n_layers, int32_t Hkv, int32_t D, int32_t dtype,
+                              void* K_out, void* V_out, int32_t* kept_idx, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Block attention of a denoising step: the block's queries attend, without a
  * mask, to [prefix cache ; the block's own keys] (the block is predicted from
  * the clean prefix and its own noisy tokens).  With GQA, query head h reads

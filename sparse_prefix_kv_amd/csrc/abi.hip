@@ -95,10 +95,10 @@ int lmhead_confidence(const void* hidden, int64_t M, int32_t H, const void* W, i
 }
 
 // ---------------------------------------------------------------- score
-static int score_impl(const void* K, int32_t n_layers, const float* conf, const int32_t* cu_len,
-                      int32_t nseq, int64_t total_L, int32_t Hkv, int32_t D, int32_t dtype,
-                      float alpha, float* ibar, float* score, void* ws, size_t ws_bytes,
-                      void* stream) {
+static int score_impl(const void* K, int32_t n_layers, int per_layer, const float* conf,
+                      const int32_t* cu_len, int32_t nseq, int64_t total_L, int32_t Hkv,
+                      int32_t D, int32_t dtype, float alpha, float* ibar, float* score, void* ws,
+                      size_t ws_bytes, void* stream) {
   if (!dtype_ok(dtype) || nseq < 1 || total_L < 0 || total_L > INT32_MAX || Hkv < 1)
     return SPRINT_EINVAL;
   if (n_layers < 1 || n_layers > 65535) return SPRINT_EINVAL;
@@ -108,8 +108,8 @@ static int score_impl(const void* K, int32_t n_layers, const float* conf, const 
     return SPRINT_EINVAL;
   const int st = check_ws(ws, ws_bytes, score_ws_bytes(total_L, nseq, n_layers));
   if (st != SPRINT_OK) return st;
-  return status_of(launch_score(K, n_layers, conf, cu_len, nseq, total_L, Hkv, D, dtype, alpha,
-                                ibar, score, ws, as_stream(stream)));
+  return status_of(launch_score(K, n_layers, per_layer, conf, cu_len, nseq, total_L, Hkv, D,
+                                dtype, alpha, ibar, score, ws, as_stream(stream)));
 }
 
 size_t sprint_score_ws(int64_t total_L, int32_t nseq) {
@@ -120,7 +120,7 @@ size_t sprint_score_ws(int64_t total_L, int32_t nseq) {
 int sprint_score(const void* K, const float* conf, const int32_t* cu_len, int32_t nseq,
                  int64_t total_L, int32_t Hkv, int32_t D, int32_t dtype, float alpha, float* ibar,
                  float* score, void* ws, size_t ws_bytes, void* stream) {
-  return score_impl(K, 1, conf, cu_len, nseq, total_L, Hkv, D, dtype, alpha, ibar, score, ws,
+  return score_impl(K, 1, 0, conf, cu_len, nseq, total_L, Hkv, D, dtype, alpha, ibar, score, ws,
                     ws_bytes, stream);
 }
 
@@ -133,16 +133,24 @@ int sprint_score_layers(const void* K, int32_t n_layers, const float* conf, cons
                         int32_t nseq, int64_t total_L, int32_t Hkv, int32_t D, int32_t dtype,
                         float alpha, float* ibar, float* score, void* ws, size_t ws_bytes,
                         void* stream) {
-  return score_impl(K, n_layers, conf, cu_len, nseq, total_L, Hkv, D, dtype, alpha, ibar, score,
-                    ws, ws_bytes, stream);
+  return score_impl(K, n_layers, 0, conf, cu_len, nseq, total_L, Hkv, D, dtype, alpha, ibar,
+                    score, ws, ws_bytes, stream);
+}
+
+int sprint_score_per_layer(const void* K, int32_t n_layers, const float* conf,
+                           const int32_t* cu_len, int32_t nseq, int64_t total_L, int32_t Hkv,
+                           int32_t D, int32_t dtype, float alpha, float* ibar, float* score,
+                           void* ws, size_t ws_bytes, void* stream) {
+  return score_impl(K, n_layers, 1, conf, cu_len, nseq, total_L, Hkv, D, dtype, alpha, ibar,
+                    score, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- prune
 static int prune_impl(const float* score, const uint8_t* modality, const int32_t* cu_len,
                       const int32_t* keep, const int32_t* cu_kept, int32_t nseq, int64_t total_L,
                       int64_t total_kept, const void* K, const void* V, int32_t n_layers,
-                      int32_t Hkv, int32_t D, int32_t dtype, void* K_out, void* V_out,
-                      int32_t* kept_idx, void* ws, size_t ws_bytes, void* stream) {
+                      int per_layer, int32_t Hkv, int32_t D, int32_t dtype, void* K_out,
+                      void* V_out, int32_t* kept_idx, void* ws, size_t ws_bytes, void* stream) {
   if (!dtype_ok(dtype) || nseq < 1 || total_L < 0 || total_L > INT32_MAX || Hkv < 1)
     return SPRINT_EINVAL;
   if (n_layers < 1 || n_layers > 65535) return SPRINT_EINVAL;
@@ -152,16 +160,16 @@ static int prune_impl(const float* score, const uint8_t* modality, const int32_t
   if (total_L > 0 && (!dev4(score) || modality == nullptr || !dev16(K) || !dev16(V)))
     return SPRINT_EINVAL;
   if (total_kept > 0 && (!dev16(K_out) || !dev16(V_out) || !dev4(kept_idx))) return SPRINT_EINVAL;
-  const int st = check_ws(ws, ws_bytes, prune_ws_bytes(total_L, nseq));
+  const int st = check_ws(ws, ws_bytes, prune_ws_bytes(total_L, nseq, per_layer ? n_layers : 1));
   if (st != SPRINT_OK) return st;
   return status_of(launch_prune(score, modality, cu_len, keep, cu_kept, nseq, total_L, total_kept,
-                                K, V, n_layers, Hkv, D, dtype, K_out, V_out, kept_idx, ws,
-                                as_stream(stream)));
+                                K, V, n_layers, per_layer, Hkv, D, dtype, K_out, V_out, kept_idx,
+                                ws, as_stream(stream)));
 }
 
 size_t sprint_prune_kv_ws(int64_t total_L, int32_t nseq) {
   if (total_L < 0 || nseq < 1) return 0;
-  return prune_ws_bytes(total_L, nseq);
+  return prune_ws_bytes(total_L, nseq, 1);
 }
 
 int sprint_prune_kv(const float* score, const uint8_t* modality, const int32_t* cu_len,
@@ -169,7 +177,7 @@ int sprint_prune_kv(const float* score, const uint8_t* modality, const int32_t* 
                     int64_t total_kept, const void* K, const void* V, int32_t Hkv, int32_t D,
                     int32_t dtype, void* K_out, void* V_out, int32_t* kept_idx, void* ws,
                     size_t ws_bytes, void* stream) {
-  return prune_impl(score, modality, cu_len, keep, cu_kept, nseq, total_L, total_kept, K, V, 1,
+  return prune_impl(score, modality, cu_len, keep, cu_kept, nseq, total_L, total_kept, K, V, 1, 0,
                     Hkv, D, dtype, K_out, V_out, kept_idx, ws, ws_bytes, stream);
 }
 
@@ -180,7 +188,22 @@ int sprint_prune_kv_layers(const float* score, const uint8_t* modality, const in
                            void* V_out, int32_t* kept_idx, void* ws, size_t ws_bytes,
                            void* stream) {
   return prune_impl(score, modality, cu_len, keep, cu_kept, nseq, total_L, total_kept, K, V,
-                    n_layers, Hkv, D, dtype, K_out, V_out, kept_idx, ws, ws_bytes, stream);
+                    n_layers, 0, Hkv, D, dtype, K_out, V_out, kept_idx, ws, ws_bytes, stream);
+}
+
+size_t sprint_prune_kv_per_layer_ws(int64_t total_L, int32_t nseq, int32_t n_layers) {
+  if (total_L < 0 || nseq < 1 || n_layers < 1) return 0;
+  return prune_ws_bytes(total_L, nseq, n_layers);
+}
+
+int sprint_prune_kv_per_layer(const float* score, const uint8_t* modality, const int32_t* cu_len,
+                              const int32_t* keep, const int32_t* cu_kept, int32_t nseq,
+                              int64_t total_L, int64_t total_kept, const void* K, const void* V,
+                              int32_t n_layers, int32_t Hkv, int32_t D, int32_t dtype,
+                              void* K_out, void* V_out, int32_t* kept_idx, void* ws,
+                              size_t ws_bytes, void* stream) {
+  return prune_impl(score, modality, cu_len, keep, cu_kept, nseq, total_L, total_kept, K, V,
+                    n_layers, 1, Hkv, D, dtype, K_out, V_out, kept_idx, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------- attention

@@ -82,6 +82,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
     const float* __restrict__ score, const uint8_t* __restrict__ modality,
     const int32_t* __restrict__ cu_len, const int32_t* __restrict__ keep, int nseq,
     int64_t total_L, SegThresh* __restrict__ thr) {
+  // grid y: the layer whose scores select its own set (one layer otherwise)
+  score += static_cast<int64_t>(blockIdx.y) * total_L;
+  thr += static_cast<int64_t>(blockIdx.y) * nseq * 2;
   const int seg = blockIdx.x;
   const int s = seg >> 1;
   const uint8_t mod = static_cast<uint8_t>(seg & 1);
@@ -226,6 +229,10 @@ __global__ __launch_bounds__(64) void chunk_count_kernel(const float* __restrict
                                                          int32_t* __restrict__ counts) {
   SeqChunk sc;
   if (!find_seq_chunk(cu_len, nseq, kChunk, total_L, blockIdx.x, sc)) return;
+  // grid y: the layer (its scores, thresholds and counts; one layer otherwise)
+  score += static_cast<int64_t>(blockIdx.y) * total_L;
+  thr += static_cast<int64_t>(blockIdx.y) * nseq * 2;
+  counts += static_cast<int64_t>(blockIdx.y) * gridDim.x;
   const int64_t p = sc.begin + static_cast<int64_t>(sc.c) * kChunk + threadIdx.x;
   const bool f = p < sc.begin + sc.len && kept_at(score, modality, thr, sc.seq, p);
   const uint64_t bal = __ballot(f);
@@ -238,15 +245,23 @@ __global__ __launch_bounds__(kCopyThreads) void compact_kernel(
     int64_t total_L, int64_t total_kept, const SegThresh* __restrict__ thr,
     const int32_t* __restrict__ counts, const char* __restrict__ K, const char* __restrict__ V,
     int row_vecs, char* __restrict__ K_out, char* __restrict__ V_out,
-    int32_t* __restrict__ kept_idx) {
+    int32_t* __restrict__ kept_idx, int per_layer) {
   SeqChunk sc;
   if (!find_seq_chunk(cu_len, nseq, kChunk, total_L, blockIdx.x, sc)) return;
-  // layer blockIdx.y: its caches; layer 0 writes kept_idx
+  // layer blockIdx.y: its caches.  One shared set: layer 0 writes kept_idx.
+  // A set per layer: the layer's own scores, thresholds, counts and kept_idx.
   const int64_t layer = blockIdx.y;
   K += layer * total_L * row_vecs * 16;
   V += layer * total_L * row_vecs * 16;
   K_out += layer * total_kept * row_vecs * 16;
   V_out += layer * total_kept * row_vecs * 16;
+  const bool writes_idx = per_layer || layer == 0;
+  if (per_layer) {
+    score += layer * total_L;
+    thr += layer * nseq * 2;
+    counts += layer * gridDim.x;
+    kept_idx += layer * total_kept;
+  }
   __shared__ int64_t s_pos[kChunk];
   __shared__ int64_t s_slot0, s_limit;
   __shared__ int s_nk;
@@ -265,7 +280,7 @@ __global__ __launch_bounds__(kCopyThreads) void compact_kernel(
     if (f) {
       s_pos[rank] = p;
       const int64_t slot = slot0 + rank;
-      if (layer == 0 && slot >= 0 && slot < limit) kept_idx[slot] = static_cast<int32_t>(p);
+      if (writes_idx && slot >= 0 && slot < limit) kept_idx[slot] = static_cast<int32_t>(p);
     }
     if (lane == 0) {
       s_nk = __popcll(bal);
@@ -308,30 +323,34 @@ __global__ __launch_bounds__(kCopyThreads) void compact_kernel(
 
 }  // namespace
 
-size_t prune_ws_bytes(int64_t total_L, int nseq) {
-  const size_t thr = align_up(static_cast<size_t>(nseq) * 2 * sizeof(SegThresh), 256);
-  const size_t cnt = align_up(static_cast<size_t>(chunk_bound(total_L, nseq, kChunk)) * 4, 256);
+size_t prune_ws_bytes(int64_t total_L, int nseq, int n_sets) {
+  const size_t thr =
+      align_up(static_cast<size_t>(nseq) * 2 * n_sets * sizeof(SegThresh), 256);
+  const size_t cnt =
+      align_up(static_cast<size_t>(chunk_bound(total_L, nseq, kChunk)) * n_sets * 4, 256);
   return thr + cnt;
 }
 
 hipError_t launch_prune(const float* score, const uint8_t* modality, const int32_t* cu_len,
                         const int32_t* keep, const int32_t* cu_kept, int nseq, int64_t total_L,
-                        int64_t total_kept, const void* K, const void* V, int n_layers, int Hkv,
-                        int D, int dtype, void* K_out, void* V_out, int32_t* kept_idx, void* ws,
-                        hipStream_t st) {
+                        int64_t total_kept, const void* K, const void* V, int n_layers,
+                        int per_layer, int Hkv, int D, int dtype, void* K_out, void* V_out,
+                        int32_t* kept_idx, void* ws, hipStream_t st) {
   if (total_L == 0) return hipSuccess;
+  const int n_sets = per_layer ? n_layers : 1;
   SegThresh* thr = static_cast<SegThresh*>(ws);
   int32_t* counts = reinterpret_cast<int32_t*>(
-      static_cast<char*>(ws) + align_up(static_cast<size_t>(nseq) * 2 * sizeof(SegThresh), 256));
+      static_cast<char*>(ws) +
+      align_up(static_cast<size_t>(nseq) * 2 * n_sets * sizeof(SegThresh), 256));
   const int es = dtype == 1 ? 2 : 4;
   const int row_vecs = Hkv * D * es / 16;
   const int64_t nchunk = chunk_bound(total_L, nseq, kChunk);
-  topk_threshold_kernel<<<dim3(nseq * 2), dim3(kSelThreads), 0, st>>>(score, modality, cu_len,
-                                                                       keep, nseq, total_L, thr);
+  topk_threshold_kernel<<<dim3(nseq * 2, n_sets), dim3(kSelThreads), 0, st>>>(
+      score, modality, cu_len, keep, nseq, total_L, thr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  chunk_count_kernel<<<dim3(nchunk), dim3(64), 0, st>>>(score, modality, cu_len, nseq, total_L,
-                                                        thr, counts);
+  chunk_count_kernel<<<dim3(static_cast<unsigned>(nchunk), n_sets), dim3(64), 0, st>>>(
+      score, modality, cu_len, nseq, total_L, thr, counts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (total_kept == 0) return hipSuccess;
@@ -339,7 +358,7 @@ hipError_t launch_prune(const float* score, const uint8_t* modality, const int32
                    dim3(kCopyThreads), 0, st>>>(
       score, modality, cu_len, cu_kept, nseq, total_L, total_kept, thr, counts,
       static_cast<const char*>(K), static_cast<const char*>(V), row_vecs,
-      static_cast<char*>(K_out), static_cast<char*>(V_out), kept_idx);
+      static_cast<char*>(K_out), static_cast<char*>(V_out), kept_idx, per_layer);
   return hipGetLastError();
 }
 

@@ -7,10 +7,11 @@
 //   2. score_kernel: every chunk re-derives its sequence's mean from the
 //      chunk sums in one fixed order (so all chunks agree bitwise), then
 //      writes I_i = n_i / mean and s_i = alpha*I_i + (1-alpha)*c_i in place.
-// With several layers (one kept set shared by every layer's cache), launch 1
-// runs once per layer (grid y) into per-layer norms and chunk sums, and I_i
-// is the mean over layers of each layer's I_i, summed in layer order; one
-// layer gives exactly the single-layer arithmetic.
+// With several layers, launch 1 runs once per layer (grid y) into per-layer
+// norms and chunk sums.  For one kept set shared by every layer's cache, I_i
+// is the mean over layers of each layer's I_i, summed in layer order; for a
+// set per layer, launch 2 also runs per layer and writes each layer's own
+// I and s.  One layer gives exactly the single-layer arithmetic either way.
 // HBM-bound: it reads each key row once (Hkv*D elements) and 12 bytes of
 // per-position floats.  Eight lanes share a row: one wave instruction reads
 // 128 contiguous bytes of eight rows (whole cache lines), and every lane has
@@ -112,10 +113,12 @@ __global__ __launch_bounds__(kThreads) void keynorm_kernel(const char* __restric
 }
 
 // One wave per 64-position chunk.  norms: [n_layers, total_L] (may be ibar
-// itself for one layer); partial: [n_layers, n_chunks].
+// itself for one layer); partial: [n_layers, n_chunks].  per_layer: grid y
+// is the layer, and each layer's own I and s go to ibar/score [n_layers,
+// total_L] (one kept set per layer); otherwise I is the layer mean.
 __global__ __launch_bounds__(64) void score_kernel(const float* __restrict__ conf,
                                                    const int32_t* __restrict__ cu_len, int nseq,
-                                                   int64_t total_L, int n_layers,
+                                                   int64_t total_L, int n_layers, int per_layer,
                                                    const float* norms,
                                                    const float* __restrict__ partial, float alpha,
                                                    float* ibar, float* __restrict__ score) {
@@ -124,8 +127,10 @@ __global__ __launch_bounds__(64) void score_kernel(const float* __restrict__ con
   const int lane = threadIdx.x;
   const int64_t p = sc.begin + static_cast<int64_t>(sc.c) * kChunk + lane;
   const bool ok = p < sc.begin + sc.len;
+  const int l0 = per_layer ? static_cast<int>(blockIdx.y) : 0;
+  const int l1 = per_layer ? l0 + 1 : n_layers;
   float ib = 0.f;
-  for (int l = 0; l < n_layers; ++l) {
+  for (int l = l0; l < l1; ++l) {
     const float* part = partial + static_cast<int64_t>(l) * gridDim.x;
     float acc = 0.f;
     for (int i = lane; i < sc.nchunks; i += 64) acc += part[sc.first + i];
@@ -134,9 +139,10 @@ __global__ __launch_bounds__(64) void score_kernel(const float* __restrict__ con
     if (ok) ib += mean > 0.f ? norms[static_cast<int64_t>(l) * total_L + p] / mean : 1.f;
   }
   if (ok) {
-    ib /= static_cast<float>(n_layers);
-    ibar[p] = ib;
-    score[p] = alpha * ib + (1.f - alpha) * conf[p];
+    ib /= static_cast<float>(l1 - l0);
+    const int64_t o = static_cast<int64_t>(l0) * total_L + p;
+    ibar[o] = ib;
+    score[o] = alpha * ib + (1.f - alpha) * conf[p];
   }
 }
 
@@ -150,9 +156,10 @@ size_t score_ws_bytes(int64_t total_L, int nseq, int n_layers) {
   return part + norms;
 }
 
-hipError_t launch_score(const void* K, int n_layers, const float* conf, const int32_t* cu_len,
-                        int nseq, int64_t total_L, int Hkv, int D, int dtype, float alpha,
-                        float* ibar, float* score, void* ws, hipStream_t st) {
+hipError_t launch_score(const void* K, int n_layers, int per_layer, const float* conf,
+                        const int32_t* cu_len, int nseq, int64_t total_L, int Hkv, int D,
+                        int dtype, float alpha, float* ibar, float* score, void* ws,
+                        hipStream_t st) {
   if (total_L == 0) return hipSuccess;
   const int es = dtype == 1 ? 2 : 4;
   const int row_vecs = Hkv * D * es / 16;
@@ -173,8 +180,9 @@ hipError_t launch_score(const void* K, int n_layers, const float* conf, const in
         static_cast<const char*>(K), cu_len, nseq, total_L, row_vecs, norms, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  score_kernel<<<dim3(nblk), dim3(64), 0, st>>>(conf, cu_len, nseq, total_L, n_layers, norms,
-                                                partial, alpha, ibar, score);
+  const dim3 sgrid(static_cast<unsigned>(nblk), per_layer ? static_cast<unsigned>(n_layers) : 1u);
+  score_kernel<<<sgrid, dim3(64), 0, st>>>(conf, cu_len, nseq, total_L, n_layers, per_layer, norms,
+                                           partial, alpha, ibar, score);
   return hipGetLastError();
 }
 

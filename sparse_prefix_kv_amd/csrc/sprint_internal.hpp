@@ -14,17 +14,18 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // K is [n_layers, total_L, Hkv, D]; I is the mean over layers of each layer's
 // mean-normalised key norm
 size_t score_ws_bytes(int64_t total_L, int nseq, int n_layers);
-hipError_t launch_score(const void* K, int n_layers, const float* conf, const int32_t* cu_len,
-                        int nseq, int64_t total_L, int Hkv, int D, int dtype, float alpha,
-                        float* ibar, float* score, void* ws, hipStream_t st);
+hipError_t launch_score(const void* K, int n_layers, int per_layer, const float* conf,
+                        const int32_t* cu_len, int nseq, int64_t total_L, int Hkv, int D,
+                        int dtype, float alpha, float* ibar, float* score, void* ws,
+                        hipStream_t st);
 
 // ---- per-modality top-k + compaction
-size_t prune_ws_bytes(int64_t total_L, int nseq);
+size_t prune_ws_bytes(int64_t total_L, int nseq, int n_sets);
 hipError_t launch_prune(const float* score, const uint8_t* modality, const int32_t* cu_len,
                         const int32_t* keep, const int32_t* cu_kept, int nseq, int64_t total_L,
-                        int64_t total_kept, const void* K, const void* V, int n_layers, int Hkv,
-                        int D, int dtype, void* K_out, void* V_out, int32_t* kept_idx, void* ws,
-                        hipStream_t st);
+                        int64_t total_kept, const void* K, const void* V, int n_layers,
+                        int per_layer, int Hkv, int D, int dtype, void* K_out, void* V_out,
+                        int32_t* kept_idx, void* ws, hipStream_t st);
 
 // ---- block attention (split-KV + combine)
 struct AttnPlan {

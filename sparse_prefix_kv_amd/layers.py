@@ -7,7 +7,8 @@ the last layer's output.  Sparse Prefix Retention then prunes every layer's
 cache, either with one kept set shared by all layers (the layer-mean of the
 mean-normalised key norms: sprint_score_layers + sprint_prune_kv_layers, one
 top-k and one compaction launch over all layers) or with a set per layer
-(sprint_score + sprint_prune_kv per layer).  Steps attend layer by layer, as
+(sprint_score_per_layer + sprint_prune_kv_per_layer: each layer's own scores
+and kept set, still one launch of each kernel over all layers).  Steps attend layer by layer, as
 a model's layers must run in order; only the layers' inputs are independent
 draws here, since no layer weights are part of this path.
 
@@ -95,7 +96,8 @@ class SprintLayers:
         self.ws_lm_prefix = ws(sprint.lmhead_confidence_ws(tl, wl.H, wl.vocab, dti))
         self.ws_lm_blk = ws(sprint.lmhead_confidence_ws(M, wl.H, wl.vocab, dti))
         self.ws_score = ws(sprint.sprint_score_layers_ws(tl, self.nseq, n_layers))
-        self.ws_prune = ws(sprint.sprint_prune_kv_ws(tl, self.nseq))
+        self.ws_prune = ws(sprint.sprint_prune_kv_ws(tl, self.nseq) if mode == "shared" else
+                           sprint.sprint_prune_kv_per_layer_ws(tl, self.nseq, n_layers))
         self.ws_att_full = ws(sprint.block_attend_ws(self.nseq, self.Lq, self.Hq, self.Hkv, self.D,
                                                      self.max_len, True))
         self.ws_att_pr = ws(sprint.block_attend_ws(self.nseq, self.Lq, self.Hq, self.Hkv, self.D,
@@ -121,13 +123,12 @@ class SprintLayers:
                                           K_out=self.K_pr, V_out=self.V_pr,
                                           kept_idx=self.kept_idx[0], ws=self.ws_prune)
             return
-        for l in range(self.n_layers):
-            sprint.sprint_score(self.K[l], self.conf_prefix, self.cu_len, self.alpha,
-                                ibar=self.ibar[l], score=self.score[l], ws=self.ws_score)
-            sprint.sprint_prune_kv(self.score[l], self.modality, self.cu_len, self.keep,
-                                   self.cu_kept, self.total_kept, self.K[l], self.V[l],
-                                   K_out=self.K_pr[l], V_out=self.V_pr[l],
-                                   kept_idx=self.kept_idx[l], ws=self.ws_prune)
+        sprint.sprint_score_per_layer(self.K, self.conf_prefix, self.cu_len, self.alpha,
+                                      ibar=self.ibar, score=self.score, ws=self.ws_score)
+        sprint.sprint_prune_kv_per_layer(self.score, self.modality, self.cu_len, self.keep,
+                                         self.cu_kept, self.total_kept, self.K, self.V,
+                                         K_out=self.K_pr, V_out=self.V_pr, kept_idx=self.kept_idx,
+                                         ws=self.ws_prune)
 
     def attend_layers(self, pruned: bool):
         for l in range(self.n_layers):

@@ -58,6 +58,15 @@ _SIGS = {
                                               _c_void_p, _i32, _i64, _i64, _c_void_p, _c_void_p,
                                               _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
                                               _c_void_p, _c_void_p, _size, _c_void_p]),
+    "sprint_score_per_layer": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i64,
+                                              _i32, _i32, _i32, _f32, _c_void_p, _c_void_p,
+                                              _c_void_p, _size, _c_void_p]),
+    "sprint_prune_kv_per_layer_ws": (_size, [_i64, _i32, _i32]),
+    "sprint_prune_kv_per_layer": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                 _c_void_p, _i32, _i64, _i64, _c_void_p,
+                                                 _c_void_p, _i32, _i32, _i32, _i32, _c_void_p,
+                                                 _c_void_p, _c_void_p, _c_void_p, _size,
+                                                 _c_void_p]),
     "moe_ffn_ws": (_size, [_i32, _i32, _i32, _i32, _i32]),
     "moe_ffn": (ctypes.c_int, [_c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i32, _f32,
                                _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _c_void_p,
@@ -418,6 +427,74 @@ def sprint_prune_kv_layers(score, modality, cu_len, keep, cu_kept, total_kept: i
          K_out=K_out, V_out=V_out, kept_idx=kept_idx)
     ws = _ws(lambda: sprint_prune_kv_ws(total_L, nseq), dev, ws)
     _check("sprint_prune_kv_layers", lib().sprint_prune_kv_layers(
+        _ptr(score), _ptr(modality), _ptr(cu_len), _ptr(keep), _ptr(cu_kept), nseq, total_L,
+        int(total_kept), _ptr(K), _ptr(V), n_layers, Hkv, D, _dt(K), _ptr(K_out), _ptr(V_out),
+        _ptr(kept_idx), _ptr(ws), ws.numel(), _stream(stream)))
+    return K_out, V_out, kept_idx
+
+
+def sprint_score_per_layer(K, conf, cu_len, alpha: float = 0.5, ibar=None, score=None, ws=None,
+                           stream=None):
+    """Each layer's own key-norm importance and score.  K [n_layers, total_L, Hkv, D];
+    ibar, score [n_layers, total_L]."""
+    n_layers, total_L, Hkv, D = K.shape
+    _dt(K)
+    _arg(K, "K")
+    f32 = torch.float32
+    _arg(conf, "conf", f32, total_L)
+    _arg(cu_len, "cu_len", torch.int32)
+    nseq = cu_len.numel() - 1
+    dev = K.device
+    shape = (n_layers, total_L)
+    ibar = (torch.empty(shape, dtype=f32, device=dev) if ibar is None
+            else _arg(ibar, "ibar", f32, shape=shape))
+    score = (torch.empty(shape, dtype=f32, device=dev) if score is None
+             else _arg(score, "score", f32, shape=shape))
+    _gpu(K=K, conf=conf, cu_len=cu_len, ibar=ibar, score=score)
+    ws = _ws(lambda: sprint_score_layers_ws(total_L, nseq, n_layers), dev, ws)
+    _check("sprint_score_per_layer", lib().sprint_score_per_layer(
+        _ptr(K), n_layers, _ptr(conf), _ptr(cu_len), nseq, total_L, Hkv, D, _dt(K),
+        float(alpha), _ptr(ibar), _ptr(score), _ptr(ws), ws.numel(), _stream(stream)))
+    return ibar, score
+
+
+def sprint_prune_kv_per_layer_ws(total_L: int, nseq: int, n_layers: int) -> int:
+    return int(lib().sprint_prune_kv_per_layer_ws(total_L, nseq, n_layers))
+
+
+def sprint_prune_kv_per_layer(score, modality, cu_len, keep, cu_kept, total_kept: int, K, V,
+                              K_out=None, V_out=None, kept_idx=None, ws=None, stream=None):
+    """Each layer's own kept set compacted in its cache.  score [n_layers, total_L];
+    K, V [n_layers, total_L, Hkv, D]; kept_idx [n_layers, total_kept]."""
+    n_layers, total_L, Hkv, D = K.shape
+    _dt(K)
+    _arg(K, "K")
+    _arg(V, "V", K.dtype, shape=K.shape)
+    i32 = torch.int32
+    _arg(cu_len, "cu_len", i32)
+    nseq = cu_len.numel() - 1
+    _arg(score, "score", torch.float32, shape=(n_layers, total_L))
+    _arg(modality, "modality", torch.uint8, total_L)
+    _arg(keep, "keep", i32, 2 * nseq)
+    _arg(cu_kept, "cu_kept", i32, nseq + 1)
+    if not 0 <= total_kept <= total_L:
+        raise ValueError("total_kept must lie in [0, total_L]")
+    dev = K.device
+    shape = (n_layers, max(total_kept, 1), Hkv, D)
+    if K_out is None:
+        K_out = torch.empty(shape, dtype=K.dtype, device=dev)[:, :total_kept]
+    if V_out is None:
+        V_out = torch.empty(shape, dtype=V.dtype, device=dev)[:, :total_kept]
+    if kept_idx is None:
+        kept_idx = torch.empty((n_layers, max(total_kept, 1)), dtype=i32, device=dev)[:, :total_kept]
+    if total_kept:
+        _arg(K_out, "K_out", K.dtype, shape=(n_layers, total_kept, Hkv, D))
+        _arg(V_out, "V_out", K.dtype, shape=(n_layers, total_kept, Hkv, D))
+        _arg(kept_idx, "kept_idx", i32, shape=(n_layers, total_kept))
+    _gpu(score=score, modality=modality, cu_len=cu_len, keep=keep, cu_kept=cu_kept, K=K, V=V,
+         K_out=K_out, V_out=V_out, kept_idx=kept_idx)
+    ws = _ws(lambda: sprint_prune_kv_per_layer_ws(total_L, nseq, n_layers), dev, ws)
+    _check("sprint_prune_kv_per_layer", lib().sprint_prune_kv_per_layer(
         _ptr(score), _ptr(modality), _ptr(cu_len), _ptr(keep), _ptr(cu_kept), nseq, total_L,
         int(total_kept), _ptr(K), _ptr(V), n_layers, Hkv, D, _dt(K), _ptr(K_out), _ptr(V_out),
         _ptr(kept_idx), _ptr(ws), ws.numel(), _stream(stream)))

@@ -104,6 +104,27 @@ def test_score_and_prune_reject_before_hip():
     assert _call("sprint_prune_kv", *a) == 3
 
 
+def test_per_layer_score_and_prune_reject_before_hip():
+    ws = sprint.sprint_prune_kv_per_layer_ws(4096, 1, 16)
+    assert ws > sprint.sprint_prune_kv_ws(4096, 1)
+    assert sprint.sprint_prune_kv_per_layer_ws(4096, 1, 0) == 0
+    sc = [FAKE, 16, FAKE, FAKE, 1, 4096, 4, 128, sprint.BF16, 0.5, FAKE, FAKE, FAKE, 1 << 30, None]
+    a = list(sc); a[1] = 0
+    assert _call("sprint_score_per_layer", *a) == 1                 # no layers
+    a = list(sc); a[1] = 65536
+    assert _call("sprint_score_per_layer", *a) == 1
+    a = list(sc); a[13] = sprint.sprint_score_layers_ws(4096, 1, 16) - 1
+    assert _call("sprint_score_per_layer", *a) == 3
+    pr = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4096, 3481, FAKE, FAKE, 16, 4, 128, sprint.BF16,
+          FAKE, FAKE, FAKE, FAKE, ws, None]
+    a = list(pr); a[18] = sprint.sprint_prune_kv_ws(4096, 1)
+    assert _call("sprint_prune_kv_per_layer", *a) == 3              # one layer's workspace
+    a = list(pr); a[10] = 0
+    assert _call("sprint_prune_kv_per_layer", *a) == 1
+    a = list(pr); a[16] = None
+    assert _call("sprint_prune_kv_per_layer", *a) == 1              # NULL kept_idx
+
+
 def test_attend_and_unmask_reject_before_hip():
     at = [FAKE, 1, 32, 16, FAKE, FAKE, FAKE, 4096, 4096, FAKE, FAKE, 4, 128, 0.088, sprint.BF16,
           FAKE, FAKE, 1 << 30, None]

@@ -3,7 +3,8 @@
 sprint_score_layers / sprint_prune_kv_layers at one layer must equal the
 single-layer calls bitwise; at several layers the layer-mean importance, the
 scores and the kept set follow the oracle, and the compaction of every layer
-is a bit copy.  A whole block of the tiny workload with three layers is
+is a bit copy.  The batched per-layer calls (a kept set per layer) equal the
+single-layer calls made layer by layer, bitwise.  A whole block of the tiny workload with three layers is
 compared in both modes (one shared kept set, one set per layer).
 """
 import numpy as np
@@ -88,6 +89,43 @@ def test_score_and_prune_layers_match_oracle(name, n_layers):
     for l in range(n_layers):
         Kc, Vc = oracle.compact(_np(K[l]), _np(V[l]), kept_o)
         assert np.array_equal(_np(Kp[l]), Kc) and np.array_equal(_np(Vp[l]), Vc)
+
+
+@pytest.mark.parametrize("name,n_layers,ratios", [("tiny", 3, None), ("single4k", 4, None),
+                                                   ("ragged8", 2, None), ("ragged8", 3, (0.0, 0.0)),
+                                                   ("tiny", 1, (0.5, 1.0))])
+def test_per_layer_batched_equals_single_calls(name, n_layers, ratios):
+    """sprint_score_per_layer / sprint_prune_kv_per_layer give, bit for bit,
+    what sprint_score / sprint_prune_kv give called on each layer alone."""
+    wl = synth.WORKLOADS[name]
+    x = synth.make_inputs(wl, 0, with_lmhead=False)
+    lay = x.layout
+    K = torch.stack([_dev(k, wl.dtype) for k in _stack(wl, x, n_layers)])
+    V = torch.stack([_dev(v, wl.dtype) for v in
+                     [x.V] + [synth.make_layer_inputs(wl, lay, l, 0)[2] for l in range(1, n_layers)]])
+    conf = torch.from_numpy(np.random.default_rng(3).uniform(0, 1e-3, lay.total_L)
+                            .astype(np.float32)).to(DEV)
+    cu = torch.from_numpy(lay.cu_len.astype(np.int32)).to(DEV)
+    mod = torch.from_numpy(lay.modality).to(DEV)
+    r_text, r_img = (wl.r_text, wl.r_img) if ratios is None else ratios
+    keep, cu_kept, tk = sprint.sprint_plan_keep(lay.n_text, lay.n_img, r_text, r_img)
+    keep_t = torch.tensor(keep, dtype=torch.int32, device=DEV)
+    cuk_t = torch.tensor(cu_kept, dtype=torch.int32, device=DEV)
+    ib, sc = sprint.sprint_score_per_layer(K, conf, cu, 0.5)
+    Kp, Vp, kept = sprint.sprint_prune_kv_per_layer(sc, mod, cu, keep_t, cuk_t, tk, K, V)
+    torch.cuda.synchronize()
+    assert kept.shape == (n_layers, tk)
+    for l in range(n_layers):
+        ib1, sc1 = sprint.sprint_score(K[l], conf, cu, 0.5)
+        K1, V1, k1 = sprint.sprint_prune_kv(sc1, mod, cu, keep_t, cuk_t, tk, K[l], V[l])
+        torch.cuda.synchronize()
+        assert torch.equal(ib[l], ib1) and torch.equal(sc[l], sc1), l
+        assert torch.equal(kept[l], k1) and torch.equal(Kp[l], K1) and torch.equal(Vp[l], V1), l
+    # every layer's own set follows the oracle's selection on that layer's scores
+    for l in range(n_layers):
+        kept_o = oracle.select_kept(_np(sc[l]).astype(np.float64), lay.modality, lay.cu_len,
+                                    np.asarray(keep).reshape(-1, 2))
+        np.testing.assert_array_equal(_np(kept[l]), kept_o)
 
 
 def _sets_agree(kept, score, cu, modality):
