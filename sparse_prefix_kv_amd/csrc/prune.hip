@@ -18,6 +18,8 @@
 //                             copies the K and V rows (16-byte vectors), of
 //                             every layer (grid y) when one kept set serves
 //                             several layers' caches.
+// With a kept set per layer, all three run once per layer (grid y), each
+// layer on its own scores, thresholds, counts and kept_idx row.
 // The copy dominates: 2 x kept x row bytes read and written, HBM-bound.
 #include <limits.h>
 

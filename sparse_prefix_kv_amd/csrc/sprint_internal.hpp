@@ -11,8 +11,9 @@ namespace sprint {
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---- key norm + composite score
-// K is [n_layers, total_L, Hkv, D]; I is the mean over layers of each layer's
-// mean-normalised key norm
+// K is [n_layers, total_L, Hkv, D].  per_layer = 0: I is the mean over
+// layers of each layer's mean-normalised key norm (ibar, score [total_L]);
+// per_layer = 1: each layer's own I and s (ibar, score [n_layers, total_L]).
 size_t score_ws_bytes(int64_t total_L, int nseq, int n_layers);
 hipError_t launch_score(const void* K, int n_layers, int per_layer, const float* conf,
                         const int32_t* cu_len, int nseq, int64_t total_L, int Hkv, int D,
@@ -20,6 +21,9 @@ hipError_t launch_score(const void* K, int n_layers, int per_layer, const float*
                         hipStream_t st);
 
 // ---- per-modality top-k + compaction
+// per_layer = 0: one kept set (from score [total_L]) compacts every layer's
+// cache; per_layer = 1: layer l selects from score[l] and writes kept_idx[l]
+// (n_sets = n_layers thresholds and chunk counts in the workspace).
 size_t prune_ws_bytes(int64_t total_L, int nseq, int n_sets);
 hipError_t launch_prune(const float* score, const uint8_t* modality, const int32_t* cu_len,
                         const int32_t* keep, const int32_t* cu_kept, int nseq, int64_t total_L,
