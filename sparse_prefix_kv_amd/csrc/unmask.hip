@@ -5,7 +5,8 @@
 //
 // One wave per sequence, one lane per block position (Lq <= 64).  The rank of
 // a masked position is the number of masked positions ahead of it in that
-// order, computed by broadcasting every lane's confidence in turn.
+// order, computed by broadcasting every lane's confidence in turn (readlane:
+// a scalar broadcast, no LDS round trip).
 #include "sprint_device.hpp"
 #include "sprint_internal.hpp"
 
@@ -22,8 +23,14 @@ __global__ __launch_bounds__(64) void unmask_kernel(const float* __restrict__ co
   const int i = threadIdx.x;
   const int64_t base = static_cast<int64_t>(s) * Lq;
   const bool valid = i < Lq;
-  const float c = valid ? conf[base + i] : 0.f;
-  const bool msk = valid && masked[base + i] != 0;
+  // Every lane loads (a lane past Lq reads position Lq - 1 and ignores it),
+  // so the three loads are in flight together.
+  const int64_t at = base + (valid ? i : Lq - 1);
+  const float c_ld = conf[at];
+  const uint8_t m_ld = masked[at];
+  const int32_t a_ld = argmax[at];
+  const float c = valid ? c_ld : 0.f;
+  const bool msk = valid && m_ld != 0;
   const uint64_t bal_m = __ballot(msk);
   const uint64_t bal_hi = __ballot(msk && c > tau);
   const int m = __popcll(bal_m);
@@ -34,14 +41,19 @@ __global__ __launch_bounds__(64) void unmask_kernel(const float* __restrict__ co
     q = ceil_q < m ? static_cast<int>(ceil_q) : m;
   }
   const int count = n_hi > q ? n_hi : q;
+  // rank = masked positions ahead in (confidence desc, position asc).  An
+  // unmasked lane (lanes past Lq included) broadcasts -inf, which is neither
+  // above nor equal to any finite confidence, so all 64 lanes are visited
+  // without a branch.
+  const float ck = msk ? c : -INFINITY;
   int rank = 0;
-  for (int j = 0; j < Lq; ++j) {
-    const float cj = __shfl(c, j, 64);
-    const bool mj = (bal_m >> j) & 1ull;
-    if (mj && (cj > c || (cj == c && j < i))) ++rank;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    const float cj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ck), j));
+    rank += (cj > c || (cj == c && j < i)) ? 1 : 0;
   }
   if (msk && rank < count) {
-    tokens[base + i] = argmax[base + i];
+    tokens[base + i] = a_ld;
     masked[base + i] = 0;
   }
   if (i == 0) n_accepted[s] = count;
