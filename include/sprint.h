@@ -193,7 +193,9 @@ int sprint_prune_kv_per_layer(const float* score, const uint8_t* modality, const
  *   Q      [nseq, Lq, Hq, D] dtype
  *   Kp, Vp [total_kv, Hkv, D] dtype, sequences packed by cu_kv [nseq+1]
  *          (full cache, or the pruned cache of sprint_prune_kv)
- *   max_kv host upper bound on any sequence's cache length (sizes the KV split)
+ *   max_kv host upper bound on any sequence's cache length (sizes the KV split);
+ *          with nseq = 1 the one cache is all total_kv rows, so total_kv >
+ *          max_kv is SPRINT_EINVAL
  *   Kb, Vb [nseq, Lq, Hkv, D] dtype, or both NULL for prefix-only attention
  *   scale  softmax scale, finite and > 0 (usually 1/sqrt(D))
  *   O      [nseq, Lq, Hq, D] dtype out (bf16 rounded to nearest even)

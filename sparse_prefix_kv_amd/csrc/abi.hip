@@ -231,6 +231,8 @@ int block_attend(const void* Q, int32_t nseq, int32_t Lq, int32_t Hq, const void
   if (ss != SPRINT_OK) return ss;
   if (total_kv < 0 || total_kv > INT32_MAX || !isfinite(scale) || !(scale > 0.f))
     return SPRINT_EINVAL;
+  // one sequence's cache is all of [0, total_kv), which max_kv must cover
+  if (nseq == 1 && total_kv > max_kv) return SPRINT_EINVAL;
   if (!dev16(Q) || !dev16(O) || !dev4(cu_kv)) return SPRINT_EINVAL;
   if ((Kb == nullptr) != (Vb == nullptr)) return SPRINT_EINVAL;
   if (Kb != nullptr && (!dev16(Kb) || !dev16(Vb))) return SPRINT_EINVAL;

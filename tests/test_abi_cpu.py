@@ -140,6 +140,8 @@ def test_attend_and_unmask_reject_before_hip():
     assert _call("block_attend", *a) == 1                           # no keys at all
     a = list(at); a[13] = 0.0
     assert _call("block_attend", *a) == 1                           # scale must be > 0
+    a = list(at); a[8] = 4095
+    assert _call("block_attend", *a) == 1                           # one sequence longer than max_kv
     a = list(at); a[17] = 8
     assert _call("block_attend", *a) == 3
     um = [FAKE, FAKE, 1, 32, 0.9, 9, FAKE, FAKE, FAKE, None]
