@@ -288,3 +288,16 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, cwd=root, timeout=120)
     assert r.returncode != 0
     assert "--gpus 2" in r.stderr and "single" in r.stderr
+
+
+def test_committed_traffic_counters_match_the_kernel_source():
+    """profiles/traffic.json names the source its counters were taken on; a
+    change to that source without new counters makes bench.py report no
+    traffic, so the committed pair must agree."""
+    import hashlib
+    tj = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    for name, ent in tj.items():
+        src = open(os.path.join(ROOT, ent["source"]), "rb").read()
+        assert hashlib.sha256(src).hexdigest()[:16] == ent["source_sha"], name
+        assert ent["hbm_bytes_per_launch"] > 0
+        assert os.path.exists(os.path.join(ROOT, ent["summary"]))
