@@ -198,8 +198,17 @@ def lmhead_confidence(X, W):
 
 
 def lmhead_top2_gap(X, W) -> np.ndarray:
-    """Gap between the largest and second-largest logit of each row (fp64)."""
+    """z* minus the second largest logit of each row, fp64 (0 when the maximum
+    is attained twice; V = 1 has no runner-up and gives +inf).
+
+    Where this gap is below the GPU's fp32 rounding of the logits, two
+    vocabulary entries are equally valid argmaxes of Sparse Prefix
+    Retention's c_i = max_v p (the confidence is the same either way), so the
+    parity tests excuse an argmax mismatch only there.
+    """
     Z = np.asarray(X, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T
+    if Z.shape[1] < 2:
+        return np.full(Z.shape[0], np.inf)
     part = np.partition(Z, Z.shape[1] - 2, axis=1)
     return part[:, -1] - part[:, -2]
 
@@ -276,8 +285,7 @@ class BlockResult:
 
 
 def run_block(Q, K, V, Kb, Vb, hidden, W, cu_len, modality, r_text, r_img,
-              tau, T: Optional[int], n_steps: int, alpha: float = 0.5,
-              pass_rows: Optional[np.ndarray] = None, moe=None,
+              tau, T: Optional[int], n_steps: int, alpha: float = 0.5, moe=None,
               store_dtype: Optional[str] = None) -> BlockResult:
     """The SPRINT block as one composition (Sparse Prefix Retention +
     Non-uniform Token Unmasking).
@@ -287,8 +295,6 @@ def run_block(Q, K, V, Kb, Vb, hidden, W, cu_len, modality, r_text, r_img,
     compact the pruned cache.  Steps t = 1..n_steps attend to the pruned cache.
     Q, Kb, Vb stay fixed across steps (the model that would refresh them is
     not part of this path).  T = None means at least one acceptance per step.
-    `pass_rows` restricts the prefix LM head to those rows (others get conf 0)
-    for large sizes; None computes all of them.
     `moe` = (w_router, bias, w_gate, w_up, w_down, top_k, route_scale) puts an
     MoE FFN between attention and the LM head: the LM head reads
     O + moe_ffn(O), with O stored in `store_dtype` first (the workload's
@@ -296,12 +302,7 @@ def run_block(Q, K, V, Kb, Vb, hidden, W, cu_len, modality, r_text, r_img,
     """
     nseq, Lq, Hq, D = np.asarray(Q).shape
     cu = np.asarray(cu_len, dtype=np.int64)
-    if pass_rows is None:
-        conf_prefix, _, _ = lmhead_confidence(hidden, W)
-    else:
-        conf_prefix = np.zeros(cu[-1])
-        c, _, _ = lmhead_confidence(np.asarray(hidden)[pass_rows], W)
-        conf_prefix[pass_rows] = c
+    conf_prefix, _, _ = lmhead_confidence(hidden, W)
     ibar = key_norm_importance(K, cu)
     score = composite_score(ibar, conf_prefix, alpha)
     keep = np.zeros((nseq, 2), dtype=np.int64)

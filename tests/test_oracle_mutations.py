@@ -6,7 +6,9 @@ against that copy; the pins must fail.  The mistakes are the kinds a reader
 could make transcribing the pages: a wrong GQA index, scale or norm, the
 wrong tie-break, >= for the strict threshold, swapped blend weights, a floor
 for a ceiling, a dropped term, a wrong offset, truncation for round-to-even,
-a sum for a mean, a missing bias, gate scale or SwiGLU factor.  The unmutated
+a sum for a mean, a missing bias, gate scale or SwiGLU factor, a top-2
+gap taken to the smallest logit, to the next distinct logit or over
+probabilities.  The unmutated
 copy must pass, so a failure is the mistake's, not the harness's.
 """
 import os
@@ -57,6 +59,16 @@ MUTATIONS = {
     "swiglu_swapped": ("return (silu(g) * u) @ np.asarray(w_down, dtype=np.float64).T",
                        "return (g * silu(u)) @ np.asarray(w_down, dtype=np.float64).T"),
     "moe_no_gate": ("y[t] += gates[t, j] * expert_ffn(", "y[t] += expert_ffn("),
+    "top2_gap_max_minus_min": ("return part[:, -1] - part[:, -2]",
+                               "return part[:, -1] - part[:, 0]"),
+    "top2_gap_distinct_runner_up": (
+        "return part[:, -1] - part[:, -2]",
+        "return part[:, -1] - np.where(part[:, -2] == part[:, -1], part[:, -3], part[:, -2])"),
+    "top2_gap_probabilities": (
+        "Z = np.asarray(X, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T\n    if Z.shape[1] < 2:",
+        "Z = np.asarray(X, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T\n"
+        "    Z = np.exp(Z - Z.max(axis=1, keepdims=True))\n    Z /= Z.sum(axis=1, keepdims=True)\n"
+        "    if Z.shape[1] < 2:"),
 }
 
 

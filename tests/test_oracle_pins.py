@@ -312,6 +312,46 @@ def test_lmhead_tie_goes_to_lowest_index_and_bounds():
     assert np.all(np.isfinite(c2))
 
 
+def test_lmhead_top2_gap_hand_examples():
+    # logits z = x * w: [0, 1, 3, 2.5] -> the runner-up is 2.5, gap 0.5
+    X = np.array([[1.0], [2.0]])
+    W = np.array([[0.0], [1.0], [3.0], [2.5]])
+    np.testing.assert_allclose(oracle.lmhead_top2_gap(X, W), [0.5, 1.0], rtol=0, atol=1e-15)
+    # a maximum attained twice has gap 0 (both entries are valid argmaxes)
+    W2 = np.array([[0.0], [math.log(3)], [math.log(2)], [math.log(3)]])
+    np.testing.assert_array_equal(oracle.lmhead_top2_gap(X, W2), [0.0, 0.0])
+    # a one-word vocabulary has no runner-up
+    assert np.all(np.isinf(oracle.lmhead_top2_gap(X, np.array([[1.0]]))))
+
+
+@pytest.mark.parametrize("gamma,beta", [(5.0, 2.0), (1.0, -3.0), (0.25, 0.25)])
+def test_lmhead_top2_gap_planted_closed_form(gamma, beta):
+    # x = e_0; W row 11 = gamma e_0, row 40 = beta e_0, every other row 0:
+    # the logits are {gamma, beta, 0, ..., 0}, so the gap is gamma - max(beta, 0)
+    V, H = 64, 5
+    X = np.zeros((1, H)); X[0, 0] = 1.0
+    W = np.zeros((V, H)); W[11, 0] = gamma; W[40, 0] = beta
+    np.testing.assert_allclose(oracle.lmhead_top2_gap(X, W), [gamma - max(beta, 0.0)],
+                               rtol=0, atol=1e-15)
+
+
+def test_lmhead_top2_gap_brute_force():
+    rng = np.random.default_rng(21)
+    X = rng.standard_normal((6, 7))
+    W = np.round(rng.standard_normal((9, 7)), 1)
+    W[5] = W[2]                    # duplicate vocabulary rows: ties in every row
+    gap = oracle.lmhead_top2_gap(X, W)
+    for i in range(X.shape[0]):
+        z = sorted((sum(X[i, h] * W[v, h] for h in range(7)) for v in range(9)), reverse=True)
+        assert abs(gap[i] - (z[0] - z[1])) <= 1e-12
+    # the gap is the distance the argmax's logit leads every other entry by
+    Z = X @ W.T
+    a = Z.argmax(axis=1)
+    for i in range(X.shape[0]):
+        others = np.delete(Z[i], a[i])
+        assert abs(gap[i] - (Z[i, a[i]] - others.max())) <= 1e-12
+
+
 # -------------------------------------------------------------------- unmask
 
 def _brute_unmask(conf, masked, tau, steps_left):
