@@ -186,21 +186,29 @@ int sprint_prune_kv_per_layer(const float* score, const uint8_t* modality, const
                               size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
- * Block attention of a denoising step: the block's queries attend, without a
- * mask, to [prefix cache ; the block's own keys] (the block is predicted from
- * the clean prefix and its own noisy tokens).  With GQA, query head h reads
- * KV head floor(h*Hkv/Hq).  O = softmax(Q K^T * scale) V per (sequence, head).
+ * Block attention of a denoising step (LLaDA2.0-Uni: "Sparse Prefix
+ * Retention" -- the block's first step attends to the full prefix cache and
+ * every later step to the pruned one; "BDLM Loss" -- a block is predicted
+ * from the clean earlier blocks and its own noisy tokens, so the block's own
+ * keys join the context, without a mask inside the block).  With GQA, query
+ * head h reads KV head floor(h*Hkv/Hq).  O = softmax(Q K^T * scale) V per
+ * (sequence, head) over the keys [prefix cache ; block].
  *   Q      [nseq, Lq, Hq, D] dtype
  *   Kp, Vp [total_kv, Hkv, D] dtype, sequences packed by cu_kv [nseq+1]
  *          (full cache, or the pruned cache of sprint_prune_kv)
- *   max_kv host upper bound on any sequence's cache length (sizes the KV split);
- *          with nseq = 1 the one cache is all total_kv rows, so total_kv >
- *          max_kv is SPRINT_EINVAL
+ *   max_kv host estimate of the longest sequence's cache length; it sizes the
+ *          split of each cache into key ranges (and so the workspace).  A
+ *          longer sequence is still attended in full (its last key range
+ *          covers the rest; only slower).  With nseq = 1 the one cache is all
+ *          total_kv rows, so total_kv > max_kv is SPRINT_EINVAL there
  *   Kb, Vb [nseq, Lq, Hkv, D] dtype, or both NULL for prefix-only attention
  *   scale  softmax scale, finite and > 0 (usually 1/sqrt(D))
  *   O      [nseq, Lq, Hq, D] dtype out (bf16 rounded to nearest even)
  * Supports D in {64, 128}, Hq % Hkv == 0, (Hq/Hkv)*Lq <= 256, Lq <= 64.
  * Every (sequence) must have at least one key (cache length + block >= 1).
+ * Partial results of key ranges are kept in ws in fp32 (fp32 inputs) or in
+ * fp16 with a power-of-two scale per row (bf16 inputs), so every finite bf16
+ * value is in range; products that overflow fp32 are out of range.
  * ------------------------------------------------------------------------ */
 size_t block_attend_ws(int32_t nseq, int32_t Lq, int32_t Hq, int32_t Hkv, int32_t D,
                        int32_t max_kv, int32_t has_block);

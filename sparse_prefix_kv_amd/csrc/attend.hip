@@ -33,8 +33,11 @@
 //   c ^ 4*(r & 3) (c ^ 4*((r >> 1) & 1) for 128-byte rows) so the four rows of
 //   a transposing-read pass land on disjoint banks.
 // A single key range writes O directly; otherwise each wave writes its rows'
-//   partial (o / l in fp16 for bf16 inputs, fp32 otherwise, plus m and l in
-//   log2 units) and a combine kernel merges the ranges.
+//   partial (o / l in fp32 for fp32 inputs; for bf16 inputs in fp16 times a
+//   power-of-two row scale that keeps every row in fp16's range, plus m in
+//   log2 units, l and the scale) and a combine kernel merges the ranges.  The
+//   last range of a sequence runs to its end, so a sequence longer than the
+//   planned cache length is still attended in full.
 #include <math.h>
 
 #include <type_traits>
@@ -60,8 +63,8 @@ struct AttnArgs {
   const char* Kb;
   const char* Vb;
   char* O;
-  void* part_o;    // [nseq*Hkv*n_splits*R, D] fp16 (bf16 inputs) or fp32, normalized by l
-  float* part_ml;  // [nseq*Hkv*n_splits*R, 2]  (m in log2 units, l)
+  void* part_o;    // [nseq*Hkv*n_splits*R, D] fp16 (bf16 inputs) or fp32: o / l, times 2^-e
+  float* part_ml;  // [nseq*Hkv*n_splits*R, 4]  (m in log2 units, l, 2^e, unused)
   int nseq, Lq, Hq, Hkv, G, R, n_splits, kps, has_block, n_rg;
   int64_t total_kv;
   float scale_log2;
@@ -292,7 +295,9 @@ void attend_split_kernel(AttnArgs args) {
   const int kv_len = args.cu_kv[seq + 1] - args.cu_kv[seq];
   const int n_keys = kv_len + (args.has_block ? args.Lq : 0);
   const int k0 = min(n_keys, split * args.kps);
-  const int k1 = min(n_keys, k0 + args.kps);
+  // the last range runs to the sequence's end, whatever the planned length,
+  // so a sequence longer than the plan assumed is covered (only slower)
+  const int k1 = split == args.n_splits - 1 ? n_keys : min(n_keys, k0 + args.kps);
   // tiles: the range's prefix keys [pk0, pk1), then its block keys [bk0, bk1)
   const int pk0 = min(k0, kv_len), pk1 = min(k1, kv_len);
   const int bk0 = max(k0, kv_len) - kv_len, bk1 = max(k1, kv_len) - kv_len;
@@ -541,15 +546,34 @@ void attend_split_kernel(AttnArgs args) {
       });
     return;
   }
+  // Partial rows.  fp16 partials (bf16 inputs) carry a power-of-two row scale
+  // 2^e chosen so the row's largest |o| lands in [2^14, 2^15): fp16's full
+  // precision at any magnitude bf16 values can take, and no overflow.
+  float pscale = 1.f, pmul = 1.f;
+  if constexpr (kBf16) {
+    float mx = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fabsf(acc_o[mt][r]));
+    mx = pair_max(mx * inv);
+    int e = 0;
+    if (mx > 0.f) {
+      e = static_cast<int>((__float_as_uint(mx) >> 23) & 255u) - 127 - 14;
+      e = e < -100 ? -100 : (e > 100 ? 100 : e);
+    }
+    pscale = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);   // 2^-e
+    pmul = __uint_as_float(static_cast<uint32_t>(127 + e) << 23);     // 2^e
+  }
   const int64_t pbase =
       ((static_cast<int64_t>(seq) * args.Hkv + g) * args.n_splits + split) * args.R + rw * 32;
-  stage_rows<PE, D>(reg, acc_o, inv, q, hh);
+  stage_rows<PE, D>(reg, acc_o, inv * pscale, q, hh);
   __syncthreads();
   flush_rows<PE, D>(reg, lane, nrows, [&](int rr) {
     return static_cast<char*>(args.part_o) + (pbase + rr) * static_cast<int64_t>(D * sizeof(PE));
   });
   if (hh == 0 && row_ok)
-    *reinterpret_cast<float2*>(args.part_ml + (pbase + q) * 2) = make_float2(m_run, l_tot);
+    *reinterpret_cast<f32x4*>(args.part_ml + (pbase + q) * 4) = f32x4{m_run, l_tot, pmul, 0.f};
 }
 
 // Combine the key ranges: one wave per output row (of one sequence and KV
@@ -581,16 +605,17 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttnArgs args) {
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = 0.f;
   for (int base = sg; base < args.n_splits; base += kSG * kNB) {
-    float ms[kNB], ls[kNB], v[kNB][8];
+    float ms[kNB], ls[kNB], mul[kNB], v[kNB][8];
 #pragma unroll
     for (int u = 0; u < kNB; ++u) {
       const int sp = base + kSG * u;
       const bool ok = sp < args.n_splits;
       const int64_t prow = row0 + static_cast<int64_t>(ok ? sp : 0) * rstride;
-      const float2 ml = ok ? *reinterpret_cast<const float2*>(args.part_ml + prow * 2)
-                           : make_float2(-INFINITY, 0.f);
-      ms[u] = ml.x;
-      ls[u] = ml.y;
+      const f32x4 ml = ok ? *reinterpret_cast<const f32x4*>(args.part_ml + prow * 4)
+                          : f32x4{-INFINITY, 0.f, 0.f, 0.f};
+      ms[u] = ml[0];
+      ls[u] = ml[1];
+      mul[u] = ml[2];
       if constexpr (kBf16) {
         const u32x4 h = ok ? ld16(static_cast<const half_t*>(args.part_o) + prow * D + d)
                            : u32x4{0u, 0u, 0u, 0u};
@@ -620,8 +645,9 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttnArgs args) {
     for (int u = 0; u < kNB; ++u) {
       const float w = ms[u] == -INFINITY ? 0.f : ls[u] * exp2f(ms[u] - mb);
       l += w;
+      const float wv = w * mul[u];               // undo the partial's row scale
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] = fmaf(w, v[u][c], acc[c]);
+      for (int c = 0; c < 8; ++c) acc[c] = fmaf(wv, v[u][c], acc[c]);
     }
     m = mb;
   }
@@ -710,7 +736,7 @@ AttnPlan attend_plan(int nseq, int Lq, int Hq, int Hkv, int D, int max_kv, int h
   const size_t parts = static_cast<size_t>(units) * p.n_splits * p.rows;
   p.ws_bytes = p.n_splits == 1 ? 0
                                : align_up(parts * D * es, 256) +
-                                     align_up(parts * 2 * sizeof(float), 256);
+                                     align_up(parts * 4 * sizeof(float), 256);
   return p;
 }
 

@@ -33,7 +33,7 @@ hipError_t launch_prune(const float* score, const uint8_t* modality, const int32
 
 // ---- block attention (split-KV + combine)
 struct AttnPlan {
-  int kps;         // keys per split (multiple of the key tile)
+  int kps;         // keys per split (the last split of a sequence runs to its end)
   int n_splits;    // splits per (sequence, KV head)
   int rows;        // query rows per KV head = (Hq/Hkv) * Lq
   size_t ws_bytes;
