@@ -105,6 +105,29 @@ def test_lmhead_full_size_sampled(M, V):
     _check_lmhead(X, W, _np(conf), _np(amax), _np(lse), rows)
 
 
+@pytest.mark.parametrize("M,V", [(32768, 163840), (76375, 65536)])
+def test_lmhead_prefix_large_sampled(M, V):
+    """The prefix-wide LM head at the long-prefix shapes: 32768 prefix rows
+    over a 163840-word vocabulary (128 x 640 tiles of the XCD-grouped GEMM),
+    and the 8-sequence ragged prefix of 76375 rows (a ragged last token tile)
+    over 65536 words.  Both tails, both sides of tile edges and random rows,
+    72 in all, against the oracle: confidence, argmax and log-sum-exp."""
+    H = 2048
+    X = synth.normal_array((M, H), 33, 1.0, "bf16")
+    W = synth.normal_array((V, H), 34, 0.02, "bf16")
+    conf, amax, lse = sprint.lmhead_confidence(_to_dev(X, "bf16", DEV), _to_dev(W, "bf16", DEV),
+                                               want_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M ^ V)
+    edges = [0, 1, 2, 3, 255, 256, 257, 2047, 2048, M // 2, M - 257, M - 256, M - 5, M - 4,
+             M - 3, M - 2, M - 1]
+    rows = np.unique(np.concatenate([edges, rng.integers(0, M, size=72 - len(edges))]))
+    while len(rows) < 72:
+        rows = np.unique(np.concatenate([rows, rng.integers(0, M, size=72 - len(rows))]))
+    assert len(rows) >= 64
+    _check_lmhead(X, W, _np(conf), _np(amax), _np(lse), rows)
+
+
 # ============================================================ score
 
 def _check_score(K, conf, cu, dtype, Hkv, D, alpha=0.5):
@@ -255,6 +278,55 @@ def test_attend_full_size(kv_lens):
     _attend_case("bf16", 16, 4, 128, 32, kv_lens, True, 80)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attend_max_kv_below_a_sequence(dtype):
+    """max_kv only sizes the split of each cache: with three sequences, two of
+    them longer than the max_kv given, every key is still attended (the last
+    key range of a sequence runs to its end)."""
+    kv_lens = [5000, 300, 9000]
+    nseq, Lq, Hq, Hkv, D = 3, 32, 16, 4, 128
+    cu = np.concatenate([[0], np.cumsum(kv_lens)]).astype(np.int32)
+    Q = synth.normal_array((nseq, Lq, Hq, D), 90, 1.0, dtype)
+    Kp = synth.normal_array((cu[-1], Hkv, D), 91, 1.0, dtype)
+    Vp = synth.normal_array((cu[-1], Hkv, D), 92, 1.0, dtype)
+    Kb = synth.normal_array((nseq, Lq, Hkv, D), 93, 1.0, dtype)
+    Vb = synth.normal_array((nseq, Lq, Hkv, D), 94, 1.0, dtype)
+    O_o = oracle.attention(Q, Kp, Vp, cu, Kb, Vb)
+    tol = 2e-2 if dtype == "bf16" else 1e-5
+    for max_kv in (1000, 200, 9000):
+        O = sprint.block_attend(_to_dev(Q, dtype, DEV), _to_dev(Kp, dtype, DEV),
+                                _to_dev(Vp, dtype, DEV), _i32(cu), max_kv,
+                                _to_dev(Kb, dtype, DEV), _to_dev(Vb, dtype, DEV))
+        err = np.max(np.abs(_np(O) - O_o))
+        assert err <= tol, (max_kv, err)
+
+
+@pytest.mark.parametrize("kv_lens", [[27852], [3000, 700]])
+def test_attend_value_scale_is_exact_across_splits(kv_lens):
+    """bf16 V of any magnitude: scaling V by a power of two scales O by it
+    bit for bit, through the key-range partials and their combine, from
+    values far past fp16's range (2^17 * N(0,1)) down to 2^-60.  The unscaled
+    call matches the oracle."""
+    nseq, Lq, Hq, Hkv, D = len(kv_lens), 32, 16, 4, 128
+    cu = np.concatenate([[0], np.cumsum(kv_lens)]).astype(np.int32)
+    Q = synth.normal_array((nseq, Lq, Hq, D), 95, 1.0, "bf16")
+    Kp = synth.normal_array((cu[-1], Hkv, D), 96, 1.0, "bf16")
+    Vp = synth.normal_array((cu[-1], Hkv, D), 97, 1.0, "bf16")
+    Kb = synth.normal_array((nseq, Lq, Hkv, D), 98, 1.0, "bf16")
+    Vb = synth.normal_array((nseq, Lq, Hkv, D), 99, 1.0, "bf16")
+    args = [_to_dev(a, "bf16", DEV) for a in (Q, Kp, Vp)]
+    Kb_d, Vb_d = _to_dev(Kb, "bf16", DEV), _to_dev(Vb, "bf16", DEV)
+    O1 = sprint.block_attend(args[0], args[1], args[2], _i32(cu), max(kv_lens), Kb_d, Vb_d)
+    O_o = oracle.attention(Q, Kp, Vp, cu, Kb, Vb)
+    assert np.max(np.abs(_np(O1) - O_o)) <= 2e-2
+    for e in (17, 30, -60):
+        f = 2.0 ** e
+        Ob = sprint.block_attend(args[0], args[1], args[2] * f, _i32(cu), max(kv_lens), Kb_d,
+                                 Vb_d * f)
+        assert torch.isfinite(Ob.float()).all()
+        assert torch.equal(Ob, (O1.float() * f).to(torch.bfloat16)), e
+
+
 def test_attend_full_retention_equals_unpruned():
     x = synth.make_inputs(synth.WORKLOADS["single4k"], 0, with_lmhead=False)
     lay = x.layout
@@ -381,6 +453,14 @@ def test_block_single4k_composition():
                            wl.r_text, wl.r_img, np.float32(wl.tau), wl.T, 1)
     kept = _compare_block(blk, res, 1, 2e-2)
     assert len(kept) == 3481
-    if np.array_equal(kept, res.kept_idx):
-        assert np.max(np.abs(_np(blk.O) - res.outputs[1])) <= 2e-2
+    # the kept set from the GPU's own scores is the oracle's, bit for bit
+    keep = np.array([[oracle.keep_count(wl.r_text, lay.n_text[0]),
+                      oracle.keep_count(wl.r_img, lay.n_img[0])]])
+    want = oracle.select_kept(_np(blk.score), lay.modality, lay.cu_len, keep)
+    np.testing.assert_array_equal(kept, want)
+    # the last pruned step's attention over the GPU's kept rows (every pruned
+    # step attends to the same cache with the same queries)
+    Kp, Vp = oracle.compact(x.K, x.V, kept)
+    O_o = oracle.attention(x.Q, Kp, Vp, [0, len(kept)], x.Kb, x.Vb)
+    assert np.max(np.abs(_np(blk.O) - O_o)) <= 2e-2
     assert int(blk.masked.sum()) == 0          # the 9-step budget finishes the block

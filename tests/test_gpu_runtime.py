@@ -136,3 +136,80 @@ def test_two_blocks_on_two_streams_match_serial_runs():
         torch.cuda.synchronize()
         for b, r in zip(blks, ref):
             assert all(torch.equal(u, v) for u, v in zip(state(b), r))
+
+
+@pytest.mark.parametrize("name", ["tiny", "single4k"])
+def test_block_graph_replay_matches_oracle(name):
+    """A whole block (pruning pass + every pruned step) captured as one HIP
+    graph and replayed: after each replay, every stage it leaves behind is
+    checked against the oracle fed that stage's GPU inputs (prefix
+    confidences on sampled rows, scores, the kept set bit for bit, the pruned
+    cache, the last step's attention and confidences, the last unmask)."""
+    import oracle
+    x = synth.make_inputs(synth.WORKLOADS[name], 0)
+    wl, lay = x.wl, x.layout
+    blk = SprintBlock(x, DEV)
+    n_steps = (blk.T - 1) if blk.T is not None else 6
+    tol = 1e-5 if wl.dtype == "f32" else 2e-2
+
+    def last_step():
+        blk.attend(pruned=True)
+        blk.block_confidence()
+
+    def run():
+        blk.run_block(n_steps - 1)
+        last_step()
+        blk.unmask(n_steps)
+
+    run()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        blk.run_block(n_steps - 1)
+        last_step()
+    keep = np.array([[oracle.keep_count(blk.r_text, lay.n_text[i]),
+                      oracle.keep_count(blk.r_img, lay.n_img[i])] for i in range(lay.nseq)])
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, lay.total_L - 1],
+                                     rng.integers(0, lay.total_L, size=30)]))
+    c_o, _, _ = oracle.lmhead_confidence(x.hidden[rows], x.W)
+    for rep in range(3):
+        blk.tokens.fill_(-7)                     # eager work between replays
+        blk.O.zero_()
+        blk.score.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        cp = blk.conf_prefix.cpu().numpy()
+        np.testing.assert_allclose(cp[rows], c_o, rtol=1e-4, atol=1e-7)
+        sc = blk.score.cpu().numpy()
+        sc_o = oracle.composite_score(oracle.key_norm_importance(x.K, lay.cu_len), cp, blk.alpha)
+        np.testing.assert_allclose(sc, sc_o, rtol=1e-5, atol=1e-7)
+        kept = blk.kept_idx.cpu().numpy().astype(np.int64)
+        np.testing.assert_array_equal(kept, oracle.select_kept(sc, lay.modality, lay.cu_len, keep))
+        Kp, Vp = oracle.compact(x.K, x.V, kept)
+        O_o = oracle.attention(x.Q, Kp, Vp, blk.cu_kept.cpu().numpy(), x.Kb, x.Vb)
+        O_g = blk.O.float().cpu().numpy()
+        assert np.max(np.abs(O_g - O_o)) <= tol, rep
+        c_g = blk.conf_blk.cpu().numpy()
+        c_b, a_b, _ = oracle.lmhead_confidence(O_g.reshape(lay.nseq * wl.Lq, -1), x.W)
+        np.testing.assert_allclose(c_g, c_b, rtol=1e-4, atol=1e-7)
+        gap = oracle.lmhead_top2_gap(O_g.reshape(lay.nseq * wl.Lq, -1), x.W)
+        a_g = blk.argmax_blk.cpu().numpy()
+        assert np.all((a_g == a_b) | (gap <= 1e-4))
+        # the last unmask step, eager, from the replayed state
+        m0, t0 = blk.masked.cpu().numpy(), blk.tokens.cpu().numpy()
+        blk.unmask(n_steps)
+        torch.cuda.synchronize()
+        m_o, t_o, _ = oracle.unmask_select(c_g.reshape(lay.nseq, -1), a_g.reshape(lay.nseq, -1),
+                                           m0, t0, np.float32(blk.tau), blk.steps_left(n_steps))
+        np.testing.assert_array_equal(blk.masked.cpu().numpy(), m_o)
+        np.testing.assert_array_equal(blk.tokens.cpu().numpy(), t_o)
+        assert int(blk.masked.sum()) == 0 or blk.T is None
+    del g
