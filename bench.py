@@ -5,9 +5,10 @@ One benchmark step is one whole SPRINT block over one batch of synthetic
 input: the pruning pass (prefix LM-head confidence, key-norm score,
 per-modality top-k, compaction, full-prefix attention, block confidence,
 unmasking) followed by the pruned denoising steps (attention over the pruned
-cache, block confidence, unmasking).  The default workload is the bf16
-single-sequence prefix of 4096 positions (1024 text + 3072 image), 16/4
-heads of dim 128, vocabulary 32768, pass + 8 steps.
+cache, block confidence, unmasking).  The default workload is the largest
+single-GPU one: a bf16 prefix of 32768 positions in 8 alternating text/image
+runs (1024 + 3072 each), 16/4 heads of dim 128, vocabulary 163840, pass + 8
+steps, r_img = 0.8 against full retention.
 
 Printed: one JSON line.  `value` is denoising block-steps per second
 (1 pass + 8 pruned steps = 9 block-steps per block and sequence): the faster
@@ -17,9 +18,11 @@ eagerly from the host; `timing` names which.  The same line carries both
 rates, the full-retention baseline, per-call GPU times (each call captured
 20 times back to back in a graph, HIP events around 11 replays on the stream
 it runs on: median, 10th and 90th percentile of the per-launch means; and
-cache-flushed single calls), the roofline of the dominant call, torch.mm on
+cache-flushed single calls), the roofline of the dominant call, the
+image-generation-shaped prefix (16384 positions) pruned against full, the
+step counts of a block whose confidences are planted above tau, torch.mm on
 the prefix GEMM's shape as a library yardstick, and the CPU oracle timed on
-the host.
+the host (measured on a bounded sample and extrapolated to one block).
 """
 from __future__ import annotations
 
@@ -49,10 +52,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50, help="timed blocks")
     ap.add_argument("--warmup", type=int, default=5, help="untimed blocks")
-    ap.add_argument("--workload", default="single4k")
+    ap.add_argument("--workload", default="interleaved32k")
     ap.add_argument("--cold-iters", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=10)
+    ap.add_argument("--compare", default="imggen16k",
+                    help="second workload timed pruned against full in the same line ('' to skip)")
+    ap.add_argument("--no-planted", action="store_true",
+                    help="skip the planted-confidence step-count measurement")
     ap.add_argument("--gen-blocks", type=int, default=8,
                     help="blocks of the generation measurement (0: skip it)")
     ap.add_argument("--layers", type=int, default=16,
@@ -133,38 +139,102 @@ def src_sha(relpath):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(call):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source."""
+def load_traffic(call, workload):
+    """HBM bytes per launch of `call` on `workload` from committed rocprofv3
+    counter runs, if they were taken on the current kernel source; None
+    otherwise (another workload's counters are never reused)."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    ent = t.get(call)
-    if not ent or ent.get("source_sha") != src_sha(ent["source"]):
+    ent = t.get(f"{call}@{workload}")
+    if not ent or ent.get("workload") != workload or ent.get("source_sha") != src_sha(ent["source"]):
         return None
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(x, wl, n_blocks):
-    import numpy as np
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x, wl, n_steps):
+    """The oracle on the host, on a bounded sample of one block of the same
+    workload, extrapolated to the whole block.
+
+    Timed in full, once each: the scoring, top-k and compaction of the whole
+    prefix; attention over the full prefix and over the pruned cache; the
+    block's LM head (32 rows per sequence); one unmask step.  The prefix-wide
+    LM head is timed on two seeded row samples and extrapolated linearly to
+    every prefix row (a fixed part per call, converting W, plus a part per
+    row).  Block time = prefix LM head + scoring/pruning + full attention +
+    (steps + 1) x (LM head + unmask) + steps x pruned attention."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        cores = max(i["num_threads"] for i in threadpool_info()) if threadpool_info() else 1
+        info = threadpool_info()
+        cores = max(i["num_threads"] for i in info) if info else 1
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
     lay = x.layout
-    t0 = time.perf_counter()
-    for _ in range(n_blocks):
-        oracle.run_block(x.Q, x.K, x.V, x.Kb, x.Vb, x.hidden, x.W, lay.cu_len, lay.modality,
-                         wl.r_text, wl.r_img, np.float32(wl.tau), wl.T, wl.T - 1)
-    dt = time.perf_counter() - t0
-    steps = n_blocks * wl.T * lay.nseq
-    return {"value": steps / dt, "unit": "block-steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n_blocks} whole block(s) of the same workload (pass + {wl.T - 1} steps), "
-                      f"fp64 NumPy, {dt:.2f} s"}
+    nseq, Lq, L = lay.nseq, wl.Lq, int(lay.total_L)
+    rng = np.random.default_rng(1)
+    t = {}
+
+    def timed(name, fn):
+        t0 = time.perf_counter()
+        r = fn()
+        t[name] = time.perf_counter() - t0
+        return r
+    n1, n2 = min(L, 256), min(L, 1024)
+    rows2 = np.sort(rng.choice(L, n2, replace=False))
+    c_s, _, _ = timed("lm_rows_a", lambda: oracle.lmhead_confidence(x.hidden[rows2[:n1]], x.W))
+    c_s2, _, _ = timed("lm_rows_b", lambda: oracle.lmhead_confidence(x.hidden[rows2], x.W))
+    per_row = max(0.0, (t["lm_rows_b"] - t["lm_rows_a"]) / max(1, n2 - n1))
+    fixed = max(0.0, t["lm_rows_a"] - per_row * n1)
+    t_prefix_lm = fixed + per_row * L
+    # scores from sampled confidences: every row gets the median of the sample
+    conf = np.full(L, float(np.median(c_s2)))
+    keep = np.array([[oracle.keep_count(wl.r_text, lay.n_text[s]),
+                      oracle.keep_count(wl.r_img, lay.n_img[s])] for s in range(nseq)])
+    cu_kept = np.concatenate([[0], np.cumsum(keep.sum(1))])
+
+    def prune():
+        ib = oracle.key_norm_importance(x.K, lay.cu_len)
+        sc = oracle.composite_score(ib, conf, wl.alpha)
+        kept = oracle.select_kept(sc, lay.modality, lay.cu_len, keep)
+        return oracle.compact(x.K, x.V, kept)
+    Kp, Vp = timed("score_topk_compact", prune)
+    O = timed("attn_full", lambda: oracle.attention(x.Q, x.K, x.V, lay.cu_len, x.Kb, x.Vb))
+    timed("attn_pruned", lambda: oracle.attention(x.Q, Kp, Vp, cu_kept, x.Kb, x.Vb))
+    c, a, _ = timed("lm_block", lambda: oracle.lmhead_confidence(
+        O.reshape(nseq * Lq, -1), x.W))
+    masked = np.ones((nseq, Lq), np.uint8)
+    tokens = np.full((nseq, Lq), -1)
+    timed("unmask", lambda: oracle.unmask_select(c.reshape(nseq, Lq), a.reshape(nseq, Lq),
+                                                masked, tokens, np.float32(wl.tau), n_steps + 1))
+    block = (t_prefix_lm + t["score_topk_compact"] + t["attn_full"] +
+             (n_steps + 1) * (t["lm_block"] + t["unmask"]) + n_steps * t["attn_pruned"])
+    steps = (n_steps + 1) * nseq
+    measured = sum(t.values())
+    return {"value": steps / block, "unit": "block-steps/s", "cores": int(cores),
+            "kind": "oracle", "extrapolated": True,
+            "sample": (f"fp64 NumPy oracle, {measured:.1f} s measured: the prefix LM head on "
+                       f"{n1} and {n2} seeded prefix rows, extrapolated linearly to all {L} rows "
+                       f"({t_prefix_lm:.1f} s); scoring + top-k + compaction of the whole "
+                       f"prefix, full and pruned attention, the block LM head and one unmask "
+                       f"step timed once each; block = pass + {n_steps} pruned steps "
+                       f"({block:.1f} s)"),
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
+            "seconds": {k: round(v, 3) for k, v in t.items()} | {
+                "prefix_lm_extrapolated": round(t_prefix_lm, 2), "block": round(block, 2)}}
 
 
 def profile_call(args, blk, n_steps, torch):
@@ -498,6 +568,145 @@ def measure_moe(args, blk, x_in, wl, n_steps, torch, reps=20):
             "note": "weights are synthetic (N(0,1/H), N(0,1/I)); the page gives no expert sizes"}
 
 
+def call_us(torch, fn, reps=20, samples=11):
+    """Median per-launch GPU time (us) of fn: reps launches captured in one
+    graph, HIP events around each of `samples` replays."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(samples):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+    del g
+    return sorted(ts)[len(ts) // 2]
+
+
+def measure_compare(name, n_steps, torch, reps=10):
+    """A second workload in the same line: its block pruned (r_img of the
+    workload) against full retention (every step on the full prefix), its
+    attention call pruned against full, and one denoising step each way."""
+    from sparse_prefix_kv_amd import synth
+    from sparse_prefix_kv_amd.block import SprintBlock
+    wl = synth.WORKLOADS[name]
+    x = synth.make_inputs(wl, 0)
+    blk = SprintBlock(x, "cuda")
+    blk.run_block(n_steps)
+    torch.cuda.synchronize()
+    g_sp = capture_graph(torch, lambda: blk.run_block(n_steps))
+    g_full = capture_graph(torch, lambda: blk.run_full_block(n_steps))
+    t_sp = replay_median(torch, g_sp, reps)
+    t_full = replay_median(torch, g_full, reps)
+    del g_sp, g_full
+    att_pr = call_us(torch, lambda: blk.attend(True))
+    att_full = call_us(torch, lambda: blk.attend(False))
+    conf_un = call_us(torch, lambda: blk.confidence_and_unmask(1))
+    work = work_model(blk)
+    out = {"workload": name, "desc": wl.desc, "prefix": int(blk.layout.total_L),
+           "kept": int(blk.total_kept),
+           "block_ms": {"sprint": round(t_sp * 1e3, 4), "full_retention": round(t_full * 1e3, 4)},
+           "block_steps_per_s": {"sprint": round((n_steps + 1) * blk.nseq / t_sp, 2),
+                                 "full_retention": round((n_steps + 1) * blk.nseq / t_full, 2)},
+           "attention_us": {"pruned": round(att_pr, 3), "full": round(att_full, 3)},
+           "attention_hbm_frac": {
+               "pruned": round(work["attend_pruned"]["bytes"] / att_pr / 1e3 / HBM_PEAK_GBS, 4),
+               "full": round(work["attend_full"]["bytes"] / att_full / 1e3 / HBM_PEAK_GBS, 4)},
+           "denoising_step_us": {"pruned": round(att_pr + conf_un, 3),
+                                 "full": round(att_full + conf_un, 3)},
+           "speedup_pruned_vs_full": {"attention_call": round(att_full / att_pr, 4),
+                                      "denoising_step": round((att_full + conf_un) /
+                                                              (att_pr + conf_un), 4),
+                                      "block": round(t_full / t_sp, 4)}}
+    del blk
+    torch.cuda.synchronize()
+    return out
+
+
+def measure_planted(x, wl, n_steps, torch, fractions=(1.0, 0.5, 0.0), gamma=24.0, reps=5):
+    """Steps a block needs under confidence-adaptive unmasking when a known
+    fraction of its positions is confident.  After the block's pass, the LM
+    head rows of a fraction f of the block's positions are planted along
+    their attention outputs (W[v_i] = gamma * O_i / |O_i|^2, so position i's
+    logit for token v_i is about gamma = 24 and its confidence about
+    1 - V e^-24).  The block then runs with a host check after every step
+    and stops once nothing is masked; the fixed schedule always takes
+    ceil(m0 / ceil(m0 / T)) steps.  The block's inputs do not change between
+    steps here (the model that would refresh them is not on this path), so a
+    confidence below tau stays below it and the remaining positions follow
+    the minimum ceil(m / (T - t)) rule."""
+    from sparse_prefix_kv_amd.block import SprintBlock
+    blk = SprintBlock(x, "cuda")
+    blk.reset()
+    blk.pruning_pass()
+    torch.cuda.synchronize()
+    M, H, V = blk.nseq * blk.Lq, wl.H, wl.vocab
+    O = blk.O.float().view(M, H)
+    W0 = blk.W
+    T = n_steps + 1
+    m0 = blk.Lq
+    per_step = -(-m0 // T)
+    fixed_steps = -(-m0 // per_step)
+    out = {"gamma": gamma, "tau": blk.tau, "steps_budget_T": T,
+           "fixed_schedule_steps": fixed_steps, "cases": []}
+    for f in fractions:
+        n_pl = int(round(f * M))
+        pos = torch.arange(n_pl, device="cuda") * M // max(n_pl, 1)
+        vocab_rows = (pos * 4099 + 17) % V
+        W = W0.clone()
+        if n_pl:
+            Op = O[pos]
+            W[vocab_rows] = (gamma * Op / (Op * Op).sum(1, keepdim=True)).to(W.dtype)
+        blk.W = W
+
+        def run_adaptive():
+            blk.reset()
+            blk.pruning_pass()
+            t = 0
+            while int(blk.masked.sum().item()) > 0 and t < n_steps:
+                t += 1
+                blk.pruned_step(t)
+            return t + 1
+        steps = run_adaptive()
+        ts, tf = [], []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            run_adaptive()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+            t0 = time.perf_counter()
+            blk.run_block(n_steps)
+            torch.cuda.synchronize()
+            tf.append(time.perf_counter() - t0)
+        conf = blk.conf_blk
+        out["cases"].append({
+            "fraction_planted": f, "adaptive_steps": steps,
+            "confident_after_pass": int((conf > blk.tau).sum().item()),
+            "block_ms_adaptive": round(sorted(ts)[reps // 2] * 1e3, 4),
+            "block_ms_all_T_steps": round(sorted(tf)[reps // 2] * 1e3, 4)})
+        del W
+    blk.W = W0
+    out["timing"] = ("eager with a host check of the mask after every step (both columns); "
+                     "all_T_steps launches every step of the budget")
+    del blk
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -715,7 +924,7 @@ def main():
     cus = calls_cold[dominant]["median_us"]
     cold_achieved = (dw["flops"] / cus / 1e6) if dw["bound"] == "mfma" else (dw["bytes"] / cus / 1e3)
     roofline = {"bound": dw["bound"], "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": load_traffic(dominant),
+                "frac": round(achieved / peak, 4), "traffic": load_traffic(dominant, wl.name),
                 "kernel": dominant, "alg_per_launch": dw["flops"] if dw["bound"] == "mfma"
                 else dw["bytes"], "mean_launch_us": round(dus, 3),
                 "cold_launch_us": round(cus, 3), "cold_frac": round(cold_achieved / peak, 4)}
@@ -749,11 +958,26 @@ def main():
         log(f"[bench] MoE FFN ({moe['config']}): {moe['us']:.1f} us, {moe['gbs']:.0f} GB/s over "
             f"{moe['distinct_experts']} chosen experts")
 
+    # ---------------------------------------------------------------- second workload
+    compare = None
+    if args.compare and args.compare != wl.name:
+        compare = measure_compare(args.compare, n_steps, torch)
+        log(f"[bench] {args.compare}: block {compare['block_ms']['sprint']:.3f} ms SPRINT, "
+            f"{compare['block_ms']['full_retention']:.3f} ms full retention; attention "
+            f"{compare['attention_us']['pruned']:.1f} vs {compare['attention_us']['full']:.1f} us")
+
+    # ---------------------------------------------------------------- planted confidences
+    planted = None
+    if not args.no_planted:
+        planted = measure_planted(x, wl, n_steps, torch)
+        log("[bench] planted confidences: " + ", ".join(
+            f"f={c['fraction_planted']}: {c['adaptive_steps']} steps" for c in planted["cases"]))
+
     # ---------------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
-        cpu = cpu_baseline(x, wl, args.cpu_blocks)
+        cpu = cpu_baseline(x, wl, n_steps)
         log(f"[bench] oracle {cpu['value']:.3f} block-steps/s on {cpu['cores']} threads")
 
     value = steps_per_block / t_sprint
@@ -796,6 +1020,8 @@ def main():
         "generation": generation,
         "layers": layers,
         "moe": moe,
+        "compare": compare,
+        "planted_confidence": planted,
         "roofline": roofline,
         "kernels": kernels,
         "yardstick": yardstick,

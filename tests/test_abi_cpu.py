@@ -291,16 +291,23 @@ def test_bench_refuses_more_than_one_gpu():
 
 
 def test_committed_traffic_counters_match_the_kernel_source():
-    """profiles/traffic.json names the source its counters were taken on.
-    Counters taken on another version of that source are stale: bench.py
-    then reports traffic null (and so this test skips) until they are
+    """profiles/traffic.json keys each entry by call and workload and names
+    the source its counters were taken on.  bench.py reports a call's
+    traffic only for the workload its counters were taken on, and only while
+    the source is unchanged: counters taken on another version are stale
+    (bench.py then reports traffic null, and this test skips) until they are
     re-taken."""
     import hashlib
     tj = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    stale = []
     for name, ent in tj.items():
+        call, workload = name.split("@")
+        assert ent["workload"] == workload and call
         assert ent["hbm_bytes_per_launch"] > 0
         assert os.path.exists(os.path.join(ROOT, ent["summary"]))
         src = open(os.path.join(ROOT, ent["source"]), "rb").read()
         if hashlib.sha256(src).hexdigest()[:16] != ent["source_sha"]:
-            pytest.skip(f"{name}: counters taken on an earlier {ent['source']}; bench.py "
-                        "reports traffic null until they are re-taken")
+            stale.append(name)
+    if stale:
+        pytest.skip(f"{stale}: counters taken on an earlier source; bench.py "
+                    "reports traffic null until they are re-taken")
