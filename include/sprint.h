@@ -218,6 +218,25 @@ int block_attend(const void* Q, int32_t nseq, int32_t Lq, int32_t Hq, const void
                  int32_t dtype, void* O, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * block_attend without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and results as block_attend, bit for
+ * bit; the key-range partials live in a fixed device array of 16 MiB
+ * (16 << 20 bytes) that each GPU the library runs on holds until the
+ * process ends.  A call whose block_attend_ws(...) exceeds 16 MiB returns
+ * SPRINT_EWORKSPACE before any HIP call.  The call allocates nothing:
+ * the array's address is looked up (hipGetSymbolAddress) on the first call
+ * on each device.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (on different streams, or from several
+ * host threads) race; serialise them.  Nothing in the array needs to start
+ * at any value: every partial is written before it is read.
+ * ------------------------------------------------------------------------ */
+int block_attend_noalloc(const void* Q, int32_t nseq, int32_t Lq, int32_t Hq, const void* Kp,
+                         const void* Vp, const int32_t* cu_kv, int64_t total_kv, int32_t max_kv,
+                         const void* Kb, const void* Vb, int32_t Hkv, int32_t D, float scale,
+                         int32_t dtype, void* O, void* stream);
+
+/* ------------------------------------------------------------------------
  * Confidence-adaptive unmasking, one step (Non-uniform Token Unmasking).
  * For each sequence: m = number of masked positions; q = min(m, ceil(m /
  * steps_left)) where steps_left = T - t (steps_left <= 0 accepts all m);

@@ -222,10 +222,10 @@ size_t block_attend_ws(int32_t nseq, int32_t Lq, int32_t Hq, int32_t Hkv, int32_
   return attend_plan(nseq, Lq, Hq, Hkv, D, max_kv, has_block, SPRINT_F32).ws_bytes;
 }
 
-int block_attend(const void* Q, int32_t nseq, int32_t Lq, int32_t Hq, const void* Kp,
-                 const void* Vp, const int32_t* cu_kv, int64_t total_kv, int32_t max_kv,
-                 const void* Kb, const void* Vb, int32_t Hkv, int32_t D, float scale,
-                 int32_t dtype, void* O, void* ws, size_t ws_bytes, void* stream) {
+static int attend_check(const void* Q, int32_t nseq, int32_t Lq, int32_t Hq, const void* Kp,
+                        const void* Vp, const int32_t* cu_kv, int64_t total_kv, int32_t max_kv,
+                        const void* Kb, const void* Vb, int32_t Hkv, int32_t D, float scale,
+                        int32_t dtype, void* O) {
   if (!dtype_ok(dtype)) return SPRINT_EINVAL;
   const int ss = attend_shape_status(nseq, Lq, Hq, Hkv, D, max_kv);
   if (ss != SPRINT_OK) return ss;
@@ -243,9 +243,39 @@ int block_attend(const void* Q, int32_t nseq, int32_t Lq, int32_t Hq, const void
   if (total_kv * row_bytes >= (int64_t(1) << 31) ||
       static_cast<int64_t>(nseq) * Lq * row_bytes >= (int64_t(1) << 31))
     return SPRINT_EUNSUPPORTED;
+  return SPRINT_OK;
+}
+
+int block_attend(const void* Q, int32_t nseq, int32_t Lq, int32_t Hq, const void* Kp,
+                 const void* Vp, const int32_t* cu_kv, int64_t total_kv, int32_t max_kv,
+                 const void* Kb, const void* Vb, int32_t Hkv, int32_t D, float scale,
+                 int32_t dtype, void* O, void* ws, size_t ws_bytes, void* stream) {
+  const int ck = attend_check(Q, nseq, Lq, Hq, Kp, Vp, cu_kv, total_kv, max_kv, Kb, Vb, Hkv, D,
+                              scale, dtype, O);
+  if (ck != SPRINT_OK) return ck;
   const AttnPlan plan = attend_plan(nseq, Lq, Hq, Hkv, D, max_kv, Kb != nullptr, dtype);
   const int st = check_ws(ws, ws_bytes, plan.ws_bytes);
   if (st != SPRINT_OK) return st;
+  return status_of(launch_attend(Q, nseq, Lq, Hq, Kp, Vp, cu_kv, total_kv, Kb, Vb, Hkv, D, scale,
+                                 dtype, O, plan, ws, as_stream(stream)));
+}
+
+int block_attend_noalloc(const void* Q, int32_t nseq, int32_t Lq, int32_t Hq, const void* Kp,
+                         const void* Vp, const int32_t* cu_kv, int64_t total_kv, int32_t max_kv,
+                         const void* Kb, const void* Vb, int32_t Hkv, int32_t D, float scale,
+                         int32_t dtype, void* O, void* stream) {
+  const int ck = attend_check(Q, nseq, Lq, Hq, Kp, Vp, cu_kv, total_kv, max_kv, Kb, Vb, Hkv, D,
+                              scale, dtype, O);
+  if (ck != SPRINT_OK) return ck;
+  const AttnPlan plan = attend_plan(nseq, Lq, Hq, Hkv, D, max_kv, Kb != nullptr, dtype);
+  if (plan.ws_bytes > kAttendScratchBytes) return SPRINT_EWORKSPACE;
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SPRINT_EHIP;
+    ws = attend_scratch(dev);
+    if (ws == nullptr) return SPRINT_EHIP;
+  }
   return status_of(launch_attend(Q, nseq, Lq, Hq, Kp, Vp, cu_kv, total_kv, Kb, Vb, Hkv, D, scale,
                                  dtype, O, plan, ws, as_stream(stream)));
 }

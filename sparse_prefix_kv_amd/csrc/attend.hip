@@ -40,12 +40,20 @@
 //   planned cache length is still attended in full.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "sprint_device.hpp"
 #include "sprint_internal.hpp"
 
 namespace sprint {
+
+// Key-range partials of block_attend_noalloc: a fixed device array (each GPU
+// the library runs on holds its own copy until the process ends).  Host code
+// never uses the array's name as an address: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) char scratch[kAttendScratchBytes];
+
 namespace {
 
 constexpr int kKT = 32;       // keys per MFMA tile (one S^T accumulator)
@@ -772,6 +780,20 @@ hipError_t launch_attend(const void* Q, int nseq, int Lq, int Hq, const void* Kp
   a.scale_log2 = scale * kLog2e;
   if (dtype == 1) return D == 128 ? launch_typed<BF16, 128>(a, st) : launch_typed<BF16, 64>(a, st);
   return D == 128 ? launch_typed<F32, 128>(a, st) : launch_typed<F32, 64>(a, st);
+}
+
+void* attend_scratch(int device) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[device] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[device] = p;
+  }
+  return ptr[device];
 }
 
 }  // namespace sprint

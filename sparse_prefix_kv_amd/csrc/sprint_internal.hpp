@@ -40,6 +40,11 @@ struct AttnPlan {
 };
 AttnPlan attend_plan(int nseq, int Lq, int Hq, int Hkv, int D, int max_kv, int has_block,
                      int dtype);
+// block_attend_noalloc: its partials live in a fixed device array of this
+// many bytes; attend_scratch(device) is that array's address on the current
+// device (device must be current), or null when it cannot be found.
+constexpr size_t kAttendScratchBytes = size_t(16) << 20;
+void* attend_scratch(int device);
 hipError_t launch_attend(const void* Q, int nseq, int Lq, int Hq, const void* Kp, const void* Vp,
                          const int32_t* cu_kv, int64_t total_kv, const void* Kb, const void* Vb,
                          int Hkv, int D, float scale, int dtype, void* O, const AttnPlan& plan,

@@ -48,6 +48,9 @@ _SIGS = {
     "block_attend": (ctypes.c_int, [_c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
                                     _i64, _i32, _c_void_p, _c_void_p, _i32, _i32, _f32, _i32,
                                     _c_void_p, _c_void_p, _size, _c_void_p]),
+    "block_attend_noalloc": (ctypes.c_int, [_c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p,
+                                            _c_void_p, _i64, _i32, _c_void_p, _c_void_p, _i32,
+                                            _i32, _f32, _i32, _c_void_p, _c_void_p]),
     "unmask_select": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _i32, _f32, _i32, _c_void_p,
                                      _c_void_p, _c_void_p, _c_void_p]),
     "sprint_score_layers_ws": (_size, [_i64, _i32, _i32]),
@@ -315,6 +318,34 @@ def block_attend(Q, Kp, Vp, cu_kv, max_kv: int, Kb=None, Vb=None, scale: Optiona
         _ptr(Q), nseq, Lq, Hq, _ptr(Kp) if total_kv else None, _ptr(Vp) if total_kv else None,
         _ptr(cu_kv), total_kv, int(max_kv), _ptr(Kb), _ptr(Vb), Hkv, D, float(scale), _dt(Q),
         _ptr(O), _ptr(ws), ws.numel(), _stream(stream)))
+    return O
+
+
+def block_attend_noalloc(Q, Kp, Vp, cu_kv, max_kv: int, Kb=None, Vb=None,
+                         scale: Optional[float] = None, O=None, stream=None):
+    """block_attend with its key-range partials in the library's fixed
+    16 MiB device array instead of a workspace (the call allocates no device
+    memory; `O` must be given for that).  Calls overlapping on one GPU race."""
+    nseq, Lq, Hq, D = Q.shape
+    _dt(Q)
+    _arg(Q, "Q")
+    total_kv, Hkv = Kp.shape[0], Kp.shape[1]
+    _arg(Kp, "Kp", Q.dtype, shape=(total_kv, Hkv, D))
+    _arg(Vp, "Vp", Q.dtype, shape=(total_kv, Hkv, D))
+    _arg(cu_kv, "cu_kv", torch.int32, shape=(nseq + 1,))
+    if (Kb is None) != (Vb is None):
+        raise ValueError("Kb and Vb go together")
+    if Kb is not None:
+        _arg(Kb, "Kb", Q.dtype, shape=(nseq, Lq, Hkv, D))
+        _arg(Vb, "Vb", Q.dtype, shape=(nseq, Lq, Hkv, D))
+    if scale is None:
+        scale = D ** -0.5
+    O = torch.empty_like(Q) if O is None else _arg(O, "O", Q.dtype, Q.numel())
+    _gpu(Q=Q, Kp=Kp, Vp=Vp, cu_kv=cu_kv, Kb=Kb, Vb=Vb, O=O)
+    _check("block_attend_noalloc", lib().block_attend_noalloc(
+        _ptr(Q), nseq, Lq, Hq, _ptr(Kp) if total_kv else None, _ptr(Vp) if total_kv else None,
+        _ptr(cu_kv), total_kv, int(max_kv), _ptr(Kb), _ptr(Vb), Hkv, D, float(scale), _dt(Q),
+        _ptr(O), _stream(stream)))
     return O
 
 

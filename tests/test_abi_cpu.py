@@ -144,6 +144,14 @@ def test_attend_and_unmask_reject_before_hip():
     assert _call("block_attend", *a) == 1                           # one sequence longer than max_kv
     a = list(at); a[17] = 8
     assert _call("block_attend", *a) == 3
+    # the workspace-free variant: same checks, and a plan whose partials
+    # exceed its 16 MiB array is refused (fp32, 4 sequences of up to 2^20 keys)
+    na = at[:16] + [None]
+    a = list(na); a[11] = 5
+    assert _call("block_attend_noalloc", *a) == 1
+    a = list(na); a[1] = 4; a[8] = 1 << 20; a[14] = sprint.F32
+    assert sprint.block_attend_ws(4, 32, 16, 4, 128, 1 << 20, 1) > (16 << 20)
+    assert _call("block_attend_noalloc", *a) == 3
     um = [FAKE, FAKE, 1, 32, 0.9, 9, FAKE, FAKE, FAKE, None]
     a = list(um); a[3] = 65
     assert _call("unmask_select", *a) == 2
