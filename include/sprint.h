@@ -122,6 +122,8 @@ int sprint_score(const void* K, const float* conf, const int32_t* cu_len, int32_
  *   kept_idx [total_kept] int32 out
  * Precondition: cu_kept must be the prefix sum of min(keep, n) per sequence;
  * the kernels never write outside [cu_kept[s], cu_kept[s+1]) or total_kept.
+ * Scores are ranked as IEEE values (-0 equal to +0); NaN scores, and modality
+ * bytes other than 0 and 1, have no defined ranking.
  * ------------------------------------------------------------------------ */
 size_t sprint_prune_kv_ws(int64_t total_L, int32_t nseq);
 int sprint_prune_kv(const float* score, const uint8_t* modality, const int32_t* cu_len,

@@ -4,14 +4,17 @@
 //
 // Ranking key of position p: (score desc, position asc).  The score is mapped
 // to an order-preserving uint32, so "the k-th largest" is found exactly by an
-// MSB-first radix select (4 passes of 8 bits) per (sequence, modality)
+// MSB-first radix select (windows of up to 8 bits) per (sequence, modality)
 // segment.  The result is a threshold key T and a tie cut: a position is
 // kept iff key > T, or key == T and p <= tie_cut (the first ties by position).
 //
 // Launches:
-//   1. topk_threshold_kernel  one 1024-thread block per segment (the keys of
-//                             a sequence of up to 32768 positions read from
-//                             HBM once, into LDS);
+//   1. topk_threshold_kernel  one 1024-thread block per segment; the keys of
+//                             a sequence of up to 32768 positions are read
+//                             from HBM once and stay in registers (32 per
+//                             thread) for every radix window; the histogram
+//                             has a copy per lane so that keys crowding into
+//                             few digits do not serialize the LDS atomics;
 //   2. chunk_count_kernel     kept count of every 64-position chunk;
 //   3. compact_kernel         per chunk: prefix of earlier chunk counts in the
 //                             sequence -> output slots; writes kept_idx and
@@ -30,7 +33,7 @@ namespace sprint {
 namespace {
 
 constexpr int kSelThreads = 1024;
-constexpr int kLdsKeys = 32768;    // a sequence's keys kept in LDS (128 KB)
+constexpr int kRegChunks = 2;      // 16-position chunks of keys held per thread
 constexpr int kChunk = 64;
 constexpr int kCopyThreads = 256;
 
@@ -40,9 +43,10 @@ struct SegThresh {
 };
 
 __device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;  // -0 ranks equal to +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // non-negative: the sign bit set; negative: the two's complement, which
+  // reverses their order and puts -0 on the key of +0.  No score has key 0.
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? 0u - u : u | 0x80000000u;
 }
 
 __device__ __forceinline__ bool is_kept(uint32_t key, int64_t p, const SegThresh& t) {
@@ -80,6 +84,93 @@ __device__ __forceinline__ int block_incl_scan(int v, int* s_wave, int& total) {
   return v + base;
 }
 
+// Per-lane copies of the 256-digit histogram: digit d, copy c at
+// d * kHistCopies + c, lane l counting into copy l % kHistCopies.  Two lanes
+// of a wave share an address only when they are 32 apart and count the same
+// digit, however the keys crowd into few digits (scores share their top
+// exponent bits, so the first windows are far from uniform).
+constexpr int kHistCopies = 32;
+
+__device__ __forceinline__ void hist_count(int* hist, uint32_t digit) {
+  atomicAdd(&hist[digit * kHistCopies + (threadIdx.x & (kHistCopies - 1))], 1);
+}
+
+// Radix-window selection step shared by both paths.  On entry every thread
+// has counted its keys into hist.  Sums the copies of each digit into s_cnt
+// (and clears them for the next window), taking `absent0` off digit 0 (slots
+// counted there that hold no key).  Then every wave scans the 256 counts on
+// its own and returns, in every thread, the digit that holds the krem-th
+// largest key, the number of keys in higher digits, the number in it and the
+// number counted.  Every thread of the block calls it.
+struct WindowPick {
+  int digit, above, count, total;
+};
+
+__device__ __forceinline__ int dpp_row_shr(int v, int ctrl_shift) {
+  // lane i of a row of 16 reads lane i - n of that row, 0 below it
+  switch (ctrl_shift) {
+    case 1: return __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);
+    case 2: return __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);
+    case 4: return __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);
+    default: return __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);
+  }
+}
+
+__device__ __forceinline__ WindowPick pick_digit(int* hist, int* s_cnt, int krem, int absent0) {
+  const int lane = threadIdx.x & 63;
+  __syncthreads();  // every count is in
+  {
+    // digit d = threadIdx.x / 4: four threads sum 8 copies each
+    const int d = threadIdx.x >> 2, part = threadIdx.x & 3;
+    int4* hp = reinterpret_cast<int4*>(hist + d * kHistCopies + part * 8);
+    const int4 x = hp[0], y = hp[1];
+    hp[0] = make_int4(0, 0, 0, 0);
+    hp[1] = make_int4(0, 0, 0, 0);
+    int h = x.x + x.y + x.z + x.w + y.x + y.y + y.z + y.w;
+    h += __builtin_amdgcn_mov_dpp(h, 0xB1, 0xF, 0xF, true);  // quad lanes 1,0,3,2
+    h += __builtin_amdgcn_mov_dpp(h, 0x4E, 0xF, 0xF, true);  // quad lanes 2,3,0,1
+    if (part == 0) s_cnt[d] = d == 0 ? h - absent0 : h;
+  }
+  __syncthreads();
+  // lane l holds digits 252-4l .. 255-4l (the highest digits in lane 0); an
+  // inclusive scan over the lanes counts the keys at or above each lane's
+  // lowest digit
+  const int4 c = *reinterpret_cast<const int4*>(s_cnt + 252 - 4 * lane);
+  const int csum = c.x + c.y + c.z + c.w;
+  int v = csum;
+  v += dpp_row_shr(v, 1);
+  v += dpp_row_shr(v, 2);
+  v += dpp_row_shr(v, 4);
+  v += dpp_row_shr(v, 8);
+  const int r15 = __builtin_amdgcn_readlane(v, 15);
+  const int r31 = __builtin_amdgcn_readlane(v, 31);
+  const int r47 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  v += (row >= 1 ? r15 : 0) + (row >= 2 ? r31 : 0) + (row >= 3 ? r47 : 0);
+  // the lane's digits from the highest down
+  int acc = v - csum;  // keys above the lane's digits
+  int found = -1, f_above = 0, f_cnt = 0;
+  const int cnt[4] = {c.w, c.z, c.y, c.x};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (found < 0 && acc < krem && krem <= acc + cnt[q]) {
+      found = 255 - 4 * lane - q;
+      f_above = acc;
+      f_cnt = cnt[q];
+    }
+    acc += cnt[q];
+  }
+  const uint64_t m = __ballot(found >= 0);
+  WindowPick r{0, 0, 0, __builtin_amdgcn_readlane(v, 63)};
+  if (m != 0ull) {
+    const int src = __builtin_ctzll(m);
+    r.digit = __builtin_amdgcn_readlane(found, src);
+    r.above = __builtin_amdgcn_readlane(f_above, src);
+    r.count = __builtin_amdgcn_readlane(f_cnt, src);
+  }
+  return r;
+}
+
 __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
     const float* __restrict__ score, const uint8_t* __restrict__ modality,
     const int32_t* __restrict__ cu_len, const int32_t* __restrict__ keep, int nseq,
@@ -93,102 +184,260 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
   int64_t a, e;
   clamp_seq(cu_len, s, total_L, a, e);
   const int k = keep[seg];
-  __shared__ int hist[256];
+  __shared__ __align__(16) int hist[256 * kHistCopies];
+  __shared__ __align__(16) int s_cnt[256];
   __shared__ int s_wave[kSelThreads / 64];
-  __shared__ int s_bucket, s_above, s_total, s_found, s_nkeys;
-  __shared__ uint32_t s_keys[kLdsKeys];
+  __shared__ int s_found;
+  __shared__ uint32_t s_min[kSelThreads / 64], s_max[kSelThreads / 64];
   if (k <= 0) {
     if (threadIdx.x == 0) thr[seg] = SegThresh{0xFFFFFFFFu, -1};
     return;
   }
+  if (e <= a) {  // empty sequence: nothing to read
+    if (threadIdx.x == 0) thr[seg] = SegThresh{0u, INT_MAX};
+    return;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 256 * kHistCopies; i += kSelThreads) hist[i] = 0;
+  __syncthreads();
   uint32_t prefix = 0, pmask = 0;
   int krem = k;
   int ties = 0;
-  // A sequence of up to kLdsKeys positions has its modality's keys read from
-  // HBM once, during the first pass, into LDS (in any order: the histograms
-  // only count); the later passes read them there.  Longer sequences read
-  // the scores again in every pass.
-  const bool in_lds = e - a <= kLdsKeys;
-  if (threadIdx.x == 0) s_nkeys = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    if (threadIdx.x < 256) hist[threadIdx.x] = 0;
-    __syncthreads();
-    if (in_lds && pass > 0) {
-      const int nk = s_nkeys;
-      for (int i = threadIdx.x; i < nk; i += kSelThreads) {
-        const uint32_t key = s_keys[i];
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-      }
-    } else {
-      // eight chunks of the sequence per round, all their loads in flight
-      // before any is used
-      const int lane = threadIdx.x & 63;
-      constexpr int kU = 8;
-      for (int64_t p0 = a; p0 < e; p0 += kU * kSelThreads) {
-        uint8_t md[kU];
-        float sc[kU];
+
+  // The positions from a rounded down to a multiple of 16 are cut into
+  // chunks of 16; thread t holds chunks t and t + 1024.  When those cover the
+  // sequence, every key is read from HBM once, into registers, and every
+  // radix window counts from there.
+  const int64_t a16 = a & ~static_cast<int64_t>(15);
+  if (e - a16 <= kRegChunks * kSelThreads * 16) {
+    // key 0 marks a slot outside the sequence or of the other modality.
+    // Chunk j of a wave is active when it starts inside the sequence; the
+    // slots of inactive chunks are never counted (shorter sequences skip
+    // most of the work).
+    uint32_t key[kRegChunks * 16];
+    bool act[kRegChunks];
+    int n_slots = 0;  // slots of the active chunks of the block
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int64_t p = p0 + u * kSelThreads + threadIdx.x;
-          md[u] = p < e ? modality[p] : static_cast<uint8_t>(mod ^ 1);
-          sc[u] = p < e ? score[p] : 0.f;
+    for (int j = 0; j < kRegChunks; ++j) {
+      act[j] = a16 + static_cast<int64_t>(j * kSelThreads + wave * 64) * 16 < e;
+      const int64_t left = e - a16 - static_cast<int64_t>(j) * kSelThreads * 16;
+      const int64_t waves = left <= 0 ? 0 : (left + 1023) / 1024;
+      n_slots += static_cast<int>(waves < kSelThreads / 64 ? waves : kSelThreads / 64) * 1024;
+    }
+    int n_mine = 0;
+    {
+      u32x4 sv[kRegChunks][4], mv[kRegChunks];
+      const bool vec = (reinterpret_cast<uintptr_t>(score) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(modality) & 15) == 0;
+      if (vec) {
+        // 16-byte buffer loads; past the resource's end they read zeros
+        int64_t span = total_L - a16;  // integer arithmetic: the resource stays scalar
+        if (span > kRegChunks * kSelThreads * 16) span = kRegChunks * kSelThreads * 16;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(score + a16), 0, static_cast<int>(span * 4), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(modality + a16), 0, static_cast<int>(span), 0x00020000);
+#pragma unroll
+        for (int j = 0; j < kRegChunks; ++j) {
+          const int q = j * kSelThreads + threadIdx.x;
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            sv[j][c] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, q * 64 + c * 16, 0, 0));
+          mv[j] = __builtin_bit_cast(u32x4,
+                                     __builtin_amdgcn_raw_buffer_load_b128(rm, q * 16, 0, 0));
+        }
+      }
+      const uint32_t rep = mod ? 0x01010101u : 0u;
+#pragma unroll
+      for (int j = 0; j < kRegChunks; ++j) {
+        if (!act[j]) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) key[j * 16 + i] = 0u;
+          continue;
+        }
+        const int64_t c0 = a16 + static_cast<int64_t>(j * kSelThreads + threadIdx.x) * 16;
+        // unaligned arrays, or the chunk that runs past the end of the
+        // arrays: one position at a time (clamped into the sequence)
+        if (!vec || (c0 < e && c0 + 16 > total_L)) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int64_t p = c0 + i;
+            const int64_t pc = p < a ? a : (p >= e ? e - 1 : p);
+            sv[j][i >> 2][i & 3] = __float_as_uint(score[pc]);
+            const uint32_t sh = 8u * (i & 3);
+            mv[j][i >> 2] = (mv[j][i >> 2] & ~(0xFFu << sh)) | (uint32_t{modality[pc]} << sh);
+          }
+        }
+        // positions outside the sequence take modality byte 0xFF (neither)
+        if (c0 < a || c0 + 16 > e) {
+          const int lo = static_cast<int>(c0 < a ? a - c0 : 0);
+          const int hi = static_cast<int>(c0 >= e ? 0 : (c0 + 16 > e ? e - c0 : 16));
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (i < lo || i >= hi) mv[j][i >> 2] |= 0xFFu << (8 * (i & 3));
         }
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const bool mine = md[u] == mod;
-          const uint32_t key = mine ? order_key(sc[u]) : 0u;
-          if (mine && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-          if (in_lds) {
-            // one LDS slot reservation per wave
-            const uint64_t bal = __ballot(mine);
-            int slot0 = 0;
-            if (lane == 0 && bal) slot0 = atomicAdd(&s_nkeys, __popcll(bal));
-            slot0 = __shfl(slot0, 0, 64);
-            if (mine) s_keys[slot0 + __popcll(bal & ((1ull << lane) - 1ull))] = key;
+        for (int w = 0; w < 4; ++w) {
+          // bit 7 of each byte of z: that position is of this modality
+          const uint32_t x = mv[j][w] ^ rep;
+          const uint32_t z = ~(((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
+          n_mine += __popc(z);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const uint32_t sel = static_cast<uint32_t>(static_cast<int>(z << (24 - 8 * b)) >> 31);
+            key[j * 16 + w * 4 + b] = order_key(__uint_as_float(sv[j][w][b])) & sel;
           }
         }
       }
     }
-    __syncthreads();
-    // Suffix sums over the 256 digits (threads 0..255 = waves 0..3).  Every
-    // wave of the block reaches both barriers below.
-    int v = 0, h = 0;
-    if (threadIdx.x < 256) {
-      const int lane = threadIdx.x & 63;
-      h = hist[threadIdx.x];
-      v = h;  // inclusive suffix within the wave (higher digits = higher lanes)
+    // the modality's key count and its smallest and largest key
+    uint32_t kmin1 = 0xFFFFFFFFu, kmax = 0u;  // kmin1: smallest key - 1 (key 0 wraps)
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_down(v, off, 64);
-        if (lane + off < 64) v += o;
-      }
-      if (lane == 0) s_wave[threadIdx.x >> 6] = v;  // wave total
+    for (int r = 0; r < kRegChunks * 16; ++r) {
+      kmin1 = min(kmin1, key[r] - 1u);
+      kmax = max(kmax, key[r]);
+    }
+    int n_m = n_mine;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      kmin1 = min(kmin1, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin1), o, 64)));
+      kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o, 64)));
+      n_m += __shfl_xor(n_m, o, 64);
+    }
+    if (lane == 0) {
+      s_min[wave] = kmin1;
+      s_max[wave] = kmax;
+      s_wave[wave] = n_m;
     }
     __syncthreads();
-    if (threadIdx.x < 256) {
-      const int t = threadIdx.x, wave = t >> 6;
-      int higher = 0;
-      for (int w = wave + 1; w < 4; ++w) higher += s_wave[w];
-      const int incl = v + higher;        // elements with digit >= t
-      const int excl = incl - h;          // elements with digit >  t
-      if (pass == 0 && t == 0) s_total = incl;
-      if (excl < krem && krem <= incl) {
-        s_bucket = t;
-        s_above = excl;
-      }
+    n_m = 0;
+#pragma unroll
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+      kmin1 = min(kmin1, s_min[w]);
+      kmax = max(kmax, s_max[w]);
+      n_m += s_wave[w];
     }
-    __syncthreads();
-    if (pass == 0 && k >= s_total) {
+    if (k >= n_m) {  // every position of the modality is kept
       if (threadIdx.x == 0) thr[seg] = SegThresh{0u, INT_MAX};
       return;
     }
-    const int b = s_bucket;
-    krem -= s_above;
-    prefix |= static_cast<uint32_t>(b) << shift;
-    pmask |= 255u << shift;
-    ties = hist[b];
-    __syncthreads();
+    const uint32_t kmin = kmin1 + 1u;
+    const int n_absent = n_slots - n_m;
+    ties = n_m;
+    // Windows of up to 8 bits from the highest bit where the smallest and
+    // largest key differ (the bits above it are common to every key).  The
+    // first window counts every slot: the key-0 slots all fall on digit 0
+    // and are taken off there; later windows count the keys under the
+    // prefix, which key 0 matches only while the prefix is 0.
+    int hi = -1;
+    if (kmin == kmax) {
+      prefix = kmin;
+      pmask = 0xFFFFFFFFu;
+    } else {
+      hi = 31 - __clz(static_cast<int>(kmin ^ kmax));
+      pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+      prefix = kmin & pmask;
+    }
+    bool first = true;
+    while (hi >= 0) {
+      const int wbits = hi + 1 < 8 ? hi + 1 : 8;
+      const int shift = hi + 1 - wbits;
+      const uint32_t dmask = (1u << wbits) - 1u;
+#pragma unroll
+      for (int j = 0; j < kRegChunks; ++j) {
+        if (!act[j]) continue;
+        if (first) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) hist_count(hist, __builtin_amdgcn_ubfe(key[j * 16 + i], shift, wbits));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const bool in = (key[j * 16 + i] & pmask) == prefix;
+            if (in) hist_count(hist, __builtin_amdgcn_ubfe(key[j * 16 + i], shift, wbits));
+          }
+        }
+      }
+      const WindowPick w =
+          pick_digit(hist, s_cnt, krem, first || prefix == 0u ? n_absent : 0);
+      first = false;
+      krem -= w.above;
+      ties = w.count;
+      prefix |= static_cast<uint32_t>(w.digit) << shift;
+      pmask |= dmask << shift;
+      hi = shift - 1;
+    }
+    if (krem >= ties) {
+      if (threadIdx.x == 0) thr[seg] = SegThresh{prefix, INT_MAX};
+      return;
+    }
+    // Tie cut: the krem-th position, in position order, whose key is the
+    // threshold (never 0).  Position order is chunk 0 of threads 0..1023,
+    // then chunk 1.
+    int before = 0;
+#pragma unroll
+    for (int j = 0; j < kRegChunks; ++j) {
+      uint32_t tie = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tie |= (key[j * 16 + i] == prefix ? 1u : 0u) << i;
+      const int c = __popc(tie);
+      int tot;
+      const int incl = block_incl_scan(c, s_wave, tot) + before;
+      const int want = krem - (incl - c);  // 1-based rank of the cut in this chunk
+      if (want >= 1 && want <= c) {
+        int seen = 0, cut = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if ((tie >> i) & 1u) {
+            ++seen;
+            if (seen == want) cut = i;
+          }
+        const int64_t p = a16 + static_cast<int64_t>(j * kSelThreads + threadIdx.x) * 16 + cut;
+        thr[seg] = SegThresh{prefix, static_cast<int32_t>(p)};
+      }
+      before += tot;
+    }
+    return;
+  }
+
+  // Longer sequences: every window reads the scores from HBM again, in four
+  // windows of 8 bits from the top.
+  bool first = true;
+  for (int hi = 31; hi >= 0; hi -= 8) {
+    const int shift = hi - 7;
+    constexpr int kU = 8;
+    for (int64_t p0 = a; p0 < e; p0 += kU * kSelThreads) {
+      uint32_t md[kU];
+      float sc[kU];
+      // every load of the round issued before any is used: positions past
+      // the sequence read its last position and count as the other modality
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t p = p0 + u * kSelThreads + threadIdx.x;
+        const bool in = p < e;
+        const int64_t pc = in ? p : e - 1;
+        const uint32_t m = modality[pc];
+        md[u] = in ? m : static_cast<uint32_t>(mod ^ 1);
+        sc[u] = score[pc];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t key = order_key(sc[u]);
+        if (md[u] == mod && (key & pmask) == prefix) hist_count(hist, (key >> shift) & 0xFFu);
+      }
+    }
+    const WindowPick w = pick_digit(hist, s_cnt, krem, 0);
+    if (first) {
+      if (k >= w.total) {  // every position of the modality is kept
+        if (threadIdx.x == 0) thr[seg] = SegThresh{0u, INT_MAX};
+        return;
+      }
+      first = false;
+    }
+    krem -= w.above;
+    ties = w.count;
+    prefix |= static_cast<uint32_t>(w.digit) << shift;
+    pmask |= 0xFFu << shift;
   }
   // prefix is now the exact key of the k-th largest; keep the first `krem`
   // of the `ties` positions that carry it.
@@ -213,6 +462,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
     if (s_found) break;
   }
 }
+
 
 __device__ __forceinline__ bool kept_at(const float* __restrict__ score,
                                         const uint8_t* __restrict__ modality,

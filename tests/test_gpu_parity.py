@@ -224,6 +224,58 @@ def test_prune_all_equal_scores_keep_lowest():
     np.testing.assert_array_equal(got, np.concatenate([np.arange(10), 50 + np.arange(2000)]))
 
 
+# Sequences on both sides of 32768 positions counted from the start rounded
+# down to 16 (the selection holds up to that many keys per thread block and
+# reads longer ones again per radix window), a start that is not a multiple
+# of 16, and an end of the arrays inside a 16-position chunk.
+BOUNDARY_RUNS = [
+    ((0, 5),),
+    ((1, 20000), (0, 12763)),           # positions 5..32767: 32768 from 0
+    ((0, 40000), (1, 1)),               # 40001 positions
+    ((1, 32767),),                      # 72769..105535: 32768 from 72768
+    ((0, 1), (1, 32768)),               # 32769 positions from a multiple of 16
+    ((1, 17), (0, 15)),                 # ends the arrays at 138337 (not / 16)
+]
+
+
+def _signed_wide_scores(n, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 3, n)).astype(np.float32)
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+@pytest.mark.parametrize("kind", ["uniform", "ties", "signed_wide"])
+def test_prune_long_short_and_unaligned_sequences(offset, kind):
+    """Kept sets at the 32768-key boundary, over sign and exponent spread.
+    offset 1 hands the scores and modality over at addresses that are not
+    16-byte aligned."""
+    lay = synth.layout_from_runs(BOUNDARY_RUNS)
+    n = lay.total_L
+    score = {"uniform": lambda: synth.random_scores(n, 70),
+             "ties": lambda: synth.random_scores(n, 71, 8),
+             "signed_wide": lambda: _signed_wide_scores(n, 72)}[kind]()
+    K = synth.normal_array((n, 1, 64), 73, 1.0, "f32")
+    V = synth.normal_array((n, 1, 64), 74, 1.0, "f32")
+    sbuf = torch.zeros(n + offset, dtype=torch.float32, device=DEV)
+    sbuf[offset:] = _f32(score)
+    mbuf = torch.zeros(n + 3 * offset, dtype=torch.uint8, device=DEV)
+    mbuf[3 * offset:] = _u8(lay.modality)
+    for rt, ri in [(0.5, 0.3), (1.0, 0.8), (0.01, 0.99)]:
+        keep = np.array([[oracle.keep_count(rt, lay.n_text[s]),
+                          oracle.keep_count(ri, lay.n_img[s])] for s in range(lay.nseq)])
+        eff = np.stack([np.minimum(keep[:, 0], lay.n_text), np.minimum(keep[:, 1], lay.n_img)], 1)
+        cu_kept = np.concatenate([[0], np.cumsum(eff.sum(1))]).astype(np.int32)
+        Ko, Vo, idx = sprint.sprint_prune_kv(sbuf[offset:], mbuf[3 * offset:], _i32(lay.cu_len),
+                                             _i32(keep.reshape(-1)), _i32(cu_kept),
+                                             int(cu_kept[-1]), _to_dev(K, "f32", DEV),
+                                             _to_dev(V, "f32", DEV))
+        want = oracle.select_kept(score, lay.modality, lay.cu_len, keep)
+        np.testing.assert_array_equal(_np(idx).astype(np.int64), want)
+        Kp, Vp = oracle.compact(K, V, want)
+        assert np.array_equal(_np(Ko), Kp.astype(np.float32))
+        assert np.array_equal(_np(Vo), Vp.astype(np.float32))
+
+
 @pytest.mark.parametrize("name", ["interleaved32k", "ragged8", "single4k"])
 def test_prune_full_size(name):
     wl = synth.WORKLOADS[name]
