@@ -15,13 +15,14 @@
 //                             thread) for every radix window; the histogram
 //                             has a copy per lane so that keys crowding into
 //                             few digits do not serialize the LDS atomics;
-//   2. chunk_count_kernel     kept count of every 64-position chunk;
-//   3. compact_kernel         per chunk: prefix of earlier chunk counts in the
+//                             each block also writes its modality's kept
+//                             count of every 64-position chunk;
+//   2. compact_kernel         per chunk: prefix of earlier chunk counts in the
 //                             sequence -> output slots; writes kept_idx and
 //                             copies the K and V rows (16-byte vectors), of
 //                             every layer (grid y) when one kept set serves
 //                             several layers' caches.
-// With a kept set per layer, all three run once per layer (grid y), each
+// With a kept set per layer, both run once per layer (grid y), each
 // layer on its own scores, thresholds, counts and kept_idx row.
 // The copy dominates: 2 x kept x row bytes read and written, HBM-bound.
 #include <limits.h>
@@ -174,32 +175,56 @@ __device__ __forceinline__ WindowPick pick_digit(int* hist, int* s_cnt, int krem
 __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
     const float* __restrict__ score, const uint8_t* __restrict__ modality,
     const int32_t* __restrict__ cu_len, const int32_t* __restrict__ keep, int nseq,
-    int64_t total_L, SegThresh* __restrict__ thr) {
+    int64_t total_L, SegThresh* __restrict__ thr, int32_t* __restrict__ counts, int64_t nchunk) {
   // grid y: the layer whose scores select its own set (one layer otherwise)
   score += static_cast<int64_t>(blockIdx.y) * total_L;
   thr += static_cast<int64_t>(blockIdx.y) * nseq * 2;
   const int seg = blockIdx.x;
   const int s = seg >> 1;
   const uint8_t mod = static_cast<uint8_t>(seg & 1);
+  // this segment's column of kept counts per 64-position chunk (chunk ids
+  // run sequence by sequence, as the compaction numbers them)
+  counts += (static_cast<int64_t>(blockIdx.y) * 2 + mod) * nchunk;
   int64_t a, e;
   clamp_seq(cu_len, s, total_L, a, e);
+  const int nc = static_cast<int>((e - a + kChunk - 1) / kChunk);
   const int k = keep[seg];
   __shared__ __align__(16) int hist[256 * kHistCopies];
   __shared__ __align__(16) int s_cnt[256];
+  __shared__ int s_cc[kSelThreads];
   __shared__ int s_wave[kSelThreads / 64];
+  __shared__ int s_first[kSelThreads / 64];
   __shared__ int s_found;
+  __shared__ int64_t s_cut;
   __shared__ uint32_t s_min[kSelThreads / 64], s_max[kSelThreads / 64];
-  if (k <= 0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 256 * kHistCopies; i += kSelThreads) hist[i] = 0;
+  s_cc[threadIdx.x] = 0;
+  {
+    // chunk id of the sequence's first chunk: chunks of the earlier ones
+    int acc = 0;
+    for (int s2 = threadIdx.x; s2 < s; s2 += kSelThreads) {
+      int64_t a2, e2;
+      clamp_seq(cu_len, s2, total_L, a2, e2);
+      acc += static_cast<int>((e2 - a2 + kChunk - 1) / kChunk);
+    }
+    acc = wave_sum_i(acc);
+    if (lane == 0) s_first[wave] = acc;
+  }
+  __syncthreads();
+  int first_chunk = 0;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) first_chunk += s_first[w];
+  counts += first_chunk;
+  if (k <= 0) {  // nothing kept
     if (threadIdx.x == 0) thr[seg] = SegThresh{0xFFFFFFFFu, -1};
+    for (int c = threadIdx.x; c < nc; c += kSelThreads) counts[c] = 0;
     return;
   }
   if (e <= a) {  // empty sequence: nothing to read
     if (threadIdx.x == 0) thr[seg] = SegThresh{0u, INT_MAX};
     return;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < 256 * kHistCopies; i += kSelThreads) hist[i] = 0;
-  __syncthreads();
   uint32_t prefix = 0, pmask = 0;
   int krem = k;
   int ties = 0;
@@ -318,91 +343,157 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
       kmax = max(kmax, s_max[w]);
       n_m += s_wave[w];
     }
-    if (k >= n_m) {  // every position of the modality is kept
-      if (threadIdx.x == 0) thr[seg] = SegThresh{0u, INT_MAX};
-      return;
+    // every position of the modality is kept when k >= n_m
+    const bool all = k >= n_m;
+    int64_t cut = INT_MAX;
+    if (!all) {
+      const uint32_t kmin = kmin1 + 1u;
+      const int n_absent = n_slots - n_m;
+      ties = n_m;
+      // Windows of up to 8 bits from the highest bit where the smallest and
+      // largest key differ (the bits above it are common to every key).  The
+      // first window counts every slot: the key-0 slots all fall on digit 0
+      // and are taken off there; later windows count the keys under the
+      // prefix, which key 0 matches only while the prefix is 0.
+      int hi = -1;
+      if (kmin == kmax) {
+        prefix = kmin;
+        pmask = 0xFFFFFFFFu;
+      } else {
+        hi = 31 - __clz(static_cast<int>(kmin ^ kmax));
+        pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
+        prefix = kmin & pmask;
+      }
+      bool first = true;
+      while (hi >= 0) {
+        const int wbits = hi + 1 < 8 ? hi + 1 : 8;
+        const int shift = hi + 1 - wbits;
+        const uint32_t dmask = (1u << wbits) - 1u;
+#pragma unroll
+        for (int j = 0; j < kRegChunks; ++j) {
+          if (!act[j]) continue;
+          if (first) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+            hist_count(hist, __builtin_amdgcn_ubfe(key[j * 16 + i], shift, wbits));
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const bool in = (key[j * 16 + i] & pmask) == prefix;
+              if (in) hist_count(hist, __builtin_amdgcn_ubfe(key[j * 16 + i], shift, wbits));
+            }
+          }
+        }
+        const WindowPick w =
+            pick_digit(hist, s_cnt, krem, first || prefix == 0u ? n_absent : 0);
+        first = false;
+        krem -= w.above;
+        ties = w.count;
+        prefix |= static_cast<uint32_t>(w.digit) << shift;
+        pmask |= dmask << shift;
+        hi = shift - 1;
+      }
+      if (krem < ties) {
+        // Tie cut: the krem-th position, in position order, whose key is the
+        // threshold (never 0).  Position order is chunk 0 of threads 0..1023,
+        // then chunk 1.
+        int before = 0;
+#pragma unroll
+        for (int j = 0; j < kRegChunks; ++j) {
+          uint32_t tie = 0;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) tie |= (key[j * 16 + i] == prefix ? 1u : 0u) << i;
+          const int c = __popc(tie);
+          int tot;
+          const int incl = block_incl_scan(c, s_wave, tot) + before;
+          const int want = krem - (incl - c);  // 1-based rank of the cut in this chunk
+          if (want >= 1 && want <= c) {
+            int seen = 0, slot = 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if ((tie >> i) & 1u) {
+                ++seen;
+                if (seen == want) slot = i;
+              }
+            s_cut = a16 + static_cast<int64_t>(j * kSelThreads + threadIdx.x) * 16 + slot;
+          }
+          before += tot;
+        }
+        __syncthreads();
+        cut = s_cut;
+      }
     }
-    const uint32_t kmin = kmin1 + 1u;
-    const int n_absent = n_slots - n_m;
-    ties = n_m;
-    // Windows of up to 8 bits from the highest bit where the smallest and
-    // largest key differ (the bits above it are common to every key).  The
-    // first window counts every slot: the key-0 slots all fall on digit 0
-    // and are taken off there; later windows count the keys under the
-    // prefix, which key 0 matches only while the prefix is 0.
-    int hi = -1;
-    if (kmin == kmax) {
-      prefix = kmin;
-      pmask = 0xFFFFFFFFu;
-    } else {
-      hi = 31 - __clz(static_cast<int>(kmin ^ kmax));
-      pmask = hi == 31 ? 0u : ~((2u << hi) - 1u);
-      prefix = kmin & pmask;
+    const uint32_t T = all ? 0u : prefix;
+    if (threadIdx.x == 0) thr[seg] = SegThresh{T, static_cast<int32_t>(cut)};
+    // Kept counts of the chunks.  Kept: key >= Tm when there is no tie cut
+    // (Tm = 1 keeps every key of the modality), else key > T or key == T at
+    // a position <= cut.
+    const bool tie_cut = cut != INT_MAX;
+    const uint32_t Tm = all ? 1u : T;
+    int kc[kRegChunks];          // kept slots of chunk j
+    uint32_t kmask[kRegChunks];  // the same as a bit mask (tie cut or unaligned start)
+    const bool aligned = (a & 15) == 0;
+#pragma unroll
+    for (int j = 0; j < kRegChunks; ++j) {
+      kc[j] = 0;
+      kmask[j] = 0;
+      if (!act[j]) continue;
+      const int64_t c0 = a16 + static_cast<int64_t>(j * kSelThreads + threadIdx.x) * 16;
+      if (!tie_cut && aligned) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kc[j] += key[j * 16 + i] >= Tm ? 1 : 0;
+      } else {
+        const int64_t rel = cut - c0;  // slots 0..lim may tie
+        const int lim = static_cast<int>(rel < -1 ? -1 : (rel > 15 ? 15 : rel));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t kk = key[j * 16 + i];
+          const bool kept = tie_cut ? (kk > T || (kk == T && i <= lim)) : kk >= Tm;
+          kmask[j] |= (kept ? 1u : 0u) << i;
+        }
+        kc[j] = __popc(kmask[j]);
+      }
     }
-    bool first = true;
-    while (hi >= 0) {
-      const int wbits = hi + 1 < 8 ? hi + 1 : 8;
-      const int shift = hi + 1 - wbits;
-      const uint32_t dmask = (1u << wbits) - 1u;
+    if (aligned) {
+      // 16-position chunk q of the sequence is quarter q % 4 of 64-position
+      // chunk q / 4, and the four quarters sit in lanes 4c .. 4c+3
 #pragma unroll
       for (int j = 0; j < kRegChunks; ++j) {
         if (!act[j]) continue;
-        if (first) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) hist_count(hist, __builtin_amdgcn_ubfe(key[j * 16 + i], shift, wbits));
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const bool in = (key[j * 16 + i] & pmask) == prefix;
-            if (in) hist_count(hist, __builtin_amdgcn_ubfe(key[j * 16 + i], shift, wbits));
-          }
-        }
+        int v = kc[j];
+        v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);  // quad lanes 1,0,3,2
+        v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);  // quad lanes 2,3,0,1
+        const int c = (j * kSelThreads + static_cast<int>(threadIdx.x)) >> 2;
+        if ((threadIdx.x & 3) == 0 && c < nc) counts[c] = v;
       }
-      const WindowPick w =
-          pick_digit(hist, s_cnt, krem, first || prefix == 0u ? n_absent : 0);
-      first = false;
-      krem -= w.above;
-      ties = w.count;
-      prefix |= static_cast<uint32_t>(w.digit) << shift;
-      pmask |= dmask << shift;
-      hi = shift - 1;
-    }
-    if (krem >= ties) {
-      if (threadIdx.x == 0) thr[seg] = SegThresh{prefix, INT_MAX};
       return;
     }
-    // Tie cut: the krem-th position, in position order, whose key is the
-    // threshold (never 0).  Position order is chunk 0 of threads 0..1023,
-    // then chunk 1.
-    int before = 0;
+    // unaligned start: a thread's 16 slots fall in at most two chunks
 #pragma unroll
     for (int j = 0; j < kRegChunks; ++j) {
-      uint32_t tie = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tie |= (key[j * 16 + i] == prefix ? 1u : 0u) << i;
-      const int c = __popc(tie);
-      int tot;
-      const int incl = block_incl_scan(c, s_wave, tot) + before;
-      const int want = krem - (incl - c);  // 1-based rank of the cut in this chunk
-      if (want >= 1 && want <= c) {
-        int seen = 0, cut = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if ((tie >> i) & 1u) {
-            ++seen;
-            if (seen == want) cut = i;
-          }
-        const int64_t p = a16 + static_cast<int64_t>(j * kSelThreads + threadIdx.x) * 16 + cut;
-        thr[seg] = SegThresh{prefix, static_cast<int32_t>(p)};
+      const uint32_t km = kmask[j];
+      if (km == 0u) continue;
+      const int64_t c0 = a16 + static_cast<int64_t>(j * kSelThreads + threadIdx.x) * 16;
+      const int r0 = static_cast<int>(c0 - a);  // -15 .. 32767
+      const int C0 = r0 >> 6, C1 = (r0 + 15) >> 6;
+      if (C0 == C1) {
+        atomicAdd(&s_cc[C0], __popc(km));
+      } else {
+        // slots before a hold key 0, so `lo` is empty when C0 is -1
+        const int ib = C1 * 64 - r0;
+        const uint32_t lo = km & ((1u << ib) - 1u), up = km >> ib;
+        if (lo != 0u) atomicAdd(&s_cc[C0], __popc(lo));
+        if (up != 0u) atomicAdd(&s_cc[C1], __popc(up));
       }
-      before += tot;
     }
+    __syncthreads();
+    if (static_cast<int>(threadIdx.x) < nc) counts[threadIdx.x] = s_cc[threadIdx.x];  // nc <= 513
     return;
   }
 
   // Longer sequences: every window reads the scores from HBM again, in four
   // windows of 8 bits from the top.
-  bool first = true;
+  bool first = true, all = false;
   for (int hi = 31; hi >= 0; hi -= 8) {
     const int shift = hi - 7;
     constexpr int kU = 8;
@@ -429,8 +520,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
     const WindowPick w = pick_digit(hist, s_cnt, krem, 0);
     if (first) {
       if (k >= w.total) {  // every position of the modality is kept
-        if (threadIdx.x == 0) thr[seg] = SegThresh{0u, INT_MAX};
-        return;
+        all = true;
+        break;
       }
       first = false;
     }
@@ -441,25 +532,38 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
   }
   // prefix is now the exact key of the k-th largest; keep the first `krem`
   // of the `ties` positions that carry it.
-  if (krem >= ties) {
-    if (threadIdx.x == 0) thr[seg] = SegThresh{prefix, INT_MAX};
-    return;
-  }
-  if (threadIdx.x == 0) s_found = 0;
-  __syncthreads();
-  int base = 0;
-  for (int64_t p0 = a; p0 < e; p0 += kSelThreads) {
-    const int64_t p = p0 + threadIdx.x;
-    const int f = (p < e && modality[p] == mod && order_key(score[p]) == prefix) ? 1 : 0;
-    int tot;
-    const int incl = block_incl_scan(f, s_wave, tot);
-    if (f && base + incl == krem) {
-      thr[seg] = SegThresh{prefix, static_cast<int32_t>(p)};
-      s_found = 1;
-    }
-    base += tot;
+  int64_t cut = INT_MAX;
+  if (!all && krem < ties) {
+    if (threadIdx.x == 0) s_found = 0;
     __syncthreads();
-    if (s_found) break;
+    int base = 0;
+    for (int64_t p0 = a; p0 < e; p0 += kSelThreads) {
+      const int64_t p = p0 + threadIdx.x;
+      const int f = (p < e && modality[p] == mod && order_key(score[p]) == prefix) ? 1 : 0;
+      int tot;
+      const int incl = block_incl_scan(f, s_wave, tot);
+      if (f && base + incl == krem) {
+        s_cut = p;
+        s_found = 1;
+      }
+      base += tot;
+      __syncthreads();
+      if (s_found) break;
+    }
+    cut = s_cut;
+  }
+  const uint32_t T = all ? 0u : prefix;
+  if (threadIdx.x == 0) thr[seg] = SegThresh{T, static_cast<int32_t>(cut)};
+  // kept counts of the chunks, a wave per chunk
+  for (int c = wave; c < nc; c += kSelThreads / 64) {
+    const int64_t p = a + static_cast<int64_t>(c) * kChunk + lane;
+    bool kept = false;
+    if (p < e && modality[p] == mod) {
+      const uint32_t kk = order_key(score[p]);
+      kept = all || kk > T || (kk == T && p <= cut);
+    }
+    const uint64_t b = __ballot(kept);
+    if (lane == 0) counts[c] = static_cast<int32_t>(__popcll(b));
   }
 }
 
@@ -470,25 +574,6 @@ __device__ __forceinline__ bool kept_at(const float* __restrict__ score,
   const uint8_t m = modality[p];
   const SegThresh t = thr[2 * s + (m ? 1 : 0)];
   return is_kept(order_key(score[p]), p, t);
-}
-
-// One wave per 64-position chunk.
-__global__ __launch_bounds__(64) void chunk_count_kernel(const float* __restrict__ score,
-                                                         const uint8_t* __restrict__ modality,
-                                                         const int32_t* __restrict__ cu_len,
-                                                         int nseq, int64_t total_L,
-                                                         const SegThresh* __restrict__ thr,
-                                                         int32_t* __restrict__ counts) {
-  SeqChunk sc;
-  if (!find_seq_chunk(cu_len, nseq, kChunk, total_L, blockIdx.x, sc)) return;
-  // grid y: the layer (its scores, thresholds and counts; one layer otherwise)
-  score += static_cast<int64_t>(blockIdx.y) * total_L;
-  thr += static_cast<int64_t>(blockIdx.y) * nseq * 2;
-  counts += static_cast<int64_t>(blockIdx.y) * gridDim.x;
-  const int64_t p = sc.begin + static_cast<int64_t>(sc.c) * kChunk + threadIdx.x;
-  const bool f = p < sc.begin + sc.len && kept_at(score, modality, thr, sc.seq, p);
-  const uint64_t bal = __ballot(f);
-  if (threadIdx.x == 0) counts[blockIdx.x] = static_cast<int32_t>(__popcll(bal));
 }
 
 __global__ __launch_bounds__(kCopyThreads) void compact_kernel(
@@ -511,7 +596,7 @@ __global__ __launch_bounds__(kCopyThreads) void compact_kernel(
   if (per_layer) {
     score += layer * total_L;
     thr += layer * nseq * 2;
-    counts += layer * gridDim.x;
+    counts += layer * 2 * gridDim.x;
     kept_idx += layer * total_kept;
   }
   __shared__ int64_t s_pos[kChunk];
@@ -520,7 +605,9 @@ __global__ __launch_bounds__(kCopyThreads) void compact_kernel(
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int pre = 0;
-    for (int i = lane; i < sc.c; i += 64) pre += counts[sc.first + i];
+    // both modality columns of the earlier chunks of the sequence
+    for (int i = lane; i < sc.c; i += 64)
+      pre += counts[sc.first + i] + counts[gridDim.x + sc.first + i];
     pre = wave_sum_i(pre);
     const int64_t p = sc.begin + static_cast<int64_t>(sc.c) * kChunk + lane;
     const bool f = p < sc.begin + sc.len && kept_at(score, modality, thr, sc.seq, p);
@@ -579,7 +666,7 @@ size_t prune_ws_bytes(int64_t total_L, int nseq, int n_sets) {
   const size_t thr =
       align_up(static_cast<size_t>(nseq) * 2 * n_sets * sizeof(SegThresh), 256);
   const size_t cnt =
-      align_up(static_cast<size_t>(chunk_bound(total_L, nseq, kChunk)) * n_sets * 4, 256);
+      align_up(static_cast<size_t>(chunk_bound(total_L, nseq, kChunk)) * n_sets * 2 * 4, 256);
   return thr + cnt;
 }
 
@@ -598,12 +685,8 @@ hipError_t launch_prune(const float* score, const uint8_t* modality, const int32
   const int row_vecs = Hkv * D * es / 16;
   const int64_t nchunk = chunk_bound(total_L, nseq, kChunk);
   topk_threshold_kernel<<<dim3(nseq * 2, n_sets), dim3(kSelThreads), 0, st>>>(
-      score, modality, cu_len, keep, nseq, total_L, thr);
+      score, modality, cu_len, keep, nseq, total_L, thr, counts, nchunk);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  chunk_count_kernel<<<dim3(static_cast<unsigned>(nchunk), n_sets), dim3(64), 0, st>>>(
-      score, modality, cu_len, nseq, total_L, thr, counts);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (total_kept == 0) return hipSuccess;
   compact_kernel<<<dim3(static_cast<unsigned>(nchunk), static_cast<unsigned>(n_layers)),
