@@ -10,6 +10,8 @@
 // tile) leave the kernel; a merge kernel folds the tiles in vocabulary order.
 // Ties keep the lowest vocabulary index.  Sums use exp2 with log2(e) scaling.
 #include <limits.h>
+
+#include <algorithm>
 #include <math.h>
 
 #include "sprint_device.hpp"
@@ -207,6 +209,9 @@ __global__ __launch_bounds__(256) void lmhead_tile_kernel(const char* __restrict
 // Blocks are mapped XCD-aware: block b runs on XCD b % 8, so each XCD gets a
 // contiguous range of tile ids, ordered in groups of 8 token tiles so the
 // ~32 blocks resident on one XCD share 4 W tiles and 8 X tiles in its L2.
+// The grid is one block per CU; a block walks its XCD's range at a stride
+// of the blocks per XCD and loads the next tile's first two chunks under the
+// current tile's last two chunks and epilogue.
 constexpr int kGB = 256;                     // tile edge (vocab and tokens)
 constexpr int kGKC = 64;                     // reduction depth per stage
 constexpr int kGStageElems = 2 * kGB * kGKC; // A rows then B rows
@@ -270,22 +275,41 @@ __device__ __forceinline__ void gemm_interleave() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-__global__ __launch_bounds__(kGThreads) void lmhead_gemm_kernel(
-    const uint16_t* __restrict__ X, int64_t M, int H, const uint16_t* __restrict__ W, int V,
-    float4* __restrict__ part, int n_vt, int n_mt, int per_xcd) {
-  __shared__ __align__(16) uint16_t st0[kGStageElems];
-  __shared__ __align__(16) uint16_t st1[kGStageElems];
-  const int b = blockIdx.x;
-  const int t = (b % kXcds) * per_xcd + b / kXcds;
-  if (t >= n_vt * n_mt) return;
+// Tile t of the vocabulary x token grid, in groups of kGroupM token tiles
+// per vocabulary tile.
+struct GemmTile {
+  int vt, v0;
+  int64_t t0;
+};
+
+__device__ __forceinline__ GemmTile gemm_tile(int t, int n_vt, int n_mt) {
   const int group = kGroupM * n_vt;
   const int first_m = (t / group) * kGroupM;
   const int gm = min(n_mt - first_m, kGroupM);
   const int r_in = t % group;
   const int mt = first_m + r_in % gm;
   const int vt = r_in / gm;
-  const int v0 = vt * kGB;
-  const int64_t t0 = static_cast<int64_t>(mt) * kGB;
+  return GemmTile{vt, vt * kGB, static_cast<int64_t>(mt) * kGB};
+}
+
+// Persistent: block b works on XCD b % 8 through the tiles of that XCD's
+// range at stride (blocks per XCD), so the blocks resident on one XCD still
+// hold consecutive tiles.  The first two K chunks of a block's next tile are
+// loaded while the last two chunks of the current one are computed, and land
+// during its epilogue.
+__global__ __launch_bounds__(kGThreads) void lmhead_gemm_kernel(
+    const uint16_t* __restrict__ X, int64_t M, int H, const uint16_t* __restrict__ W, int V,
+    float4* __restrict__ part, int n_vt, int n_mt, int per_xcd) {
+  __shared__ __align__(16) uint16_t st0[kGStageElems];
+  __shared__ __align__(16) uint16_t st1[kGStageElems];
+  __shared__ Stat red[kGB * 2];  // [256 tokens][2 vocab waves]
+  __shared__ float4 res[kGB];    // a tile's result per token column
+  const int n_tiles = n_vt * n_mt;
+  const int xcd = blockIdx.x % kXcds, slots = gridDim.x / kXcds;
+  const int tbase = xcd * per_xcd;
+  int it = blockIdx.x / kXcds;  // position in the XCD's range
+  if (it >= per_xcd || tbase + it >= n_tiles) return;
+  GemmTile tile = gemm_tile(tbase + it, n_vt, n_mt);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -305,8 +329,8 @@ __global__ __launch_bounds__(kGThreads) void lmhead_gemm_kernel(
       const_cast<uint16_t*>(W), 0, static_cast<int>(static_cast<int64_t>(V) * H * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rX = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(X), 0, static_cast<int>(M * H * 2), 0x00020000);
-  const uint32_t soA = static_cast<uint32_t>(v0 + 32 * wave_u) * H * 2;
-  const uint32_t soB = static_cast<uint32_t>(t0 + 32 * wave_u) * H * 2;
+  uint32_t soA = static_cast<uint32_t>(tile.v0 + 32 * wave_u) * H * 2;
+  uint32_t soB = static_cast<uint32_t>(tile.t0 + 32 * wave_u) * H * 2;
   uint16_t* const dA0 = st0 + wave_u * 4 * 512;
   uint16_t* const dB0 = st0 + kGB * kGKC + wave_u * 4 * 512;
   uint16_t* const dA1 = st1 + wave_u * 4 * 512;
@@ -321,25 +345,40 @@ __global__ __launch_bounds__(kGThreads) void lmhead_gemm_kernel(
   const int aoff = (wv * 128 + q) * kGKC;
   const int boff = kGB * kGKC + (wt * 64 + q) * kGKC;
 
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
+  // H is a multiple of 2 * kGKC, so a tile has an even number of chunks and
+  // its chunk 0 always sits in st0
   const int nk = H / kGKC;
   gemm_dma(rW, rX, soA, soB, rs_bytes, offE, offO, dA0, dB0);
-  if (nk > 1) {
-    gemm_dma(rW, rX, soA + 2 * kGKC, soB + 2 * kGKC, rs_bytes, offE, offO, dA1, dB1);
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(8));
-  } else {
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-  }
+  gemm_dma(rW, rX, soA + 2 * kGKC, soB + 2 * kGKC, rs_bytes, offE, offO, dA1, dB1);
+  __builtin_amdgcn_s_waitcnt(vm_wait_imm(8));
   __builtin_amdgcn_s_barrier();
-  bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
-  gemm_frags(st0 + aoff, st0 + boff, so[0], fa0, fb0);
+
+  // the previous tile's result waits in res until the next tile is under way
+  bool pend = false;
+  GemmTile prev = tile;
+
+  while (true) {
+    const int in = it + slots;
+    const bool has_next = in < per_xcd && tbase + in < n_tiles;
+    GemmTile nt = tile;
+    uint32_t nsoA = 0, nsoB = 0;
+    if (has_next) {
+      nt = gemm_tile(tbase + in, n_vt, n_mt);
+      nsoA = static_cast<uint32_t>(nt.v0 + 32 * wave_u) * H * 2;
+      nsoB = static_cast<uint32_t>(nt.t0 + 32 * wave_u) * H * 2;
+    }
+    if (pend && tid < kGB && prev.t0 + tid < M) part[(prev.t0 + tid) * n_vt + prev.vt] = res[tid];
+    pend = false;
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
+    gemm_frags(st0 + aoff, st0 + boff, so[0], fa0, fb0);
 
 #define SPRINT_GEMM_STEP(CUR, NXT, DA, DB, U)                                                \
   {                                                                                          \
@@ -359,80 +398,92 @@ __global__ __launch_bounds__(kGThreads) void lmhead_gemm_kernel(
       if (kc + 2 < nk) {                                                                     \
         const uint32_t k2 = 2u * (kc + 2) * kGKC;                                            \
         gemm_dma(rW, rX, soA + k2, soB + k2, rs_bytes, offE, offO, DA, DB);                  \
+      } else if (has_next) {                                                                 \
+        const uint32_t k2 = 2u * (kc + 2 - nk) * kGKC;                                       \
+        gemm_dma(rW, rX, nsoA + k2, nsoB + k2, rs_bytes, offE, offO, DA, DB);                \
       }                                                                                      \
       if (kc + 1 < nk) gemm_frags(NXT + aoff, NXT + boff, so[0], fa0, fb0);                  \
       gemm_mma8(fa1, fb1, acc);                                                              \
     }                                                                                        \
   }
-  for (int kb = 0; kb < nk; kb += 2) {
-    SPRINT_GEMM_STEP(st0, st1, dA0, dB0, 0)
-    SPRINT_GEMM_STEP(st1, st0, dA1, dB1, 1)
-  }
+    for (int kb = 0; kb < nk; kb += 2) {
+      SPRINT_GEMM_STEP(st0, st1, dA0, dB0, 0)
+      SPRINT_GEMM_STEP(st1, st0, dA1, dB1, 1)
+    }
 #undef SPRINT_GEMM_STEP
-  __syncthreads();
 
-  // Epilogue: per token column fold this wave's 128 vocabulary rows, then
-  // the partner half-wave, then the other vocabulary wave through LDS.
-  // Per column a lane holds 64 logits (4 tiles x 16); rows ascend with
-  // (i, r).  One max, the lowest row holding it (scanning down, so the last
-  // match written is the lowest row), then one pass of raw exp2 (arguments
-  // <= 0) for the sum.  Rows past V exist only in the last vocabulary tile
-  // and are masked to -inf there.
-  const int vbase = v0 + wv * 128 + 4 * hh;
-  if (v0 + kGB > V) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (vbase + i * 32 + 8 * (r >> 2) + (r & 3) >= V) acc[i][j][r] = -INFINITY;
-  }
-  Stat* red = reinterpret_cast<Stat*>(st0);   // [256 tokens][2 vocab waves]
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
-    int am = INT_MAX;
-#pragma unroll
-    for (int i = 3; i >= 0; --i)
-#pragma unroll
-      for (int r = 15; r >= 0; --r)
-        am = acc[i][j][r] == mx ? vbase + i * 32 + 8 * (r >> 2) + (r & 3) : am;
-    float sum = 0.f;
-    if (mx != -INFINITY) {
-      const float ml = mx * kLog2e;
+    // Epilogue: per token column fold this wave's 128 vocabulary rows, then
+    // the partner half-wave, then the other vocabulary wave through LDS.
+    // Per column a lane holds 64 logits (4 tiles x 16); rows ascend with
+    // (i, r).  One max, the lowest row holding it (scanning down, so the last
+    // match written is the lowest row), then one pass of raw exp2 (arguments
+    // <= 0) for the sum.  Rows past V exist only in the last vocabulary tile
+    // and are masked to -inf there.
+    const int vbase = tile.v0 + wv * 128 + 4 * hh;
+    if (tile.v0 + kGB > V) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          sum += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -ml));
-    } else {
-      am = INT_MAX;
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (vbase + i * 32 + 8 * (r >> 2) + (r & 3) >= V) acc[i][j][r] = -INFINITY;
     }
-    Stat st{mx, sum, am};
-    Stat other;
-    other.m = shfl_xor_f(st.m, 32);
-    other.s = shfl_xor_f(st.s, 32);
-    other.a = shfl_xor_i(st.a, 32);
-    if (hh == 0) {
-      merge(st, other);
-      red[(wt * 64 + j * 32 + q) * 2 + wv] = st;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+      int am = INT_MAX;
+#pragma unroll
+      for (int i = 3; i >= 0; --i)
+#pragma unroll
+        for (int r = 15; r >= 0; --r)
+          am = acc[i][j][r] == mx ? vbase + i * 32 + 8 * (r >> 2) + (r & 3) : am;
+      float sum = 0.f;
+      if (mx != -INFINITY) {
+        const float ml = mx * kLog2e;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sum += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -ml));
+      } else {
+        am = INT_MAX;
+      }
+      Stat st{mx, sum, am};
+      Stat other;
+      other.m = shfl_xor_f(st.m, 32);
+      other.s = shfl_xor_f(st.s, 32);
+      other.a = shfl_xor_i(st.a, 32);
+      if (hh == 0) {
+        merge(st, other);
+        red[(wt * 64 + j * 32 + q) * 2 + wv] = st;
+      }
     }
-  }
-  __syncthreads();
-  if (tid < kGB) {
-    const int c = tid;                        // 256 token columns
-    const int64_t tok = t0 + c;
-    if (tok < M) {
+    __syncthreads();
+    if (tid < kGB) {
+      const int c = tid;  // 256 token columns
       Stat st = red[c * 2 + 0];
       merge(st, red[c * 2 + 1]);
-      part[tok * n_vt + vt] = make_float4(st.m, st.s, __int_as_float(st.a), 0.f);
+      res[c] = make_float4(st.m, st.s, __int_as_float(st.a), 0.f);
     }
+    pend = true;
+    prev = tile;
+    if (!has_next) break;
+    // the next tile's chunks 0 and 1 were loaded into st0 and st1 during the
+    // last two chunks; red and res are next written after this tile's
+    // barriers, res read by the same threads that wrote it
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_zero_imm());
+    __builtin_amdgcn_s_barrier();
+    it = in;
+    tile = nt;
+    soA = nsoA;
+    soB = nsoB;
   }
+  if (tid < kGB && prev.t0 + tid < M) part[(prev.t0 + tid) * n_vt + prev.vt] = res[tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -926,7 +977,14 @@ hipError_t launch_lmhead(const void* X, int64_t M, int H, const void* W, int V, 
   } else if (gemm_path(M, H, V, dtype)) {
     const int n_mt = static_cast<int>((M + kGB - 1) / kGB);
     const int per_xcd = (n_vt * n_mt + kXcds - 1) / kXcds;
-    lmhead_gemm_kernel<<<dim3(per_xcd * kXcds), dim3(kGThreads), 0, st>>>(
+    // one block per CU (the stages take most of the LDS), at most one per tile
+    int dev = 0, cus = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int slots = std::max(1, std::min(cus / kXcds, per_xcd));
+    lmhead_gemm_kernel<<<dim3(slots * kXcds), dim3(kGThreads), 0, st>>>(
         static_cast<const uint16_t*>(X), M, H, static_cast<const uint16_t*>(W), V, part, n_vt,
         n_mt, per_xcd);
     e = hipGetLastError();
