@@ -614,37 +614,55 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttnArgs args) {
   for (int c = 0; c < 8; ++c) acc[c] = 0.f;
   for (int base = sg; base < args.n_splits; base += kSG * kNB) {
     float ms[kNB], ls[kNB], mul[kNB], v[kNB][8];
+    // Every load of the batch is issued unconditionally (a range past the
+    // last reads range 0's row, which exists) and the values are selected
+    // afterwards: loads under a per-lane condition compile to branches that
+    // wait for each load before issuing the next.
+    // (m, l) and 2^e are loaded apart: a 16-byte load whose last word is
+    // never read lets that register be reused at once, which waits for the
+    // load.
+    bool okv[kNB];
+    float2 mlv[kNB];
+    float mulv[kNB];
+    u32x4 hv0[kNB], hv1[kNB];
 #pragma unroll
     for (int u = 0; u < kNB; ++u) {
       const int sp = base + kSG * u;
-      const bool ok = sp < args.n_splits;
-      const int64_t prow = row0 + static_cast<int64_t>(ok ? sp : 0) * rstride;
-      const f32x4 ml = ok ? *reinterpret_cast<const f32x4*>(args.part_ml + prow * 4)
-                          : f32x4{-INFINITY, 0.f, 0.f, 0.f};
-      ms[u] = ml[0];
-      ls[u] = ml[1];
-      mul[u] = ml[2];
+      okv[u] = sp < args.n_splits;
+      const int64_t prow = row0 + static_cast<int64_t>(okv[u] ? sp : 0) * rstride;
+      mlv[u] = *reinterpret_cast<const float2*>(args.part_ml + prow * 4);
+      mulv[u] = args.part_ml[prow * 4 + 2];
       if constexpr (kBf16) {
-        const u32x4 h = ok ? ld16(static_cast<const half_t*>(args.part_o) + prow * D + d)
-                           : u32x4{0u, 0u, 0u, 0u};
-        const f16x8 hv = __builtin_bit_cast(f16x8, h);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) v[u][c] = static_cast<float>(hv[c]);
+        hv0[u] = ld16(static_cast<const half_t*>(args.part_o) + prow * D + d);
       } else {
         const float* src = static_cast<const float*>(args.part_o) + prow * D + d;
-        const u32x4 a = ok ? ld16(src) : u32x4{0u, 0u, 0u, 0u};
-        const u32x4 b = ok ? ld16(src + 4) : u32x4{0u, 0u, 0u, 0u};
+        hv0[u] = ld16(src);
+        hv1[u] = ld16(src + 4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kNB; ++u) {
+      ms[u] = okv[u] ? mlv[u].x : -INFINITY;
+      ls[u] = okv[u] ? mlv[u].y : 0.f;
+      mul[u] = mulv[u];
+      if constexpr (kBf16) {
+        const f16x8 hv = __builtin_bit_cast(f16x8, hv0[u]);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[u][c] = okv[u] ? static_cast<float>(hv[c]) : 0.f;
+      } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          v[u][c] = __uint_as_float(a[c]);
-          v[u][4 + c] = __uint_as_float(b[c]);
+          v[u][c] = okv[u] ? __uint_as_float(hv0[u][c]) : 0.f;
+          v[u][4 + c] = okv[u] ? __uint_as_float(hv1[u][c]) : 0.f;
         }
       }
     }
+    // no early exit when every range so far is empty (mb = -inf): it would
+    // make the partials' loads wait for the (m, l) loads; empty ranges
+    // already get weight 0 and leave m at -inf
     float mb = m;
 #pragma unroll
     for (int u = 0; u < kNB; ++u) mb = fmaxf(mb, ms[u]);
-    if (mb == -INFINITY) continue;              // only empty ranges so far
     const float a = m == -INFINITY ? 0.f : exp2f(m - mb);
     l *= a;
 #pragma unroll
