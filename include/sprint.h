@@ -124,6 +124,8 @@ int sprint_score(const void* K, const float* conf, const int32_t* cu_len, int32_
  * the kernels never write outside [cu_kept[s], cu_kept[s+1]) or total_kept.
  * Scores are ranked as IEEE values (-0 equal to +0); NaN scores, and modality
  * bytes other than 0 and 1, have no defined ranking.
+ * K_out and V_out (per layer) must be under 2 GiB each: total_kept * Hkv * D *
+ * element size >= 2^31 returns SPRINT_EUNSUPPORTED.
  * ------------------------------------------------------------------------ */
 size_t sprint_prune_kv_ws(int64_t total_L, int32_t nseq);
 int sprint_prune_kv(const float* score, const uint8_t* modality, const int32_t* cu_len,
@@ -206,7 +208,8 @@ int sprint_prune_kv_per_layer(const float* score, const uint8_t* modality, const
  *   Kb, Vb [nseq, Lq, Hkv, D] dtype, or both NULL for prefix-only attention
  *   scale  softmax scale, finite and > 0 (usually 1/sqrt(D))
  *   O      [nseq, Lq, Hq, D] dtype out (bf16 rounded to nearest even)
- * Supports D in {64, 128}, Hq % Hkv == 0, (Hq/Hkv)*Lq <= 256, Lq <= 64.
+ * Supports D in {64, 128}, Hq % Hkv == 0, (Hq/Hkv)*Lq <= 256, Lq <= 64, and
+ * Kp, Vp, Kb, Vb each under 2 GiB (SPRINT_EUNSUPPORTED otherwise).
  * Every (sequence) must have at least one key (cache length + block >= 1).
  * Partial results of key ranges are kept in ws in fp32 (fp32 inputs) or in
  * fp16 with a power-of-two scale per row (bf16 inputs), so every finite bf16

@@ -17,6 +17,13 @@ bool dev16(const void* p) { return p != nullptr && aligned(p, 16); }
 bool dev4(const void* p) { return p != nullptr && aligned(p, 4); }
 bool dtype_ok(int32_t dt) { return dt == SPRINT_F32 || dt == SPRINT_BF16; }
 bool head_dim_ok(int32_t D) { return D == 64 || D == 128; }
+// Arrays that kernels address through 32-bit buffer offsets stay below 2 GiB.
+bool under_2gib(int64_t rows, int64_t row_bytes) {
+  return rows * row_bytes < (static_cast<int64_t>(1) << 31);
+}
+int64_t kv_row_bytes(int32_t Hkv, int32_t D, int32_t dtype) {
+  return static_cast<int64_t>(Hkv) * D * (dtype == SPRINT_BF16 ? 2 : 4);
+}
 int status_of(hipError_t e) { return e == hipSuccess ? SPRINT_OK : SPRINT_EHIP; }
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
@@ -157,6 +164,8 @@ static int prune_impl(const float* score, const uint8_t* modality, const int32_t
   if (total_kept < 0 || total_kept > total_L) return SPRINT_EINVAL;
   if (!dev4(cu_len) || !dev4(keep) || !dev4(cu_kept)) return SPRINT_EINVAL;
   if (!head_dim_ok(D)) return SPRINT_EUNSUPPORTED;
+  // the pruned cache of a layer is written through 32-bit buffer offsets
+  if (!under_2gib(total_kept, kv_row_bytes(Hkv, D, dtype))) return SPRINT_EUNSUPPORTED;
   if (total_L > 0 && (!dev4(score) || modality == nullptr || !dev16(K) || !dev16(V)))
     return SPRINT_EINVAL;
   if (total_kept > 0 && (!dev16(K_out) || !dev16(V_out) || !dev4(kept_idx))) return SPRINT_EINVAL;
@@ -231,6 +240,10 @@ static int attend_check(const void* Q, int32_t nseq, int32_t Lq, int32_t Hq, con
   if (ss != SPRINT_OK) return ss;
   if (total_kv < 0 || total_kv > INT32_MAX || !isfinite(scale) || !(scale > 0.f))
     return SPRINT_EINVAL;
+  // K/V tiles are loaded through 32-bit buffer offsets
+  const int64_t row = kv_row_bytes(Hkv, D, dtype);
+  if (!under_2gib(total_kv, row) || !under_2gib(static_cast<int64_t>(nseq) * Lq, row))
+    return SPRINT_EUNSUPPORTED;
   // one sequence's cache is all of [0, total_kv), which max_kv must cover
   if (nseq == 1 && total_kv > max_kv) return SPRINT_EINVAL;
   if (!dev16(Q) || !dev16(O) || !dev4(cu_kv)) return SPRINT_EINVAL;

@@ -632,31 +632,40 @@ __global__ __launch_bounds__(kCopyThreads) void compact_kernel(
   const int64_t slot0 = s_slot0, limit = s_limit;
   const int64_t row_bytes = static_cast<int64_t>(row_vecs) * 16;
   const int units = nk * row_vecs;
-  // four 16-byte vectors of K and of V per thread in flight per round; the
-  // source rows are read once (non-temporal), the pruned cache is written
-  // with ordinary stores since the denoising steps read it next
+  // Four 16-byte vectors of K and of V per thread in flight per round.  The
+  // source rows are read once (non-temporal); the pruned cache is written
+  // with ordinary-policy buffer stores, since the denoising steps read it
+  // next.  Nothing is branched: a unit past the chunk's last reads that last
+  // unit, and a store that must not happen goes to an offset past the end of
+  // the output resource, which the hardware drops.  (Loads or stores under a
+  // per-lane condition compile to branches that wait for each load in turn.)
+  const uint32_t out_bytes = static_cast<uint32_t>(total_kept * row_bytes);  // < 2^31 (host)
+  const __amdgpu_buffer_rsrc_t rKo =
+      __builtin_amdgcn_make_buffer_rsrc(K_out, 0, static_cast<int>(out_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rVo =
+      __builtin_amdgcn_make_buffer_rsrc(V_out, 0, static_cast<int>(out_bytes), 0x00020000);
+  constexpr uint32_t kDrop = 0x80000000u;  // past every output resource
   constexpr int kU = 4;
   for (int u0 = threadIdx.x; u0 < units; u0 += kU * kCopyThreads) {
     u32x4 kv[kU], vv[kU];
-    int64_t dst[kU];
-    bool ok[kU];
+    uint32_t dst[kU];
 #pragma unroll
     for (int i = 0; i < kU; ++i) {
       const int u = u0 + i * kCopyThreads;
-      const int r = u / row_vecs, v = u - r * row_vecs;
+      const int uc = u < units ? u : units - 1;
+      const int r = uc / row_vecs, v = uc - r * row_vecs;
       const int64_t slot = slot0 + r;
-      ok[i] = u < units && slot >= 0 && slot < limit;
-      const int64_t src = ok[i] ? s_pos[r] * row_bytes + v * 16 : 0;
-      dst[i] = slot * row_bytes + v * 16;
-      kv[i] = ok[i] ? ld16_nt(K + src) : u32x4{0u, 0u, 0u, 0u};
-      vv[i] = ok[i] ? ld16_nt(V + src) : u32x4{0u, 0u, 0u, 0u};
+      const bool ok = u < units && slot >= 0 && slot < limit;
+      const int64_t src = s_pos[r] * row_bytes + v * 16;
+      dst[i] = ok ? static_cast<uint32_t>(slot * row_bytes + v * 16) : kDrop;
+      kv[i] = ld16_nt(K + src);
+      vv[i] = ld16_nt(V + src);
     }
 #pragma unroll
-    for (int i = 0; i < kU; ++i)
-      if (ok[i]) {
-        st16(K_out + dst[i], kv[i]);
-        st16(V_out + dst[i], vv[i]);
-      }
+    for (int i = 0; i < kU; ++i) {
+      __builtin_amdgcn_raw_buffer_store_b128(kv[i], rKo, static_cast<int>(dst[i]), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(vv[i], rVo, static_cast<int>(dst[i]), 0, 0);
+    }
   }
 }
 

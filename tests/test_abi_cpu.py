@@ -102,6 +102,10 @@ def test_score_and_prune_reject_before_hip():
     assert _call("sprint_prune_kv", *a) == 1                        # NULL K_out
     a = list(pr); a[17] = 1
     assert _call("sprint_prune_kv", *a) == 3
+    a = list(pr); a[6] = 1 << 22; a[7] = 1 << 21
+    assert _call("sprint_prune_kv", *a) == 2                        # 2 GiB pruned cache
+    a = list(pr); a[6] = 1 << 22; a[7] = (1 << 21) - 1; a[17] = 1
+    assert _call("sprint_prune_kv", *a) == 3                        # just under: passes to ws
 
 
 def test_per_layer_score_and_prune_reject_before_hip():
@@ -144,6 +148,10 @@ def test_attend_and_unmask_reject_before_hip():
     assert _call("block_attend", *a) == 1                           # one sequence longer than max_kv
     a = list(at); a[17] = 8
     assert _call("block_attend", *a) == 3
+    a = list(at); a[7] = 1 << 21; a[8] = 1 << 21
+    assert _call("block_attend", *a) == 2                           # 2 GiB of K rows
+    a = list(at); a[7] = (1 << 21) - 1; a[8] = (1 << 21) - 1; a[17] = 8
+    assert _call("block_attend", *a) == 3                           # just under: passes to ws
     # the workspace-free variant: same checks, and a plan whose partials
     # exceed its 16 MiB array is refused (fp32, 4 sequences of up to 2^20 keys)
     na = at[:16] + [None]
