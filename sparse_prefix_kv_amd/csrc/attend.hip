@@ -586,17 +586,19 @@ void attend_split_kernel(AttnArgs args) {
 
 // Combine the key ranges: one wave per output row (of one sequence and KV
 // head).  A lane owns 8 columns and every (64/(D/8))-th range, so all of its
-// loads for a batch of eight ranges are in flight together; it folds them
+// loads for a batch of NB ranges are in flight together; it folds them
 // with the running (m, l) in log2 units, then a butterfly over the lanes
 // that share its columns merges the range groups.  The fold order is fixed,
-// so the result is bitwise reproducible.
-template <typename T, int D>
+// so the result is bitwise reproducible.  NB = 16 when one batch of 8 would
+// not cover every range, so that up to 64 (D = 128) or 128 (D = 64) ranges
+// take one memory round trip instead of two.
+template <typename T, int D, int NB>
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttnArgs args) {
   using S = typename T::storage;
   constexpr bool kBf16 = sizeof(S) == 2;
   constexpr int kCL = D / 8;        // lanes across the columns
   constexpr int kSG = 64 / kCL;     // lanes across the ranges
-  constexpr int kNB = 8;            // ranges per lane per batch
+  constexpr int kNB = NB;           // ranges per lane per batch
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n_rb = (args.R + 3) / 4;
   const int rb = blockIdx.x % n_rb;
@@ -738,7 +740,11 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t st) {
     e = launch_split<T, D, 8>(a, st);
   if (e != hipSuccess || a.n_splits == 1) return e;
   const int blocks = a.nseq * a.Hkv * ((a.R + 3) / 4);
-  attend_combine_kernel<T, D><<<dim3(blocks), dim3(256), 0, st>>>(a);
+  constexpr int kSG = 64 / (D / 8);  // lanes across the ranges
+  if (a.n_splits > kSG * 8)
+    attend_combine_kernel<T, D, 16><<<dim3(blocks), dim3(256), 0, st>>>(a);
+  else
+    attend_combine_kernel<T, D, 8><<<dim3(blocks), dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -334,6 +334,15 @@ def test_attend_full_size(kv_lens):
     _attend_case("bf16", 16, 4, 128, 32, kv_lens, True, 80)
 
 
+@pytest.mark.parametrize("dtype,Hq,D,kv_len", [("f32", 2, 64, 20000), ("bf16", 4, 64, 12000),
+                                                ("f32", 4, 128, 6000), ("bf16", 2, 128, 20000)])
+def test_attend_many_key_ranges(dtype, Hq, D, kv_len):
+    """One KV head, so the plan cuts the cache into 48-157 key ranges of 128
+    keys: the combine folds them in batches of 16 per lane, one to three
+    batches deep."""
+    _attend_case(dtype, Hq, 1, D, 32, [kv_len], True, 85)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_attend_max_kv_below_a_sequence(dtype):
     """max_kv only sizes the split of each cache: with three sequences, two of
