@@ -35,6 +35,7 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kRegChunks = 2;      // 16-position chunks of keys held per thread
+constexpr int kFewKeys = 64;       // keys under the prefix one wave ranks directly
 constexpr int kChunk = 64;
 constexpr int kCopyThreads = 256;
 
@@ -197,9 +198,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
   __shared__ int s_found;
   __shared__ int64_t s_cut;
   __shared__ uint32_t s_min[kSelThreads / 64], s_max[kSelThreads / 64];
+  __shared__ uint32_t s_cand[kFewKeys];
+  __shared__ int s_ncand;
+  __shared__ uint32_t s_sel[3];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < 256 * kHistCopies; i += kSelThreads) hist[i] = 0;
   s_cc[threadIdx.x] = 0;
+  if (threadIdx.x == 0) s_ncand = 0;
   {
     // chunk id of the sequence's first chunk: chunks of the earlier ones
     int acc = 0;
@@ -392,6 +397,51 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_kernel(
         prefix |= static_cast<uint32_t>(w.digit) << shift;
         pmask |= dmask << shift;
         hi = shift - 1;
+        if (hi >= 0 && ties <= kFewKeys) {
+          // At most 64 keys left under the prefix: one wave ranks them
+          // directly instead of further radix windows.  The key holding
+          // rank krem among them (gt keys above it, eq equal to it, with
+          // gt < krem <= gt + eq) is the threshold.
+#pragma unroll
+          for (int j = 0; j < kRegChunks; ++j) {
+            if (!act[j]) continue;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const uint32_t kk = key[j * 16 + i];
+              if (kk != 0u && (kk & pmask) == prefix) {
+                const int slot = atomicAdd(&s_ncand, 1);
+                if (slot < kFewKeys) s_cand[slot] = kk;
+              }
+            }
+          }
+          __syncthreads();
+          if (wave == 0) {
+            const int nk = min(__builtin_amdgcn_readfirstlane(s_ncand), kFewKeys);
+            const uint32_t v = lane < nk ? s_cand[lane] : 0u;
+            int gt = 0, eq = 0;
+            for (int i = 0; i < nk; ++i) {
+              const uint32_t u = __builtin_amdgcn_readlane(v, i);
+              gt += u > v ? 1 : 0;
+              eq += u == v ? 1 : 0;
+            }
+            const uint64_t hit = __ballot(lane < nk && gt < krem && krem <= gt + eq);
+            const int src = hit ? __builtin_ctzll(hit) : 0;
+            const uint32_t t = __builtin_amdgcn_readlane(v, src);
+            const int tg = __builtin_amdgcn_readlane(gt, src);
+            const int te = __builtin_amdgcn_readlane(eq, src);
+            if (lane == 0) {
+              s_sel[0] = t;
+              s_sel[1] = static_cast<uint32_t>(tg);
+              s_sel[2] = static_cast<uint32_t>(te);
+            }
+          }
+          __syncthreads();
+          prefix = s_sel[0];
+          pmask = 0xFFFFFFFFu;
+          krem -= static_cast<int>(s_sel[1]);
+          ties = static_cast<int>(s_sel[2]);
+          break;
+        }
       }
       if (krem < ties) {
         // Tie cut: the krem-th position, in position order, whose key is the

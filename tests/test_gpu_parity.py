@@ -220,6 +220,29 @@ def test_prune_small(li, levels, dtype, Hkv, D):
         _run_prune(score, lay, keep, K, V, dtype)
 
 
+@pytest.mark.parametrize("nbin", [1, 2, 63, 64, 65])
+@pytest.mark.parametrize("dup", [False, True])
+def test_prune_few_keys_left_under_the_prefix(nbin, dup):
+    """Scores in [1, 2): the keys first differ at the mantissa's top bit, so
+    the first radix window bins mantissa bits 22..15.  `nbin` scores share
+    bin 0x80 ([1.5, 1.5 + 2^-9), up to 2^11 steps of 2^-20, or 8 steps for
+    many duplicates), 300 lie above it and 500 below.  The k-th largest
+    falls inside the bin (or at its edges), where 64 keys or fewer are
+    ranked directly instead of by more windows."""
+    rng = np.random.default_rng(100 + 2 * nbin + dup)
+    above = rng.uniform(1.6, 1.99, 300)
+    below = rng.uniform(1.0, 1.45, 500)
+    inbin = 1.5 + rng.integers(0, 8 if dup else 1 << 11, nbin) * 2.0 ** -20
+    score = np.concatenate([above, inbin, below]).astype(np.float32)
+    score = score[rng.permutation(len(score))]
+    n = len(score)
+    lay = synth.layout_from_runs([((1, n),)])
+    K = synth.normal_array((n, 1, 64), 61, 1.0, "f32")
+    V = synth.normal_array((n, 1, 64), 62, 1.0, "f32")
+    for k in sorted({299, 300, 301, 300 + (nbin + 1) // 2, 300 + nbin, 301 + nbin}):
+        _run_prune(score, lay, [[0, k]], K, V, "f32")
+
+
 def test_prune_all_equal_scores_keep_lowest():
     lay = synth.layout_from_runs([((0, 50), (1, 3000))])
     got = _run_prune(np.ones(3050, np.float32), lay, [[10, 2000]],
