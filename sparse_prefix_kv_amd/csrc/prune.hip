@@ -15,8 +15,11 @@
 //                             thread) for every radix window; the histogram
 //                             has a copy per lane so that keys crowding into
 //                             few digits do not serialize the LDS atomics;
-//                             each block also writes its modality's kept
-//                             count of every 64-position chunk;
+//                             once at most 64 keys share the prefix, one
+//                             wave ranks them directly instead of further
+//                             windows; each block also writes its
+//                             modality's kept count of every 64-position
+//                             chunk;
 //   2. compact_kernel         per chunk: prefix of earlier chunk counts in the
 //                             sequence -> output slots; writes kept_idx and
 //                             copies the K and V rows (16-byte vectors), of
