@@ -243,6 +243,45 @@ def test_prune_few_keys_left_under_the_prefix(nbin, dup):
         _run_prune(score, lay, [[0, k]], K, V, "f32")
 
 
+def _random_scores(rng, n, kind):
+    if kind == "uniform":
+        return rng.uniform(0.0, 2.0, n)
+    if kind == "signed_wide":
+        return rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 3, n)
+    if kind == "levels":
+        return rng.integers(0, int(rng.integers(2, 40)), n) * 0.25
+    # clustered: one value plus noise a few ulps wide, so the radix windows
+    # run deep and the last bins hold a few keys with near ties
+    base = rng.uniform(0.5, 4.0)
+    return base + rng.integers(-200, 200, n) * np.spacing(np.float32(base))
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_prune_random_distributions(case):
+    """Random layouts (1-4 sequences, runs of both modalities, empty ones
+    included), score distributions and keep ratios; the kept set bit for bit
+    against the oracle."""
+    rng = np.random.default_rng(1000 + case)
+    nseq = int(rng.integers(1, 5))
+    runs = []
+    for _ in range(nseq):
+        seq = tuple((int(rng.integers(0, 2)), int(rng.integers(0, 3000)))
+                    for _ in range(int(rng.integers(0, 4))))
+        runs.append(seq)
+    if sum(length for seq in runs for _, length in seq) == 0:
+        runs[0] = ((1, 500),)          # at least one position; empty sequences stay
+    lay = synth.layout_from_runs(runs)
+    n = lay.total_L
+    kind = ["uniform", "signed_wide", "levels", "clustered"][case % 4]
+    score = _random_scores(rng, n, kind).astype(np.float32)
+    K = synth.normal_array((n, 1, 64), 63, 1.0, "f32")
+    V = synth.normal_array((n, 1, 64), 64, 1.0, "f32")
+    rt, ri = rng.uniform(0, 1, 2)
+    keep = [[oracle.keep_count(rt, lay.n_text[s]), oracle.keep_count(ri, lay.n_img[s])]
+            for s in range(lay.nseq)]
+    _run_prune(score, lay, keep, K, V, "f32")
+
+
 def test_prune_all_equal_scores_keep_lowest():
     lay = synth.layout_from_runs([((0, 50), (1, 3000))])
     got = _run_prune(np.ones(3050, np.float32), lay, [[10, 2000]],
