@@ -109,6 +109,27 @@ def test_lmhead_full_size_sampled(M, V):
     _check_lmhead(X, W, _np(conf), _np(amax), _np(lse), rows)
 
 
+@pytest.mark.parametrize("case", range(16))
+def test_lmhead_random_shapes(case):
+    """Random token counts (one row to several token tiles), hidden sizes
+    (multiples of 64) and vocabulary sizes, in both dtypes: the per-step ring
+    (M <= 64), the persistent XCD-grouped GEMM with tile counts that leave
+    remainders across the eight XCDs, and the fallbacks for other hidden
+    sizes, against the oracle."""
+    rng = np.random.default_rng(4000 + case)
+    dtype = ["bf16", "f32"][case % 2]
+    M = int(rng.choice([1, 7, 32, 33, 64, 65, 200, 513, 1500]))
+    H = 64 * int(rng.integers(1, 33))
+    if dtype == "bf16" and M > 64:
+        H = 256 * max(1, H // 256)                 # the tiled GEMM's hidden sizes
+    V = int(rng.integers(100, max(101, min(40000, 20_000_000 // M))))
+    X = synth.normal_array((M, H), 5000 + case, 1.0, dtype)
+    W = synth.normal_array((V, H), 6000 + case, 0.02, dtype)
+    conf, amax, lse = sprint.lmhead_confidence(_to_dev(X, dtype, DEV), _to_dev(W, dtype, DEV),
+                                               want_lse=True)
+    _check_lmhead(X, W, _np(conf), _np(amax), _np(lse))
+
+
 @pytest.mark.parametrize("M,V", [(32768, 163840), (76375, 65536)])
 def test_lmhead_prefix_large_sampled(M, V):
     """The prefix-wide LM head at the long-prefix shapes: 32768 prefix rows
@@ -452,6 +473,26 @@ def test_attend_value_scale_is_exact_across_splits(kv_lens):
                                  Vb_d * f)
         assert torch.isfinite(Ob.float()).all()
         assert torch.equal(Ob, (O1.float() * f).to(torch.bfloat16)), e
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_attend_random_shapes(case):
+    """Random GQA ratios, block lengths, head sizes, sequence counts and
+    cache lengths (up to 6000 keys, empty caches included when the block's
+    own keys are attended), in both dtypes, against the oracle."""
+    rng = np.random.default_rng(2000 + case)
+    dtype = ["bf16", "f32"][case % 2]
+    D = [64, 128][(case // 2) % 2]
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Lq = int(rng.choice([1, 5, 16, 32, 64]))
+    while G * Lq > 256:
+        Lq //= 2
+    block = bool(rng.integers(0, 2))
+    kv_lens = [int(v) for v in rng.integers(0, 6001, int(rng.integers(1, 5)))]
+    if not block:
+        kv_lens = [max(v, 1) for v in kv_lens]
+    _attend_case(dtype, G * Hkv, Hkv, D, Lq, kv_lens, block, 3000 + case)
 
 
 def test_attend_full_retention_equals_unpruned():
