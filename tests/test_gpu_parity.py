@@ -181,6 +181,24 @@ def test_score_small_ragged(dtype, Hkv, D):
     _check_score(K, conf, cu, dtype, Hkv, D, alpha=0.25)
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_score_random_shapes(case):
+    """Random sequence counts and lengths (empty ones included), KV heads,
+    head sizes, dtypes and blend weights against the oracle."""
+    rng = np.random.default_rng(8000 + case)
+    dtype = ["bf16", "f32"][case % 2]
+    Hkv, D = int(rng.choice([1, 2, 3, 4, 8])), int(rng.choice([64, 128]))
+    lens = [int(v) for v in rng.integers(0, 5000, int(rng.integers(1, 6)))]
+    lens[int(rng.integers(0, len(lens)))] += 1                 # at least one position
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    K = synth.lognormal_rows(synth.normal_array((cu[-1], Hkv, D), 8100 + case, 1.0, "f32"),
+                             8200 + case)
+    if dtype == "bf16":
+        K = synth.bf16_round(K)
+    conf = synth.random_scores(cu[-1], 8300 + case) / 2
+    _check_score(K, conf, cu, dtype, Hkv, D, alpha=float(rng.choice([0.5, 0.25, 0.9])))
+
+
 def test_score_zero_keys():
     cu = np.array([0, 10, 30], np.int32)
     K = np.zeros((30, 4, 128), np.float32)
@@ -522,6 +540,30 @@ def test_unmask_parity(Lq, ties, steps_left):
                                                            tie_levels=ties)
     conf[0, :] = tau                                   # exactly tau is not accepted by '>'
     masked[1, :] = 0                                   # nothing masked
+    m_d, t_d = _u8(masked), _i32(tokens)
+    n = sprint.unmask_select(_f32(conf), _i32(amax), m_d, t_d, float(tau), steps_left)
+    m_o, t_o, n_o = oracle.unmask_select(conf, amax, masked, tokens, tau, steps_left)
+    np.testing.assert_array_equal(_np(m_d), m_o)
+    np.testing.assert_array_equal(_np(t_d), t_o)
+    np.testing.assert_array_equal(_np(n), n_o)
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_unmask_random(case):
+    """Random batches (1-16 sequences, 1-64 positions), confidence laws with
+    and without ties and values above tau, mask densities, thresholds and
+    steps left, against the oracle bit for bit."""
+    rng = np.random.default_rng(7000 + case)
+    nseq, Lq = int(rng.integers(1, 17)), int(rng.integers(1, 65))
+    tau = np.float32(rng.choice([0.5, 0.9, 0.95, 1.5]))
+    if case % 3 == 0:
+        conf = rng.integers(0, 6, (nseq, Lq)).astype(np.float32) / 5.0     # many ties
+    else:
+        conf = rng.uniform(0, 1, (nseq, Lq)).astype(np.float32)
+    amax = rng.integers(0, 50000, (nseq, Lq)).astype(np.int32)
+    masked = (rng.uniform(0, 1, (nseq, Lq)) < rng.uniform(0, 1)).astype(np.uint8)
+    tokens = np.where(masked == 1, -1, rng.integers(0, 50000, (nseq, Lq))).astype(np.int32)
+    steps_left = int(rng.choice([-2, 0, 1, 2, 5, 9, 1 << 30]))
     m_d, t_d = _u8(masked), _i32(tokens)
     n = sprint.unmask_select(_f32(conf), _i32(amax), m_d, t_d, float(tau), steps_left)
     m_o, t_o, n_o = oracle.unmask_select(conf, amax, masked, tokens, tau, steps_left)
