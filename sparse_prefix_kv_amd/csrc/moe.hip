@@ -445,12 +445,14 @@ hipError_t launch_moe(const void* x, int M, int H, const void* wr, const float* 
   if (nvh == A && nvi == B)                                                                   \
     return launch_moe_typed<T, A, B>(x, M, H, wr, bias, E, top_k, scale, wg, wu, wd, I,       \
                                      residual, y, ids, gates, ws, st);
+  // every width moe_shape_supported accepts (1-4 vectors per lane across H,
+  // 1-2 across inter) has an instantiation
   if (dtype == 1) {
-    SPRINT_MOE(BF16, 1, 1) SPRINT_MOE(BF16, 2, 1) SPRINT_MOE(BF16, 4, 1)
-    SPRINT_MOE(BF16, 1, 2) SPRINT_MOE(BF16, 2, 2) SPRINT_MOE(BF16, 4, 2)
+    SPRINT_MOE(BF16, 1, 1) SPRINT_MOE(BF16, 2, 1) SPRINT_MOE(BF16, 3, 1) SPRINT_MOE(BF16, 4, 1)
+    SPRINT_MOE(BF16, 1, 2) SPRINT_MOE(BF16, 2, 2) SPRINT_MOE(BF16, 3, 2) SPRINT_MOE(BF16, 4, 2)
   } else {
-    SPRINT_MOE(F32, 1, 1) SPRINT_MOE(F32, 2, 1) SPRINT_MOE(F32, 4, 1)
-    SPRINT_MOE(F32, 1, 2) SPRINT_MOE(F32, 2, 2) SPRINT_MOE(F32, 4, 2)
+    SPRINT_MOE(F32, 1, 1) SPRINT_MOE(F32, 2, 1) SPRINT_MOE(F32, 3, 1) SPRINT_MOE(F32, 4, 1)
+    SPRINT_MOE(F32, 1, 2) SPRINT_MOE(F32, 2, 2) SPRINT_MOE(F32, 3, 2) SPRINT_MOE(F32, 4, 2)
   }
 #undef SPRINT_MOE
   return hipErrorInvalidValue;

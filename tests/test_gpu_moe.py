@@ -70,6 +70,28 @@ def test_moe_matches_oracle(M, H, E, K, inter, dtype):
     _run(M, H, E, K, inter, dtype)
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_moe_random_shapes(case):
+    """Random supported shapes: token counts, hidden and expert widths (in
+    the units the expert kernels stream), expert counts and top-k, with and
+    without a residual and with one expert forced for every token."""
+    rng = np.random.default_rng(9000 + case)
+    dtype = ["bf16", "f32"][case % 2]
+    unit = 512 if dtype == "bf16" else 256
+    H = unit * int(rng.integers(1, 5))
+    inter = unit * int(rng.integers(1, 3))
+    E = int(rng.integers(1, 65))
+    while E * inter * H > 40_000_000:          # keep the host weights small
+        E = max(1, E // 2)
+    K = int(rng.integers(1, min(E, 16) + 1))
+    M = int(rng.integers(1, 97))
+    force = int(rng.integers(0, E)) if case % 4 == 3 else None
+    ids = _run(M, H, E, K, inter, dtype, seed=9100 + case, residual=bool(case % 3 == 0),
+               force=force)
+    if force is not None:
+        assert np.all(ids[:, 0] == force)
+
+
 def test_moe_residual_and_one_expert_for_all():
     # every token's first choice is expert 3: 40 tokens on one expert take
     # two LDS chunks in the expert kernels
