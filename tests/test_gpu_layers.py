@@ -204,3 +204,63 @@ def test_block_with_carried_confidences_matches_a_full_pass(mode):
     blk.run_block(n_steps, prefix_conf=False)
     torch.cuda.synchronize()
     assert all(torch.equal(u, v) for u, v in zip(state(), ref))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_layers_random_shapes(case):
+    """Random layouts, layer counts (1-6), KV heads, head sizes, dtypes and
+    keep ratios.  Even cases: one shared set (the layer-mean importance,
+    the scores and the kept set against the oracle, every layer's
+    compaction a bit copy); odd cases: a set per layer (the batched calls
+    equal the single-layer calls, and each set follows the oracle)."""
+    rng = np.random.default_rng(11000 + case)
+    dtype = ["bf16", "f32"][(case // 2) % 2]
+    n_layers, Hkv, D = int(rng.integers(1, 7)), int(rng.choice([1, 2, 4])), int(rng.choice([64, 128]))
+    runs = [tuple((int(rng.integers(0, 2)), int(rng.integers(1, 1500)))
+                  for _ in range(int(rng.integers(1, 4)))) for _ in range(int(rng.integers(1, 4)))]
+    lay = synth.layout_from_runs(runs)
+    n = lay.total_L
+
+    def draw(l, which):
+        a = synth.normal_array((n, Hkv, D), 11100 + 10 * case + 2 * l + which, 1.0, "f32")
+        if which == 0:
+            a = synth.lognormal_rows(a, 11500 + 10 * case + l)
+        return synth.bf16_round(a) if dtype == "bf16" else a
+    Ks = [draw(l, 0) for l in range(n_layers)]
+    K = torch.stack([_dev(k, dtype) for k in Ks])
+    V = torch.stack([_dev(draw(l, 1), dtype) for l in range(n_layers)])
+    conf_np = rng.uniform(0, 1e-3, n).astype(np.float32)
+    conf = torch.from_numpy(conf_np).to(DEV)
+    cu = torch.from_numpy(lay.cu_len.astype(np.int32)).to(DEV)
+    mod = torch.from_numpy(lay.modality).to(DEV)
+    r_text, r_img = (float(v) for v in rng.uniform(0, 1, 2))
+    keep, cu_kept, tk = sprint.sprint_plan_keep(lay.n_text, lay.n_img, r_text, r_img)
+    keep_t = torch.tensor(keep, dtype=torch.int32, device=DEV)
+    cuk_t = torch.tensor(cu_kept, dtype=torch.int32, device=DEV)
+    if case % 2 == 0:
+        ib, sc = sprint.sprint_score_layers(K, conf, cu, 0.5)
+        Kp, Vp, kept = sprint.sprint_prune_kv_layers(sc, mod, cu, keep_t, cuk_t, tk, K, V)
+        torch.cuda.synchronize()
+        ib_o = oracle.key_norm_importance_layers([_np(k) for k in K], lay.cu_len)
+        np.testing.assert_allclose(_np(ib), ib_o, rtol=1e-5, atol=1e-7)
+        np.testing.assert_allclose(_np(sc), oracle.composite_score(ib_o, conf_np, 0.5),
+                                   rtol=1e-5, atol=1e-7)
+        kept_o = oracle.select_kept(_np(sc).astype(np.float64), lay.modality, lay.cu_len,
+                                    np.asarray(keep).reshape(-1, 2))
+        np.testing.assert_array_equal(_np(kept), kept_o)
+        for l in range(n_layers):
+            Kc, Vc = oracle.compact(_np(K[l]), _np(V[l]), kept_o)
+            assert np.array_equal(_np(Kp[l]), Kc) and np.array_equal(_np(Vp[l]), Vc), l
+    else:
+        ib, sc = sprint.sprint_score_per_layer(K, conf, cu, 0.5)
+        Kp, Vp, kept = sprint.sprint_prune_kv_per_layer(sc, mod, cu, keep_t, cuk_t, tk, K, V)
+        torch.cuda.synchronize()
+        for l in range(n_layers):
+            ib1, sc1 = sprint.sprint_score(K[l], conf, cu, 0.5)
+            K1, V1, k1 = sprint.sprint_prune_kv(sc1, mod, cu, keep_t, cuk_t, tk, K[l], V[l])
+            torch.cuda.synchronize()
+            assert torch.equal(ib[l], ib1) and torch.equal(sc[l], sc1), l
+            assert torch.equal(kept[l], k1) and torch.equal(Kp[l], K1) and torch.equal(Vp[l], V1), l
+            kept_o = oracle.select_kept(_np(sc[l]).astype(np.float64), lay.modality, lay.cu_len,
+                                        np.asarray(keep).reshape(-1, 2))
+            np.testing.assert_array_equal(_np(kept[l]), kept_o)
