@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void lmhead_tile_kernel(const char* __restrict
 // ~32 blocks resident on one XCD share 4 W tiles and 8 X tiles in its L2.
 // The grid is one block per CU; a block walks its XCD's range at a stride
 // of the blocks per XCD and loads the next tile's first two chunks under the
-// current tile's last two chunks and epilogue.
+// current tile's last two chunks.
 constexpr int kGB = 256;                     // tile edge (vocab and tokens)
 constexpr int kGKC = 64;                     // reduction depth per stage
 constexpr int kGStageElems = 2 * kGB * kGKC; // A rows then B rows
@@ -295,8 +295,8 @@ __device__ __forceinline__ GemmTile gemm_tile(int t, int n_vt, int n_mt) {
 // Persistent: block b works on XCD b % 8 through the tiles of that XCD's
 // range at stride (blocks per XCD), so the blocks resident on one XCD still
 // hold consecutive tiles.  The first two K chunks of a block's next tile are
-// loaded while the last two chunks of the current one are computed, and land
-// during its epilogue.
+// loaded while the last two chunks of the current one are computed; the
+// epilogue starts once they have landed.
 __global__ __launch_bounds__(kGThreads) void lmhead_gemm_kernel(
     const uint16_t* __restrict__ X, int64_t M, int H, const uint16_t* __restrict__ W, int V,
     float4* __restrict__ part, int n_vt, int n_mt, int per_xcd) {
@@ -350,7 +350,10 @@ __global__ __launch_bounds__(kGThreads) void lmhead_gemm_kernel(
   const int nk = H / kGKC;
   gemm_dma(rW, rX, soA, soB, rs_bytes, offE, offO, dA0, dB0);
   gemm_dma(rW, rX, soA + 2 * kGKC, soB + 2 * kGKC, rs_bytes, offE, offO, dA1, dB1);
-  __builtin_amdgcn_s_waitcnt(vm_wait_imm(8));
+  // both chunks: with chunk 1 still pending on entry to the K loop, the
+  // compiler can no longer tell the two stages' DMA apart and would wait
+  // for every load at the loop head
+  __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
   __builtin_amdgcn_s_barrier();
 
   // the previous tile's result waits in res until the next tile is under way
@@ -412,6 +415,9 @@ __global__ __launch_bounds__(kGThreads) void lmhead_gemm_kernel(
     }
 #undef SPRINT_GEMM_STEP
 
+    // the next tile's first two chunks land before the epilogue starts
+    // (measured faster than running the epilogue under them)
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
     // Epilogue: per token column fold this wave's 128 vocabulary rows, then
     // the partner half-wave, then the other vocabulary wave through LDS.
     // Per column a lane holds 64 logits (4 tiles x 16); rows ascend with
@@ -436,12 +442,17 @@ __global__ __launch_bounds__(kGThreads) void lmhead_gemm_kernel(
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
-      int am = INT_MAX;
+      // the position (i, r) of the lowest row holding the max as a 6-bit
+      // code, an inline constant, so that no row index is held in a
+      // register (64 row indices beside the accumulators made the compiler
+      // spill); 64 = none (every logit NaN)
+      int code = 64;
 #pragma unroll
       for (int i = 3; i >= 0; --i)
 #pragma unroll
-        for (int r = 15; r >= 0; --r)
-          am = acc[i][j][r] == mx ? vbase + i * 32 + 8 * (r >> 2) + (r & 3) : am;
+        for (int r = 15; r >= 0; --r) code = acc[i][j][r] == mx ? i * 16 + r : code;
+      int am = code == 64 ? INT_MAX
+                          : vbase + (code >> 4) * 32 + 8 * ((code >> 2) & 3) + (code & 3);
       float sum = 0.f;
       if (mx != -INFINITY) {
         const float ml = mx * kLog2e;
