@@ -493,6 +493,16 @@ def test_attend_value_scale_is_exact_across_splits(kv_lens):
         assert torch.equal(Ob, (O1.float() * f).to(torch.bfloat16)), e
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_attend_eight_row_waves(dtype, D):
+    """256 query rows per KV head (G 8 x 32 block tokens): the blocks of
+    eight row-waves, over ragged caches with and without one long enough
+    for many key ranges."""
+    _attend_case(dtype, 16, 2, D, 32, [3000, 17, 0, 900], True, 4100 + D)
+    _attend_case(dtype, 8, 1, D, 32, [9000], False, 4200 + D)
+
+
 @pytest.mark.parametrize("case", range(24))
 def test_attend_random_shapes(case):
     """Random GQA ratios, block lengths, head sizes, sequence counts and
