@@ -65,6 +65,11 @@ def _run(M, H, E, K, inter, dtype, seed=0, residual=False, force=None):
     (32, 2048, 64, 8, 512, "bf16"),
     (5, 512, 8, 2, 512, "bf16"),
     (64, 1024, 32, 8, 1024, "bf16"),
+    # more experts than one selection lane group holds: 65-256 and 257-1024
+    (32, 512, 100, 8, 512, "bf16"),
+    (24, 256, 200, 8, 256, "f32"),
+    (32, 256, 300, 16, 256, "f32"),
+    (8, 256, 1024, 16, 256, "f32"),
 ])
 def test_moe_matches_oracle(M, H, E, K, inter, dtype):
     _run(M, H, E, K, inter, dtype)
