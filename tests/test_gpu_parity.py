@@ -109,6 +109,45 @@ def test_lmhead_full_size_sampled(M, V):
     _check_lmhead(X, W, _np(conf), _np(amax), _np(lse), rows)
 
 
+def test_lmhead_generic_tile_path_bf16():
+    """bf16 with more than 64 rows and a hidden size that is not a multiple
+    of 128: the generic tile kernel, against the oracle."""
+    M, H, V = 100, 192, 3000
+    X = synth.normal_array((M, H), 4301, 1.0, "bf16")
+    W = synth.normal_array((V, H), 4302, 0.02, "bf16")
+    conf, amax, lse = sprint.lmhead_confidence(_to_dev(X, "bf16", DEV), _to_dev(W, "bf16", DEV),
+                                               want_lse=True)
+    _check_lmhead(X, W, _np(conf), _np(amax), _np(lse))
+
+
+def test_lmhead_generic_small_m_over_2gib():
+    """A few rows against a vocabulary matrix just over 2 GiB whose hidden
+    size (65 x 64) fits neither the ring nor the buffer-load paths: the
+    generic small-M kernel with 64-bit addressing.  W is zero but for two
+    planted rows, so the planted closed form gives the result (LLaDA2.0-Uni,
+    Sparse Prefix Retention: c = max_v softmax): logit g on one word and 0 on
+    the other V - 1 give c = 1 / (1 + (V - 1) e^-g) and lse = log(e^g + V - 1);
+    a zero row gives c = 1/V, argmax 0 (lowest index) and lse = log V."""
+    H, V = 4160, 258200
+    assert V * H * 2 >= 1 << 31
+    va, vb = V - 1, 129001
+    W = torch.zeros((V, H), dtype=torch.bfloat16, device=DEV)
+    W[va, 0] = 12.0
+    W[vb, 1] = 5.0
+    X = torch.zeros((3, H), dtype=torch.bfloat16, device=DEV)
+    X[0, 0] = 1.0
+    X[1, 1] = 2.0                       # logit 10 on word vb
+    conf, amax, lse = sprint.lmhead_confidence(X, W, want_lse=True)
+    torch.cuda.synchronize()
+    del W
+    want_c = [1.0 / (1.0 + (V - 1) * math.exp(-12.0)), 1.0 / (1.0 + (V - 1) * math.exp(-10.0)),
+              1.0 / V]
+    want_l = [math.log(math.exp(12.0) + V - 1), math.log(math.exp(10.0) + V - 1), math.log(V)]
+    np.testing.assert_allclose(_np(conf), want_c, rtol=1e-4)
+    np.testing.assert_allclose(_np(lse), want_l, rtol=1e-5)
+    assert _np(amax).tolist() == [va, vb, 0]
+
+
 @pytest.mark.parametrize("case", range(16))
 def test_lmhead_random_shapes(case):
     """Random token counts (one row to several token tiles), hidden sizes
