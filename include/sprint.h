@@ -26,6 +26,10 @@
  *    same inputs give bitwise-identical outputs.
  *  - Non-finite inputs violate the preconditions; results are then unspecified.
  *  - Calls that share a workspace must not overlap in time.
+ *  - Size limits common to every call (SPRINT_EUNSUPPORTED beyond them):
+ *    nseq <= 2^24 sequences; a key/value row (Hkv * D * element size) of at
+ *    most 1 MiB, and a K or V array (all layers) under 2^48 bytes.  The
+ *    *_ws() queries return 0 for sizes beyond their call's range.
  */
 #ifndef SPRINT_H
 #define SPRINT_H
@@ -82,7 +86,7 @@ int sprint_plan_keep(const int64_t* n_text, const int64_t* n_img, int32_t nseq,
  * (max, sum of exp, argmax) that a merge kernel combines.
  *   hidden [M, H] dtype;  W [V, H] dtype (nn.Linear layout)
  *   conf [M] float out;  argmax [M] int32 out;  lse [M] float out or NULL
- * Requires M >= 1, V >= 1, H a multiple of 64 (<= 65536).
+ * Requires M >= 1, V >= 1, H a multiple of 64 (<= 65536); V < 2^30.
  * ------------------------------------------------------------------------ */
 size_t lmhead_confidence_ws(int64_t M, int32_t H, int32_t V, int32_t dtype);
 int lmhead_confidence(const void* hidden, int64_t M, int32_t H, const void* W, int32_t V,

@@ -17,10 +17,24 @@ bool dev16(const void* p) { return p != nullptr && aligned(p, 16); }
 bool dev4(const void* p) { return p != nullptr && aligned(p, 4); }
 bool dtype_ok(int32_t dt) { return dt == SPRINT_F32 || dt == SPRINT_BF16; }
 bool head_dim_ok(int32_t D) { return D == 64 || D == 128; }
+// a * b * c < limit for a, b, c >= 0 and limit >= 1, without forming the
+// product (which can overflow int64 for absurd sizes).
+bool product_below(int64_t a, int64_t b, int64_t c, int64_t limit) {
+  if (a == 0 || b == 0 || c == 0) return true;
+  return a <= ((limit - 1) / c) / b;
+}
 // Arrays that kernels address through 32-bit buffer offsets stay below 2 GiB.
 bool under_2gib(int64_t rows, int64_t row_bytes) {
-  return rows * row_bytes < (static_cast<int64_t>(1) << 31);
+  return product_below(rows, 1, row_bytes, static_cast<int64_t>(1) << 31);
 }
+// Arrays addressed through 64-bit offsets: a key row of at most 1 MiB (the
+// kernels count a row's 16-byte vectors in 32 bits) and a whole stack under
+// 2^48 bytes, the GPU's virtual address space, so no offset overflows.
+constexpr int64_t kMaxRowBytes = int64_t(1) << 20;
+constexpr int64_t kMaxArrayBytes = int64_t(1) << 48;
+// Vocabulary and sequence-count limits that keep tile and grid counts in 32 bits.
+constexpr int32_t kMaxVocab = (1 << 30) - 1;
+constexpr int32_t kMaxSeqs = 1 << 24;
 int64_t kv_row_bytes(int32_t Hkv, int32_t D, int32_t dtype) {
   return static_cast<int64_t>(Hkv) * D * (dtype == SPRINT_BF16 ? 2 : 4);
 }
@@ -65,7 +79,7 @@ int sprint_plan_keep(const int64_t* n_text, const int64_t* n_img, int32_t nseq, 
   int64_t acc = 0;
   for (int32_t s = 0; s < nseq; ++s) {
     if (n_text[s] < 0 || n_img[s] < 0) return SPRINT_EINVAL;
-    if (n_text[s] + n_img[s] > INT32_MAX) return SPRINT_EINVAL;
+    if (n_text[s] > INT32_MAX || n_img[s] > INT32_MAX - n_text[s]) return SPRINT_EINVAL;
   }
   cu_kept[0] = 0;
   for (int32_t s = 0; s < nseq; ++s) {
@@ -83,7 +97,7 @@ int sprint_plan_keep(const int64_t* n_text, const int64_t* n_img, int32_t nseq, 
 
 // ---------------------------------------------------------------- LM head
 size_t lmhead_confidence_ws(int64_t M, int32_t H, int32_t V, int32_t dtype) {
-  if (M < 1 || V < 1) return 0;
+  if (M < 1 || M > INT32_MAX || V < 1 || V > kMaxVocab || H < 1) return 0;
   return lmhead_ws_bytes(M, H, V, dtype);
 }
 
@@ -94,7 +108,7 @@ int lmhead_confidence(const void* hidden, int64_t M, int32_t H, const void* W, i
   if (M < 1 || V < 1 || H < 1 || M > INT32_MAX) return SPRINT_EINVAL;
   if (!dev16(hidden) || !dev16(W) || !dev4(conf) || !dev4(argmax)) return SPRINT_EINVAL;
   if (lse != nullptr && !aligned(lse, 4)) return SPRINT_EINVAL;
-  if (H % 64 != 0 || H > 65536) return SPRINT_EUNSUPPORTED;
+  if (H % 64 != 0 || H > 65536 || V > kMaxVocab) return SPRINT_EUNSUPPORTED;
   const int st = check_ws(ws, ws_bytes, lmhead_ws_bytes(M, H, V, dtype));
   if (st != SPRINT_OK) return st;
   return status_of(launch_lmhead(hidden, M, H, W, V, dtype, conf, argmax, lse, ws,
@@ -110,7 +124,10 @@ static int score_impl(const void* K, int32_t n_layers, int per_layer, const floa
     return SPRINT_EINVAL;
   if (n_layers < 1 || n_layers > 65535) return SPRINT_EINVAL;
   if (!dev4(cu_len) || !isfinite(alpha)) return SPRINT_EINVAL;
-  if (!head_dim_ok(D)) return SPRINT_EUNSUPPORTED;
+  if (!head_dim_ok(D) || nseq > kMaxSeqs) return SPRINT_EUNSUPPORTED;
+  const int64_t row = kv_row_bytes(Hkv, D, dtype);
+  if (row > kMaxRowBytes || !product_below(n_layers, total_L, row, kMaxArrayBytes))
+    return SPRINT_EUNSUPPORTED;
   if (total_L > 0 && (!dev16(K) || !dev4(conf) || !dev4(ibar) || !dev4(score)))
     return SPRINT_EINVAL;
   const int st = check_ws(ws, ws_bytes, score_ws_bytes(total_L, nseq, n_layers));
@@ -120,7 +137,7 @@ static int score_impl(const void* K, int32_t n_layers, int per_layer, const floa
 }
 
 size_t sprint_score_ws(int64_t total_L, int32_t nseq) {
-  if (total_L < 0 || nseq < 1) return 0;
+  if (total_L < 0 || total_L > INT32_MAX || nseq < 1 || nseq > kMaxSeqs) return 0;
   return score_ws_bytes(total_L, nseq, 1);
 }
 
@@ -132,7 +149,9 @@ int sprint_score(const void* K, const float* conf, const int32_t* cu_len, int32_
 }
 
 size_t sprint_score_layers_ws(int64_t total_L, int32_t nseq, int32_t n_layers) {
-  if (total_L < 0 || nseq < 1 || n_layers < 1) return 0;
+  if (total_L < 0 || total_L > INT32_MAX || nseq < 1 || nseq > kMaxSeqs || n_layers < 1 ||
+      n_layers > 65535)
+    return 0;
   return score_ws_bytes(total_L, nseq, n_layers);
 }
 
@@ -163,9 +182,12 @@ static int prune_impl(const float* score, const uint8_t* modality, const int32_t
   if (n_layers < 1 || n_layers > 65535) return SPRINT_EINVAL;
   if (total_kept < 0 || total_kept > total_L) return SPRINT_EINVAL;
   if (!dev4(cu_len) || !dev4(keep) || !dev4(cu_kept)) return SPRINT_EINVAL;
-  if (!head_dim_ok(D)) return SPRINT_EUNSUPPORTED;
+  if (!head_dim_ok(D) || nseq > kMaxSeqs) return SPRINT_EUNSUPPORTED;
+  const int64_t row = kv_row_bytes(Hkv, D, dtype);
+  if (row > kMaxRowBytes || !product_below(n_layers, total_L, row, kMaxArrayBytes))
+    return SPRINT_EUNSUPPORTED;
   // the pruned cache of a layer is written through 32-bit buffer offsets
-  if (!under_2gib(total_kept, kv_row_bytes(Hkv, D, dtype))) return SPRINT_EUNSUPPORTED;
+  if (!under_2gib(total_kept, row)) return SPRINT_EUNSUPPORTED;
   if (total_L > 0 && (!dev4(score) || modality == nullptr || !dev16(K) || !dev16(V)))
     return SPRINT_EINVAL;
   if (total_kept > 0 && (!dev16(K_out) || !dev16(V_out) || !dev4(kept_idx))) return SPRINT_EINVAL;
@@ -177,7 +199,7 @@ static int prune_impl(const float* score, const uint8_t* modality, const int32_t
 }
 
 size_t sprint_prune_kv_ws(int64_t total_L, int32_t nseq) {
-  if (total_L < 0 || nseq < 1) return 0;
+  if (total_L < 0 || total_L > INT32_MAX || nseq < 1 || nseq > kMaxSeqs) return 0;
   return prune_ws_bytes(total_L, nseq, 1);
 }
 
@@ -201,7 +223,9 @@ int sprint_prune_kv_layers(const float* score, const uint8_t* modality, const in
 }
 
 size_t sprint_prune_kv_per_layer_ws(int64_t total_L, int32_t nseq, int32_t n_layers) {
-  if (total_L < 0 || nseq < 1 || n_layers < 1) return 0;
+  if (total_L < 0 || total_L > INT32_MAX || nseq < 1 || nseq > kMaxSeqs || n_layers < 1 ||
+      n_layers > 65535)
+    return 0;
   return prune_ws_bytes(total_L, nseq, n_layers);
 }
 
@@ -220,7 +244,11 @@ static int attend_shape_status(int32_t nseq, int32_t Lq, int32_t Hq, int32_t Hkv
                                int32_t max_kv) {
   if (nseq < 1 || Lq < 1 || Hq < 1 || Hkv < 1 || max_kv < 0) return SPRINT_EINVAL;
   if (Hq % Hkv != 0) return SPRINT_EINVAL;
-  if (!head_dim_ok(D) || Lq > 64 || (Hq / Hkv) * Lq > 256) return SPRINT_EUNSUPPORTED;
+  if (!head_dim_ok(D) || Lq > 64 || static_cast<int64_t>(Hq / Hkv) * Lq > 256 || nseq > kMaxSeqs)
+    return SPRINT_EUNSUPPORTED;
+  // the block's rows stay under 2 GiB even in bf16 (checked per dtype later)
+  if (!under_2gib(static_cast<int64_t>(nseq) * Lq, kv_row_bytes(Hkv, D, SPRINT_BF16)))
+    return SPRINT_EUNSUPPORTED;
   return SPRINT_OK;
 }
 
@@ -251,11 +279,6 @@ static int attend_check(const void* Q, int32_t nseq, int32_t Lq, int32_t Hq, con
   if (Kb != nullptr && (!dev16(Kb) || !dev16(Vb))) return SPRINT_EINVAL;
   if (Kb == nullptr && max_kv < 1) return SPRINT_EINVAL;  // no keys at all
   if (total_kv > 0 && (!dev16(Kp) || !dev16(Vp))) return SPRINT_EINVAL;
-  // K/V are addressed through 32-bit buffer descriptors
-  const int64_t row_bytes = static_cast<int64_t>(Hkv) * D * (dtype == SPRINT_BF16 ? 2 : 4);
-  if (total_kv * row_bytes >= (int64_t(1) << 31) ||
-      static_cast<int64_t>(nseq) * Lq * row_bytes >= (int64_t(1) << 31))
-    return SPRINT_EUNSUPPORTED;
   return SPRINT_OK;
 }
 
@@ -298,7 +321,7 @@ int unmask_select(const float* conf, const int32_t* argmax, int32_t nseq, int32_
                   int32_t steps_left, uint8_t* masked, int32_t* tokens, int32_t* n_accepted,
                   void* stream) {
   if (nseq < 1 || Lq < 1 || tau != tau) return SPRINT_EINVAL;
-  if (Lq > 64) return SPRINT_EUNSUPPORTED;
+  if (Lq > 64 || nseq > kMaxSeqs) return SPRINT_EUNSUPPORTED;
   if (!dev4(conf) || !dev4(argmax) || masked == nullptr || !dev4(tokens) || !dev4(n_accepted))
     return SPRINT_EINVAL;
   return status_of(launch_unmask(conf, argmax, nseq, Lq, tau, steps_left, masked, tokens,
@@ -309,8 +332,10 @@ int unmask_select(const float* conf, const int32_t* argmax, int32_t nseq, int32_
 int sprint_append_rows(const void* old, const int32_t* cu_old, int32_t nseq, int64_t total_old,
                        const void* blk, int32_t n_blk, int64_t row_bytes, void* out,
                        int32_t* cu_out, void* stream) {
-  if (nseq < 1 || n_blk < 0 || total_old < 0 || row_bytes < 1 || row_bytes > (int64_t(1) << 31))
+  if (nseq < 1 || n_blk < 0 || total_old < 0 || total_old > INT32_MAX || row_bytes < 1 ||
+      row_bytes > (int64_t(1) << 31))
     return SPRINT_EINVAL;
+  if (nseq > kMaxSeqs) return SPRINT_EUNSUPPORTED;
   if (!dev4(cu_old) || (cu_out != nullptr && (!aligned(cu_out, 4) || cu_out == cu_old)))
     return SPRINT_EINVAL;
   const int64_t total_rows = total_old + static_cast<int64_t>(nseq) * n_blk;
@@ -335,6 +360,9 @@ int sprint_append_rows(const void* old, const int32_t* cu_old, int32_t nseq, int
 // ---------------------------------------------------------------- MoE FFN
 size_t moe_ffn_ws(int32_t M, int32_t H, int32_t n_experts, int32_t top_k, int32_t inter) {
   if (M < 1 || H < 1 || n_experts < 1 || top_k < 1 || inter < 1) return 0;
+  if (!moe_shape_supported(H, inter, n_experts, top_k, M, SPRINT_BF16) &&
+      !moe_shape_supported(H, inter, n_experts, top_k, M, SPRINT_F32))
+    return 0;
   return moe_ws_bytes(M, H, n_experts, top_k, inter);
 }
 

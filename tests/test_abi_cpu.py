@@ -327,3 +327,236 @@ def test_committed_traffic_counters_match_the_kernel_source():
     if stale:
         pytest.skip(f"{stale}: counters taken on an earlier source; bench.py "
                     "reports traffic null until they are re-taken")
+
+
+# ---------------------------------------------------------------- argument fuzz
+# Each entry point's arguments, as (kind, valid value) pairs, where a kind
+# lists values that must be rejected before any HIP call when they replace
+# the valid value alone ("bad"), and values that may or may not be valid
+# ("alt").  The valid tuples pass every host check; with no GPU present they
+# then fail at the first HIP call (SPRINT_EHIP), or succeed when they launch
+# nothing.
+NAN, INF = float("nan"), float("inf")
+I32_MIN, I32_MAX, I64_MIN, I64_MAX = -2**31, 2**31 - 1, -2**63, 2**63 - 1
+STREAM = ("stream", (), ())
+
+
+def _p16(v=FAKE):
+    return ("ptr16", (None, FAKE + 2, FAKE + 8), (FAKE + 16, FAKE + (1 << 20))), v
+
+
+def _p4(v=FAKE):
+    return ("ptr4", (None, FAKE + 1, FAKE + 2), (FAKE + 4,)), v
+
+
+def _pb(v=FAKE):
+    return ("bytes", (None,), (FAKE + 1, FAKE + 3)), v
+
+
+def _o16(v=None):
+    return ("opt16", (FAKE + 2, FAKE + 8), (None, FAKE + 32)), v
+
+
+def _o4(v=None):
+    return ("opt4", (FAKE + 2,), (None, FAKE + 4)), v
+
+
+def _int(v, bad, alt=()):
+    return ("int", tuple(bad), tuple(alt)), v
+
+
+def _dt(v=None):
+    return ("dtype", (2, 7, -1, 1 << 20), (sprint.F32, sprint.BF16)), sprint.BF16 if v is None else v
+
+
+def _finite(v):
+    return ("finite", (NAN, INF, -INF), (0.0, -3.0, 1e30)), v
+
+
+def _wsb(v=1 << 30):
+    return ("ws_bytes", (0, 1, 255), (1 << 40, 2**64 - 1)), v
+
+
+NSEQ_BAD = (0, -1, I32_MIN, (1 << 24) + 1, I32_MAX)
+HKV_BAD = (0, -1, 4097, I32_MAX)                          # 4097 * 128 * 2 bytes > 1 MiB
+D_BAD = (0, -128, 80, 96, 256, I32_MAX)
+NL_BAD = (0, -1, 65536, I32_MAX)
+
+
+def _score_spec(n_layers=None):
+    lay = [] if n_layers is None else [_int(n_layers, NL_BAD, (1, 2, 65535))]
+    return [_p16()] + lay + [
+        _p4(), _p4(), _int(1, NSEQ_BAD, (2, 4096)),
+        _int(4096, (-1, I64_MIN, 2**31, 2**62), (0, 1, 100)),
+        _int(4, HKV_BAD, (1, 8, 1024)), _int(128, D_BAD, (64,)), _dt(), _finite(0.5),
+        _p4(), _p4(), _p16(), _wsb(), (STREAM, None)]
+
+
+def _prune_spec(n_layers=None, ws=1 << 30):
+    lay = [] if n_layers is None else [_int(n_layers, NL_BAD, (1, 2, 16))]
+    return [_p4(), _pb(), _p4(), _p4(), _p4(), _int(1, NSEQ_BAD, (2,)),
+            _int(4096, (-1, I64_MIN, 2**31, 2**62, 3480), (8192,)),
+            _int(3481, (-1, I64_MIN, 4097, 2**62), (0, 1, 4096)), _p16(), _p16()] + lay + [
+            _int(4, HKV_BAD, (1, 8)), _int(128, D_BAD, (64,)), _dt(), _p16(), _p16(), _p4(),
+            _p16(), _wsb(ws), (STREAM, None)]
+
+
+def _attend_spec(with_ws):
+    head = [_p16(), _int(1, NSEQ_BAD, (2, 3)), _int(32, (0, -1, 65, I32_MAX), (1, 8, 64)),
+            _int(16, (0, -1, 5, I32_MAX, 2**31 - 4), (4, 8, 32)), _p16(), _p16(), _p4(),
+            _int(4096, (-1, I64_MIN, 2**31, 2**62, 4097), (0, 100)),
+            _int(4096, (-1, I32_MIN, 4095), (I32_MAX, 8192)), _p16(), _p16(),
+            _int(4, (0, -1, 1, 3, 32, I32_MAX), (2, 8, 16)), _int(128, D_BAD, (64,)),
+            (("scale", (NAN, INF, -INF, 0.0, -0.0, -1.0), (1e-30, 1e30)), 0.088), _dt(), _p16()]
+    return head + ([_p16(), _wsb()] if with_ws else []) + [(STREAM, None)]
+
+
+FUZZ_SPECS = {
+    "lmhead_confidence": [
+        _p16(), _int(32, (0, -1, I64_MIN, 2**31, 2**62), (1, 4096)),
+        _int(2048, (0, -1, 100, 65600, I32_MAX), (64, 65536)), _p16(),
+        _int(32768, (0, -1, I32_MIN, 2**30, I32_MAX), (1, 3000)), _dt(), _p4(), _p4(), _o4(),
+        _p16(), _wsb(), (STREAM, None)],
+    "sprint_score": _score_spec(),
+    "sprint_score_layers": _score_spec(4),
+    "sprint_score_per_layer": _score_spec(16),
+    "sprint_prune_kv": _prune_spec(),
+    "sprint_prune_kv_layers": _prune_spec(4),
+    "sprint_prune_kv_per_layer": _prune_spec(16, sprint.sprint_prune_kv_per_layer_ws(4096, 1, 16)),
+    "block_attend": _attend_spec(True),
+    "block_attend_noalloc": _attend_spec(False),
+    "unmask_select": [
+        _p4(), _p4(), _int(1, NSEQ_BAD, (2, 1000)), _int(32, (0, -1, 65, I32_MAX), (1, 64)),
+        (("tau", (NAN,), (INF, -INF, 2.0, -1.0)), 0.9), _int(9, (), (0, -1, I32_MIN, I32_MAX)),
+        _pb(), _p4(), _p4(), (STREAM, None)],
+    "sprint_append_rows": [
+        _pb(), (("cu_old", (None, FAKE + 2), (FAKE + 4,)), FAKE),
+        _int(2, NSEQ_BAD, (1, 3)), _int(100, (-1, I64_MIN, 2**31, 2**62), (0, 5)),
+        _pb(FAKE + (1 << 20)), _int(32, (-1, I32_MIN), (0, 1)),
+        _int(1024, (0, -1, 2**31 + 1, 2**62), (1, 3, 16)),
+        (("out", (None, FAKE + 1024, FAKE + (1 << 20) + 64), (FAKE + (1 << 30),)),
+         FAKE + (1 << 24)),
+        (("cu_out", (FAKE, FAKE + 66), (None, FAKE + 128)), FAKE + 64), (STREAM, None)],
+    "moe_ffn": [
+        _p16(), _int(32, (0, -1, I32_MIN, 1025, I32_MAX), (1, 8, 1024)),
+        _int(2048, (0, -1, 100, 2304, 4096, I32_MAX), (512, 1024)), _p16(), _p4(),
+        _int(256, (0, -1, 7, 1025, I32_MAX), (8, 1024)),
+        _int(8, (0, -1, 17, 257, I32_MAX), (1, 16)), _finite(2.5), _p16(), _p16(), _p16(),
+        _int(512, (0, -1, 500, 1536, I32_MAX), (1024,)), _dt(), _o16(), _p16(), _p4(), _p4(),
+        _p16(), _wsb(), (STREAM, None)],
+}
+
+
+def _status(name, args):
+    st = _call(name, *args)
+    assert isinstance(st, int)
+    return st
+
+
+needs_no_gpu = pytest.mark.skipif(
+    os.path.exists("/dev/kfd"),
+    reason="fake device pointers must never reach a kernel: runs only where no GPU exists")
+
+
+@needs_no_gpu
+def test_fuzz_specs_cover_every_device_entry_point():
+    """Every compute call the header declares is fuzzed, with one spec entry
+    per argument, and its valid tuple passes the host checks."""
+    compute = [n for n in sprint.EXPORTS if not n.endswith("_ws") and n not in (
+        "sprint_strerror", "sprint_version", "sprint_keep_count", "sprint_plan_keep")]
+    assert sorted(compute) == sorted(FUZZ_SPECS)
+    for name, spec in FUZZ_SPECS.items():
+        assert len(spec) == len(sprint._SIGS[name][1]), name
+        assert _status(name, [v for _, v in spec]) == 4, name        # SPRINT_EHIP: no device
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("name", sorted(FUZZ_SPECS))
+def test_abi_rejects_each_invalid_argument_before_hip(name):
+    """Each argument replaced alone by an invalid value is rejected with
+    EINVAL, EUNSUPPORTED or EWORKSPACE; other values never crash and give a
+    documented status."""
+    spec = FUZZ_SPECS[name]
+    base = [v for _, v in spec]
+    for i, ((kind, bad, alt), _) in enumerate(spec):
+        for v in bad:
+            a = list(base); a[i] = v
+            assert _status(name, a) in (1, 2, 3), (name, i, kind, v)
+        for v in alt:
+            a = list(base); a[i] = v
+            assert _status(name, a) in (0, 1, 2, 3, 4), (name, i, kind, v)
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("seed", range(4))
+def test_abi_survives_random_invalid_argument_mixes(seed):
+    """Seeded fuzz: several arguments at once take bad or alternative values.
+    Every call returns a documented status without crashing; when one of the
+    changed arguments is a misaligned device pointer and no size was set to 0
+    (an empty array's pointer is not checked), the call is rejected before
+    HIP."""
+    import random
+    rng = random.Random(1000 + seed)
+    n_calls = 0
+    for name in sorted(FUZZ_SPECS):
+        spec = FUZZ_SPECS[name]
+        slots = [i for i, ((_, bad, alt), _) in enumerate(spec) if bad or alt]
+        for _ in range(150):
+            a = [v for _, v in spec]
+            hard = zeroed = False
+            for i in rng.sample(slots, rng.randint(2, min(5, len(slots)))):
+                (kind, bad, alt), _ = spec[i]
+                pool = [(v, True) for v in bad] + [(v, False) for v in alt]
+                a[i], is_bad = rng.choice(pool)
+                hard |= is_bad and kind in ("ptr16", "ptr4", "opt16", "opt4") and a[i] is not None
+                zeroed |= kind == "int" and a[i] == 0
+            st = _status(name, a)
+            assert st in (0, 1, 2, 3, 4), (name, a, st)
+            if hard and not zeroed:
+                assert st in (1, 2, 3), (name, a, st)
+            n_calls += 1
+    assert n_calls == 150 * len(FUZZ_SPECS)
+
+
+def test_plan_keep_random_counts_and_ratios():
+    """Host-only keep planning over random counts (with negative and
+    near-overflow ones) and ratios (with NaN, infinities and values outside
+    [0, 1]): a valid plan keeps floor(r * n) clamped to [0, n] per sequence
+    and modality, with prefix sums in cu_kept; anything else is EINVAL."""
+    import math
+    import random
+    rng = random.Random(7)
+    f = sprint.lib().sprint_plan_keep
+    ratios = [0.0, 0.25, 0.5, 0.85, 1.0, 1.5, -0.5, NAN, INF, -INF, 1e-9, 0.999999]
+    for trial in range(400):
+        nseq = rng.randint(1, 6)
+        pick = lambda: rng.choice([rng.randint(0, 5000), rng.randint(0, 2**31), 0, 1, -1,
+                                   2**31 - 1, 2**62, I64_MAX])
+        nt = (ctypes.c_int64 * nseq)(*[pick() for _ in range(nseq)])
+        ni = (ctypes.c_int64 * nseq)(*[pick() for _ in range(nseq)])
+        rt, ri = rng.choice(ratios), rng.choice(ratios)
+        keep = (ctypes.c_int32 * (2 * nseq))()
+        cu = (ctypes.c_int32 * (nseq + 1))()
+        tot = ctypes.c_int64(-5)
+        st = f(nt, ni, nseq, rt, ri, keep, cu, ctypes.byref(tot))
+
+        def kc(r, n):
+            if n <= 0 or r != r:
+                return 0
+            k = math.floor(r * n) if math.isfinite(r * n) else (n if r > 0 else 0)
+            return max(0, min(int(k), n))
+        ok = all(0 <= nt[s] and 0 <= ni[s] and nt[s] + ni[s] <= I32_MAX for s in range(nseq))
+        if ok:
+            ks = [(kc(rt, nt[s]), kc(ri, ni[s])) for s in range(nseq)]
+            ok = sum(a + b for a, b in ks) <= I32_MAX
+        if not ok:
+            assert st == 1, (trial, list(nt), list(ni))
+            continue
+        assert st == 0, (trial, list(nt), list(ni), rt, ri)
+        acc = 0
+        assert cu[0] == 0
+        for s, (kt, ki) in enumerate(ks):
+            assert (keep[2 * s], keep[2 * s + 1]) == (kt, ki), (trial, s)
+            acc += kt + ki
+            assert cu[s + 1] == acc
+        assert tot.value == acc
