@@ -129,20 +129,35 @@ __global__ __launch_bounds__(64) void score_kernel(const float* __restrict__ con
   const bool ok = p < sc.begin + sc.len;
   const int l0 = per_layer ? static_cast<int>(blockIdx.y) : 0;
   const int l1 = per_layer ? l0 + 1 : n_layers;
+  // The position's confidence and norms do not depend on the chunk sums:
+  // they are loaded first, so that their latency overlaps the sums'.
+  const int64_t pc = ok ? p : sc.begin;
+  const float cf = conf[pc];
   float ib = 0.f;
   for (int l = l0; l < l1; ++l) {
-    const float* part = partial + static_cast<int64_t>(l) * gridDim.x;
+    const float nv = norms[static_cast<int64_t>(l) * total_L + pc];
+    const float* part = partial + static_cast<int64_t>(l) * gridDim.x + sc.first;
+    // lane-strided sum of the chunk sums, eight loads in flight per round,
+    // added in index order (the same order, so the same bits, in every chunk)
     float acc = 0.f;
-    for (int i = lane; i < sc.nchunks; i += 64) acc += part[sc.first + i];
+    int i = lane;
+    for (; i + 7 * 64 < sc.nchunks; i += 8 * 64) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[i + 64 * u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; i < sc.nchunks; i += 64) acc += part[i];
     acc = wave_sum(acc);
     const float mean = acc / static_cast<float>(sc.len);
-    if (ok) ib += mean > 0.f ? norms[static_cast<int64_t>(l) * total_L + p] / mean : 1.f;
+    ib += mean > 0.f ? nv / mean : 1.f;
   }
   if (ok) {
     ib /= static_cast<float>(l1 - l0);
     const int64_t o = static_cast<int64_t>(l0) * total_L + p;
     ibar[o] = ib;
-    score[o] = alpha * ib + (1.f - alpha) * conf[p];
+    score[o] = alpha * ib + (1.f - alpha) * cf;
   }
 }
 
