@@ -250,7 +250,8 @@ def profile_call(args, blk, n_steps, torch):
         fns = {"lmhead_prefix": blk.prefix_confidence, "score": blk.score_prefix,
                "prune": blk.prune_prefix, "attend_full": lambda: blk.attend(False),
                "attend_pruned": lambda: blk.attend(True), "lmhead_block": blk.block_confidence,
-               "unmask": lambda: blk.unmask(1)}
+               "unmask": lambda: blk.unmask(1),
+               "lmhead_unmask": lambda: blk.confidence_and_unmask(1)}
         blk.run_block(n_steps)
         fn = fns[args.profile_call]
         what = args.profile_call
@@ -833,6 +834,22 @@ def main():
     launches_full = {"attend_full": n_steps + 1, "lmhead_block": n_steps + 1,
                      "unmask": n_steps + 1}
 
+    # ---------------------------------------------------------------- fused step tail
+    # The end of a step as one lmhead_confidence_unmask call (the block's
+    # default) against lmhead_confidence + unmask_select, and a whole pruned
+    # step each way: graph replays of 20 launches, bitwise the same state.
+    step_tail = {}
+    for fused in (True, False):
+        blk.fused_tail = fused
+        blk.reset()
+        key = "fused" if fused else "two_calls"
+        step_tail[key] = {"tail_us": round(call_us(torch, lambda: blk.confidence_and_unmask(1)), 3),
+                          "pruned_step_us": round(call_us(torch, lambda: blk.pruned_step(1)), 3)}
+    blk.fused_tail = True
+    step_tail["note"] = ("tail = the block LM head and the unmasking step of one denoising "
+                         "step; fused: one call, two launches (the block that merges a "
+                         "sequence's last row runs its unmasking step)")
+
     # ---------------------------------------------------------------- library yardstick
     # The prefix GEMM's shape through torch.mm (hipBLASLt), for comparison
     # only: logits^T = W . hidden^T, written out in bf16, which the fused
@@ -1024,6 +1041,7 @@ def main():
         "planted_confidence": planted,
         "roofline": roofline,
         "kernels": kernels,
+        "step_tail": step_tail,
         "yardstick": yardstick,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},

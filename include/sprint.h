@@ -263,6 +263,34 @@ int unmask_select(const float* conf, const int32_t* argmax, int32_t nseq, int32_
                   void* stream);
 
 /* ------------------------------------------------------------------------
+ * The end of one denoising step, fused: lmhead_confidence over the block's
+ * rows, then unmask_select on the result (Non-uniform Token Unmasking: the
+ * confidences c_n of the greedy predictions decide which masked positions
+ * are accepted).  Same results, bit for bit, as
+ *     lmhead_confidence(hidden, nseq*Lq, H, W, V, dtype, conf, argmax, NULL, ...)
+ *     unmask_select(conf, argmax, nseq, Lq, tau, steps_left, masked, tokens,
+ *                   n_accepted, ...)
+ * in one call.  For bf16 with nseq*Lq <= 64 and H a multiple of 256 it takes
+ * two launches instead of three: the block that merges the last row of a
+ * sequence also runs that sequence's unmasking step.  Other shapes run the
+ * two calls' launches in turn.
+ *   hidden [nseq*Lq, H] dtype;  W [V, H] dtype;  conf [nseq*Lq] float out;
+ *   argmax [nseq*Lq] int32 out;  masked [nseq, Lq] uint8 in/out;
+ *   tokens [nseq, Lq] int32 in/out;  n_accepted [nseq] int32 out
+ * Requires the limits of both calls (1 <= Lq <= 64, H a multiple of 64 up
+ * to 65536, V < 2^30).  The workspace holds lmhead_confidence's plus one
+ * counter per sequence; the call sets what it needs, so it may hold
+ * anything on entry.  Calls that share a workspace must not overlap.
+ * ------------------------------------------------------------------------ */
+size_t lmhead_confidence_unmask_ws(int32_t nseq, int32_t Lq, int32_t H, int32_t V,
+                                   int32_t dtype);
+int lmhead_confidence_unmask(const void* hidden, int32_t nseq, int32_t Lq, int32_t H,
+                             const void* W, int32_t V, int32_t dtype, float* conf,
+                             int32_t* argmax, float tau, int32_t steps_left, uint8_t* masked,
+                             int32_t* tokens, int32_t* n_accepted, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* ------------------------------------------------------------------------
  * Prefix growth between blocks (block-wise generation, SPRINT introduction;
  * Sparse Prefix Retention: each block's first step sees the complete cache,
  * so a finished block joins the prefix before the next block is scored and

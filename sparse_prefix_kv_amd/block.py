@@ -42,12 +42,14 @@ class SprintBlock:
     def __init__(self, x: synth.Inputs, device="cuda", r_text: Optional[float] = None,
                  r_img: Optional[float] = None, tau: Optional[float] = None,
                  T: Optional[int] = "wl", alpha: Optional[float] = None, grow: int = 0,
-                 moe=None):
+                 moe=None, fused_tail: bool = True):
         """`grow`: rows per sequence the prefix may gain later (blocks appended
         by a generation loop); buffers and workspaces are sized for it once.
         `moe` = (w_router, bias, w_gate, w_up, w_down, top_k, route_scale) as
         device tensors puts an MoE FFN between attention and the LM head: the
-        LM head then reads O + moe_ffn(O)."""
+        LM head then reads O + moe_ffn(O).  `fused_tail`: each step ends with
+        one lmhead_confidence_unmask call instead of lmhead_confidence and
+        unmask_select (bitwise the same state)."""
         wl = x.wl
         lay = x.layout
         self.wl, self.layout = wl, lay
@@ -115,6 +117,8 @@ class SprintBlock:
         # workspace sizes grow with the sizes they are queried for
         self.ws_lm_prefix = ws(sprint.lmhead_confidence_ws(self._cap_L, H, Vv, dti))
         self.ws_lm_blk = ws(sprint.lmhead_confidence_ws(M, H, Vv, dti))
+        self.fused_tail = fused_tail
+        self.ws_lm_unmask = ws(sprint.lmhead_confidence_unmask_ws(self.nseq, self.Lq, H, Vv, dti))
         self.ws_score = ws(sprint.sprint_score_ws(self._cap_L, self.nseq))
         self.ws_prune = ws(sprint.sprint_prune_kv_ws(self._cap_L, self.nseq))
         # the attention split plan is not monotone in the cache length: size
@@ -230,8 +234,20 @@ class SprintBlock:
                                  n_accepted=self.n_acc)
 
     def confidence_and_unmask(self, t: int):
-        self.block_confidence()
-        self.unmask(t)
+        if not self.fused_tail:
+            self.block_confidence()
+            self.unmask(t)
+            return
+        M = self.nseq * self.Lq
+        h = self.O.view(M, self.Hq * self.D)
+        if self.moe is not None:
+            self.moe_ffn()
+            h = self.moe_y
+        with self._t("lmhead_unmask"):
+            sprint.lmhead_confidence_unmask(h, self.W, self.masked, self.tokens, self.tau,
+                                            self.steps_left(t), conf=self.conf_blk,
+                                            argmax=self.argmax_blk, n_accepted=self.n_acc,
+                                            ws=self.ws_lm_unmask)
 
     # ------------------------------------------------------------------ block
     def pruning_pass(self, prefix_conf: bool = True):

@@ -115,6 +115,32 @@ int lmhead_confidence(const void* hidden, int64_t M, int32_t H, const void* W, i
                                  as_stream(stream)));
 }
 
+size_t lmhead_confidence_unmask_ws(int32_t nseq, int32_t Lq, int32_t H, int32_t V,
+                                   int32_t dtype) {
+  if (nseq < 1 || nseq > kMaxSeqs || Lq < 1 || Lq > 64 || V < 1 || V > kMaxVocab || H < 1)
+    return 0;
+  return lmhead_unmask_ws_bytes(nseq, Lq, H, V, dtype);
+}
+
+int lmhead_confidence_unmask(const void* hidden, int32_t nseq, int32_t Lq, int32_t H,
+                             const void* W, int32_t V, int32_t dtype, float* conf,
+                             int32_t* argmax, float tau, int32_t steps_left, uint8_t* masked,
+                             int32_t* tokens, int32_t* n_accepted, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (!dtype_ok(dtype)) return SPRINT_EINVAL;
+  if (nseq < 1 || Lq < 1 || V < 1 || H < 1 || tau != tau) return SPRINT_EINVAL;
+  if (Lq > 64 || nseq > kMaxSeqs) return SPRINT_EUNSUPPORTED;
+  if (!dev16(hidden) || !dev16(W) || !dev4(conf) || !dev4(argmax) || masked == nullptr ||
+      !dev4(tokens) || !dev4(n_accepted))
+    return SPRINT_EINVAL;
+  if (H % 64 != 0 || H > 65536 || V > kMaxVocab) return SPRINT_EUNSUPPORTED;
+  const int st = check_ws(ws, ws_bytes, lmhead_unmask_ws_bytes(nseq, Lq, H, V, dtype));
+  if (st != SPRINT_OK) return st;
+  return status_of(launch_lmhead_unmask(hidden, nseq, Lq, H, W, V, dtype, conf, argmax, tau,
+                                        steps_left, masked, tokens, n_accepted, ws,
+                                        as_stream(stream)));
+}
+
 // ---------------------------------------------------------------- score
 static int score_impl(const void* K, int32_t n_layers, int per_layer, const float* conf,
                       const int32_t* cu_len, int32_t nseq, int64_t total_L, int32_t Hkv,

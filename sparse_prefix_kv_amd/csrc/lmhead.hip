@@ -688,7 +688,9 @@ __global__ __launch_bounds__(64 * NW) void lmhead_ring_kernel(const uint16_t* __
                                                               int64_t M, int H,
                                                               const uint16_t* __restrict__ W,
                                                               int V, float4* __restrict__ part,
-                                                              int n_vt) {
+                                                              int n_vt,
+                                                              int32_t* __restrict__ arrive,
+                                                              int n_arrive) {
   constexpr int kBV = 32 * NW;               // vocabulary rows per block
   constexpr int kBT = 32 * NT;
   constexpr int kXP = 4 * NT / NW;           // X load instructions per wave per chunk
@@ -704,6 +706,10 @@ __global__ __launch_bounds__(64 * NW) void lmhead_ring_kernel(const uint16_t* __
   const int lane = threadIdx.x & 63;
   const int q = lane & 31, hh = lane >> 5;
   const int lr = lane >> 3, lc = lane & 7;
+  // the fused merge-and-unmask launch that follows counts its finished rows
+  // per sequence in `arrive`; this launch starts every count at zero
+  if (arrive != nullptr && vt == 0 && static_cast<int>(threadIdx.x) < n_arrive)
+    arrive[threadIdx.x] = 0;
 
   // load plan: W rows 32*wave + 8*j + lr, X rows 8*(wave + NW*p) + lr, chunk
   // lc of each 64-deep slice; LDS slot lc ^ ((row >> 1) & 7).  Rows past V
@@ -909,6 +915,75 @@ __global__ __launch_bounds__(256) void lmhead_merge_row_kernel(const float4* __r
   }
 }
 
+// The last two launches of a denoising step in one (for the register-ring
+// path, M = nseq * Lq <= 64): the merge of lmhead_merge_row_kernel for row
+// blockIdx.x, then, in the block that finishes a sequence's last row, the
+// unmasking step of that sequence (unmask_rule, as unmask_select applies
+// it).  Each block stores its row's confidence and argmax with agent-scope
+// atomic stores, which are coherent across the XCDs' L2 caches, waits for
+// them to complete, and only then counts the row in arrive[sequence]; the
+// block that sees the count reach Lq reads the sequence's rows back with
+// agent-scope atomic loads.  No fence is needed (an agent-scope release or
+// acquire writes back or invalidates a whole L2), and no block waits for
+// another.  Results are bitwise those of the two separate launches.
+__global__ __launch_bounds__(256) void lmhead_merge_unmask_kernel(
+    const float4* __restrict__ part, int n_vt, float* conf, int32_t* argmax, int Lq, float tau,
+    int steps_left, uint8_t* __restrict__ masked, int32_t* __restrict__ tokens,
+    int32_t* __restrict__ n_accepted, int32_t* __restrict__ arrive) {
+  __shared__ Stat wst[4];
+  __shared__ int s_last;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float4* pr = part + row * n_vt;
+  Stat st{-INFINITY, 0.f, INT_MAX};
+  for (int t0 = tid; t0 < n_vt; t0 += 4 * 256) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + 256 * u;
+      v[u] = t < n_vt ? pr[t] : make_float4(-INFINITY, 0.f, __int_as_float(INT_MAX), 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) merge(st, Stat{v[u].x, v[u].y, __float_as_int(v[u].z)});
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    Stat o;
+    o.m = shfl_xor_f(st.m, m);
+    o.s = shfl_xor_f(st.s, m);
+    o.a = shfl_xor_i(st.a, m);
+    Stat lo = (lane & m) ? o : st;
+    const Stat hi = (lane & m) ? st : o;
+    merge(lo, hi);
+    st = lo;
+  }
+  if (lane == 0) wst[wave] = st;
+  __syncthreads();
+  const int seq = static_cast<int>(row / Lq);
+  if (tid == 0) {
+    Stat r = wst[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) merge(r, wst[w]);
+    __hip_atomic_store(conf + row, 1.f / r.s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(argmax + row, r.a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // both stores are complete before the row is counted
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int before = __hip_atomic_fetch_add(arrive + seq, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    s_last = before == Lq - 1 ? 1 : 0;
+  }
+  __syncthreads();
+  if (s_last == 0 || wave != 0) return;
+  // every row of the sequence was stored before it was counted
+  const int64_t base = static_cast<int64_t>(seq) * Lq;
+  const int i = lane;
+  const int64_t at = base + (i < Lq ? i : Lq - 1);
+  const float c_ld = __hip_atomic_load(conf + at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int32_t a_ld = __hip_atomic_load(argmax + at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint8_t m_ld = masked[at];
+  unmask_rule(c_ld, m_ld, a_ld, i, Lq, tau, steps_left, base, masked, tokens, n_accepted + seq);
+}
+
 struct TileShape {
   int BV, BT;
 };
@@ -969,10 +1044,12 @@ hipError_t launch_lmhead(const void* X, int64_t M, int H, const void* W, int V, 
     const uint16_t* w16 = static_cast<const uint16_t*>(W);
     if (M <= 32)
       lmhead_ring_kernel<1, kRingWaves>
-          <<<dim3(n_vt), dim3(64 * kRingWaves), 0, st>>>(x16, M, H, w16, V, part, n_vt);
+          <<<dim3(n_vt), dim3(64 * kRingWaves), 0, st>>>(x16, M, H, w16, V, part, n_vt,
+                                                          nullptr, 0);
     else
       lmhead_ring_kernel<2, kRingWaves>
-          <<<dim3(n_vt), dim3(64 * kRingWaves), 0, st>>>(x16, M, H, w16, V, part, n_vt);
+          <<<dim3(n_vt), dim3(64 * kRingWaves), 0, st>>>(x16, M, H, w16, V, part, n_vt,
+                                                          nullptr, 0);
     e = hipGetLastError();
   } else if (stream_path(M, H, V, dtype)) {
     const dim3 grid(n_vt);
@@ -1012,6 +1089,44 @@ hipError_t launch_lmhead(const void* X, int64_t M, int H, const void* W, int V, 
   else
     lmhead_merge_kernel<<<dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0, st>>>(
         part, M, n_vt, conf, argmax, lse);
+  return hipGetLastError();
+}
+
+size_t lmhead_unmask_ws_bytes(int nseq, int Lq, int H, int V, int dtype) {
+  const int64_t M = static_cast<int64_t>(nseq) * Lq;
+  return lmhead_ws_bytes(M, H, V, dtype) + align_up(static_cast<size_t>(nseq) * 4, 256);
+}
+
+hipError_t launch_lmhead_unmask(const void* X, int nseq, int Lq, int H, const void* W, int V,
+                                int dtype, float* conf, int32_t* argmax, float tau,
+                                int steps_left, uint8_t* masked, int32_t* tokens,
+                                int32_t* n_accepted, void* ws, hipStream_t st) {
+  const int64_t M = static_cast<int64_t>(nseq) * Lq;
+  if (!ring_path(M, H, V, dtype)) {
+    // no fused form for this shape: the two calls, in order
+    const hipError_t e =
+        launch_lmhead(X, M, H, W, V, dtype, conf, argmax, nullptr, ws, st);
+    if (e != hipSuccess) return e;
+    return launch_unmask(conf, argmax, nseq, Lq, tau, steps_left, masked, tokens, n_accepted, st);
+  }
+  const int n_vt = (V + tile_bv(M, H, V, dtype) - 1) / tile_bv(M, H, V, dtype);
+  float4* part = static_cast<float4*>(ws);
+  int32_t* arrive =
+      reinterpret_cast<int32_t*>(static_cast<char*>(ws) + lmhead_ws_bytes(M, H, V, dtype));
+  const uint16_t* x16 = static_cast<const uint16_t*>(X);
+  const uint16_t* w16 = static_cast<const uint16_t*>(W);
+  if (M <= 32)
+    lmhead_ring_kernel<1, kRingWaves>
+        <<<dim3(n_vt), dim3(64 * kRingWaves), 0, st>>>(x16, M, H, w16, V, part, n_vt, arrive,
+                                                        nseq);
+  else
+    lmhead_ring_kernel<2, kRingWaves>
+        <<<dim3(n_vt), dim3(64 * kRingWaves), 0, st>>>(x16, M, H, w16, V, part, n_vt, arrive,
+                                                        nseq);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  lmhead_merge_unmask_kernel<<<dim3(static_cast<unsigned>(M)), dim3(256), 0, st>>>(
+      part, n_vt, conf, argmax, Lq, tau, steps_left, masked, tokens, n_accepted, arrive);
   return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace sprint {
@@ -96,6 +97,49 @@ constexpr int kCpolNT = 2;
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---------------------------------------------------------------- unmask rule
+// One unmasking step for one sequence, on one wave (lane i = block position,
+// Lq <= 64), from each lane's loaded confidence, mask byte and argmax (lanes
+// past Lq pass any value): accept every masked position whose confidence
+// exceeds tau, and at least q = min(m, ceil(m / steps_left)) of the m masked
+// ones (all of them when steps_left <= 0), ranked by (confidence descending,
+// position ascending).  Writes the accepted tokens and mask bytes and, from
+// lane 0, the number accepted.
+__device__ __forceinline__ void unmask_rule(float c_ld, uint8_t m_ld, int32_t a_ld, int i, int Lq,
+                                            float tau, int steps_left, int64_t base,
+                                            uint8_t* masked, int32_t* tokens,
+                                            int32_t* n_accepted_s) {
+  const bool valid = i < Lq;
+  const float c = valid ? c_ld : 0.f;
+  const bool msk = valid && m_ld != 0;
+  const uint64_t bal_m = __ballot(msk);
+  const uint64_t bal_hi = __ballot(msk && c > tau);
+  const int m = __popcll(bal_m);
+  const int n_hi = __popcll(bal_hi);
+  int q = m;
+  if (steps_left > 0) {
+    const int64_t ceil_q = (static_cast<int64_t>(m) + steps_left - 1) / steps_left;
+    q = ceil_q < m ? static_cast<int>(ceil_q) : m;
+  }
+  const int count = n_hi > q ? n_hi : q;
+  // rank = masked positions ahead in (confidence desc, position asc).  An
+  // unmasked lane (lanes past Lq included) broadcasts -inf, which is neither
+  // above nor equal to any finite confidence, so all 64 lanes are visited
+  // without a branch.
+  const float ck = msk ? c : -INFINITY;
+  int rank = 0;
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    const float cj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ck), j));
+    rank += (cj > c || (cj == c && j < i)) ? 1 : 0;
+  }
+  if (msk && rank < count) {
+    tokens[base + i] = a_ld;
+    masked[base + i] = 0;
+  }
+  if (i == 0) *n_accepted_s = count;
+}
 
 // ---------------------------------------------------------------- sequence chunks
 // Work is split into chunks of `chunk` positions that never cross a sequence

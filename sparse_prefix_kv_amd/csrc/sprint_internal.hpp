@@ -52,6 +52,14 @@ hipError_t launch_attend(const void* Q, int nseq, int Lq, int Hq, const void* Kp
 
 // ---- LM-head confidence (fused GEMM + streaming max / log-sum-exp, then merge)
 size_t lmhead_ws_bytes(int64_t M, int H, int V, int dtype);
+// The LM head of a denoising step fused with its unmasking step (M = nseq*Lq
+// <= 64 on the register-ring path; other shapes run the two launches in
+// turn).  Workspace: lmhead_ws_bytes(M, ...) then nseq arrival counters.
+size_t lmhead_unmask_ws_bytes(int nseq, int Lq, int H, int V, int dtype);
+hipError_t launch_lmhead_unmask(const void* X, int nseq, int Lq, int H, const void* W, int V,
+                                int dtype, float* conf, int32_t* argmax, float tau,
+                                int steps_left, uint8_t* masked, int32_t* tokens,
+                                int32_t* n_accepted, void* ws, hipStream_t st);
 hipError_t launch_lmhead(const void* X, int64_t M, int H, const void* W, int V, int dtype,
                          float* conf, int32_t* argmax, float* lse, void* ws, hipStream_t st);
 

@@ -6,7 +6,8 @@
 // One wave per sequence, one lane per block position (Lq <= 64).  The rank of
 // a masked position is the number of masked positions ahead of it in that
 // order, computed by broadcasting every lane's confidence in turn (readlane:
-// a scalar broadcast, no LDS round trip).
+// a scalar broadcast, no LDS round trip); unmask_rule holds the rule, which
+// the LM head's fused merge-and-unmask kernel applies too.
 #include "sprint_device.hpp"
 #include "sprint_internal.hpp"
 
@@ -29,34 +30,7 @@ __global__ __launch_bounds__(64) void unmask_kernel(const float* __restrict__ co
   const float c_ld = conf[at];
   const uint8_t m_ld = masked[at];
   const int32_t a_ld = argmax[at];
-  const float c = valid ? c_ld : 0.f;
-  const bool msk = valid && m_ld != 0;
-  const uint64_t bal_m = __ballot(msk);
-  const uint64_t bal_hi = __ballot(msk && c > tau);
-  const int m = __popcll(bal_m);
-  const int n_hi = __popcll(bal_hi);
-  int q = m;
-  if (steps_left > 0) {
-    const int64_t ceil_q = (static_cast<int64_t>(m) + steps_left - 1) / steps_left;
-    q = ceil_q < m ? static_cast<int>(ceil_q) : m;
-  }
-  const int count = n_hi > q ? n_hi : q;
-  // rank = masked positions ahead in (confidence desc, position asc).  An
-  // unmasked lane (lanes past Lq included) broadcasts -inf, which is neither
-  // above nor equal to any finite confidence, so all 64 lanes are visited
-  // without a branch.
-  const float ck = msk ? c : -INFINITY;
-  int rank = 0;
-#pragma unroll
-  for (int j = 0; j < 64; ++j) {
-    const float cj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ck), j));
-    rank += (cj > c || (cj == c && j < i)) ? 1 : 0;
-  }
-  if (msk && rank < count) {
-    tokens[base + i] = a_ld;
-    masked[base + i] = 0;
-  }
-  if (i == 0) n_accepted[s] = count;
+  unmask_rule(c_ld, m_ld, a_ld, i, Lq, tau, steps_left, base, masked, tokens, n_accepted + s);
 }
 
 }  // namespace

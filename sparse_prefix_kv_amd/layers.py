@@ -94,7 +94,8 @@ class SprintLayers:
         def ws(n):
             return torch.empty(max(int(n), 256), dtype=u8, device=dev)
         self.ws_lm_prefix = ws(sprint.lmhead_confidence_ws(tl, wl.H, wl.vocab, dti))
-        self.ws_lm_blk = ws(sprint.lmhead_confidence_ws(M, wl.H, wl.vocab, dti))
+        self.ws_lm_blk = ws(sprint.lmhead_confidence_unmask_ws(self.nseq, self.Lq, wl.H, wl.vocab,
+                                                               dti))
         self.ws_score = ws(sprint.sprint_score_layers_ws(tl, self.nseq, n_layers))
         self.ws_prune = ws(sprint.sprint_prune_kv_ws(tl, self.nseq) if mode == "shared" else
                            sprint.sprint_prune_kv_per_layer_ws(tl, self.nseq, n_layers))
@@ -141,12 +142,13 @@ class SprintLayers:
                                     self.Kb[l], self.Vb[l], O=self.O[l], ws=self.ws_att_full)
 
     def confidence_and_unmask(self, t: int):
+        """The last layer's LM-head confidences and one unmasking step, in one
+        call (bitwise lmhead_confidence followed by unmask_select)."""
         M = self.nseq * self.Lq
-        sprint.lmhead_confidence(self.O[-1].view(M, self.Hq * self.D), self.W,
-                                 conf=self.conf_blk, argmax=self.argmax_blk, ws=self.ws_lm_blk)
-        sprint.unmask_select(self.conf_blk.view(self.nseq, self.Lq),
-                             self.argmax_blk.view(self.nseq, self.Lq), self.masked, self.tokens,
-                             self.tau, self.steps_left(t), n_accepted=self.n_acc)
+        sprint.lmhead_confidence_unmask(self.O[-1].view(M, self.Hq * self.D), self.W,
+                                        self.masked, self.tokens, self.tau, self.steps_left(t),
+                                        conf=self.conf_blk, argmax=self.argmax_blk,
+                                        n_accepted=self.n_acc, ws=self.ws_lm_blk)
 
     # ------------------------------------------------------------------ block
     def pruning_pass(self, prefix_conf: bool = True):

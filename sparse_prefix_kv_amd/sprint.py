@@ -36,6 +36,11 @@ _SIGS = {
     "lmhead_confidence_ws": (_size, [_i64, _i32, _i32, _i32]),
     "lmhead_confidence": (ctypes.c_int, [_c_void_p, _i64, _i32, _c_void_p, _i32, _i32, _c_void_p,
                                          _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
+    "lmhead_confidence_unmask_ws": (_size, [_i32, _i32, _i32, _i32, _i32]),
+    "lmhead_confidence_unmask": (ctypes.c_int, [_c_void_p, _i32, _i32, _i32, _c_void_p, _i32,
+                                                _i32, _c_void_p, _c_void_p, _f32, _i32,
+                                                _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                _size, _c_void_p]),
     "sprint_score_ws": (_size, [_i64, _i32]),
     "sprint_score": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _i32,
                                     _f32, _c_void_p, _c_void_p, _c_void_p, _size, _c_void_p]),
@@ -365,6 +370,39 @@ def unmask_select(conf, argmax, masked, tokens, tau: float, steps_left: int, n_a
         _ptr(conf), _ptr(argmax), nseq, Lq, float(tau), int(steps_left), _ptr(masked),
         _ptr(tokens), _ptr(n_accepted), _stream(stream)))
     return n_accepted
+
+
+def lmhead_confidence_unmask_ws(nseq, Lq, H, V, dtype) -> int:
+    return int(lib().lmhead_confidence_unmask_ws(nseq, Lq, H, V, dtype))
+
+
+def lmhead_confidence_unmask(hidden, W, masked, tokens, tau: float, steps_left: int, conf=None,
+                             argmax=None, n_accepted=None, ws=None, stream=None):
+    """The block's LM-head confidences, then one unmasking step, in one call.
+    hidden [nseq*Lq, H]; masked, tokens [nseq, Lq] (updated in place)."""
+    nseq, Lq = masked.shape
+    M, H = hidden.shape
+    V = W.shape[0]
+    dt = _dt(hidden)
+    _arg(hidden, "hidden", shape=(nseq * Lq, H))
+    _arg(W, "W", hidden.dtype, shape=(V, H))
+    _arg(masked, "masked", torch.uint8, shape=(nseq, Lq))
+    _arg(tokens, "tokens", torch.int32, shape=(nseq, Lq))
+    dev = hidden.device
+    f32, i32 = torch.float32, torch.int32
+    conf = torch.empty(M, dtype=f32, device=dev) if conf is None else _arg(conf, "conf", f32, M)
+    argmax = (torch.empty(M, dtype=i32, device=dev) if argmax is None
+              else _arg(argmax, "argmax", i32, M))
+    n_accepted = (torch.empty(nseq, dtype=i32, device=dev) if n_accepted is None
+                  else _arg(n_accepted, "n_accepted", i32, nseq))
+    _gpu(hidden=hidden, W=W, masked=masked, tokens=tokens, conf=conf, argmax=argmax,
+         n_accepted=n_accepted)
+    ws = _ws(lambda: lmhead_confidence_unmask_ws(nseq, Lq, H, V, dt), dev, ws)
+    _check("lmhead_confidence_unmask", lib().lmhead_confidence_unmask(
+        _ptr(hidden), nseq, Lq, H, _ptr(W), V, dt, _ptr(conf), _ptr(argmax), float(tau),
+        int(steps_left), _ptr(masked), _ptr(tokens), _ptr(n_accepted), _ptr(ws), ws.numel(),
+        _stream(stream)))
+    return conf, argmax, n_accepted
 
 
 def sprint_append_rows(old, cu_old, blk, out=None, cu_out=None, stream=None):

@@ -417,6 +417,12 @@ FUZZ_SPECS = {
         _int(2048, (0, -1, 100, 65600, I32_MAX), (64, 65536)), _p16(),
         _int(32768, (0, -1, I32_MIN, 2**30, I32_MAX), (1, 3000)), _dt(), _p4(), _p4(), _o4(),
         _p16(), _wsb(), (STREAM, None)],
+    "lmhead_confidence_unmask": [
+        _p16(), _int(1, NSEQ_BAD, (2, 64)), _int(32, (0, -1, 65, I32_MAX), (1, 64)),
+        _int(2048, (0, -1, 100, 65600, I32_MAX), (64, 65536)), _p16(),
+        _int(32768, (0, -1, I32_MIN, 2**30, I32_MAX), (1, 3000)), _dt(), _p4(), _p4(),
+        (("tau", (NAN,), (INF, -INF, 2.0, -1.0)), 0.95), _int(9, (), (0, -1, I32_MIN, I32_MAX)),
+        _pb(), _p4(), _p4(), _p16(), _wsb(), (STREAM, None)],
     "sprint_score": _score_spec(),
     "sprint_score_layers": _score_spec(4),
     "sprint_score_per_layer": _score_spec(16),

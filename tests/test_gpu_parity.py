@@ -246,6 +246,18 @@ def test_score_zero_keys():
     assert np.all(_np(ib)[:10] == 1.0)
 
 
+def test_score_long_sequences():
+    """Sequences of more than 512 chunks of 64 positions: each lane of the
+    score kernel reads several rounds of eight chunk sums and then a ragged
+    remainder (70001 positions = 1094 chunks, 33000 = 516)."""
+    lens = [70001, 17, 33000]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    K = synth.bf16_round(synth.lognormal_rows(
+        synth.normal_array((cu[-1], 4, 128), 47, 1.0, "f32"), 48))
+    conf = synth.random_scores(cu[-1], 49) / 2
+    _check_score(K, conf, cu, "bf16", 4, 128)
+
+
 @pytest.mark.parametrize("name", ["interleaved32k", "ragged8"])
 def test_score_full_size(name):
     x = synth.make_inputs(synth.WORKLOADS[name], 0, with_lmhead=False)
