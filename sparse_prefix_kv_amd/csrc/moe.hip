@@ -119,9 +119,37 @@ __global__ __launch_bounds__(kMoeThreads) void moe_router_kernel(
 // ---------------------------------------------------------------- 2. select
 // One wave per token; lane l holds experts l, l + 64, ... (NE of them).  Each
 // of the top_k rounds takes the lane's best, then a wave arg-max (ties to the
-// lowest expert); lane j keeps the affinity of the j-th choice.
+// lowest expert); lane j keeps the affinity of the j-th choice.  The arg-max
+// runs on one 64-bit key per lane, (order-preserving bits of the selection
+// score, ~expert), through DPP lane moves: a prefix max within each row of
+// 16 lanes, then the row broadcasts, so lane 63 holds the winner.  No LDS
+// permutes, whose latency the eight rounds would otherwise queue one after
+// another.
 constexpr int kMaxSlots = 8192;             // M * top_k
 constexpr int kMaxTokens = 1024;            // an expert's slot list (LDS)
+
+__device__ __forceinline__ uint32_t order_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : u | 0x80000000u;
+}
+
+// key of lane := max(key, key of the lane the DPP control moves in); lanes
+// with no source keep their own key (old = the lane's own value)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_max64(uint32_t& hi, uint32_t& lo) {
+  const uint32_t oh = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(hi), static_cast<int>(hi), CTRL, ROW_MASK, 0xF,
+                                  false));
+  const uint32_t ol = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(lo), static_cast<int>(lo), CTRL, ROW_MASK, 0xF,
+                                  false));
+  const uint64_t mine = (static_cast<uint64_t>(hi) << 32) | lo;
+  const uint64_t other = (static_cast<uint64_t>(oh) << 32) | ol;
+  if (other > mine) {
+    hi = oh;
+    lo = ol;
+  }
+}
 
 template <int NE>
 __global__ __launch_bounds__(kMoeThreads) void moe_select_kernel(
@@ -142,30 +170,30 @@ __global__ __launch_bounds__(kMoeThreads) void moe_select_kernel(
   float my_aff = 0.f, ssum = 0.f;
   for (int j = 0; j < top_k; ++j) {
     float bv = -INFINITY;
-    int be = INT_MAX;
+    int be = lane;
 #pragma unroll
     for (int i = 0; i < NE; ++i)
       if (sel[i] > bv) {       // ascending i: the first maximum is the lowest expert
         bv = sel[i];
         be = lane + 64 * i;
       }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = shfl_xor_f(bv, m);
-      const int oe = shfl_xor_i(be, m);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    uint32_t hi = order_bits(bv), lo = ~static_cast<uint32_t>(be);
+    dpp_max64<0x111, 0xF>(hi, lo);   // row_shr:1
+    dpp_max64<0x112, 0xF>(hi, lo);   // row_shr:2
+    dpp_max64<0x114, 0xF>(hi, lo);   // row_shr:4
+    dpp_max64<0x118, 0xF>(hi, lo);   // row_shr:8: lane 15 of each row holds its row's max
+    dpp_max64<0x142, 0xA>(hi, lo);   // row_bcast:15 into rows 1 and 3
+    dpp_max64<0x143, 0xC>(hi, lo);   // row_bcast:31 into rows 2 and 3: lane 63 holds the max
+    be = static_cast<int>(~static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), 63)));
+    const int slot = be >> 6, owner = be & 63;
     float a = 0.f;
 #pragma unroll
     for (int i = 0; i < NE; ++i)
-      if (lane + 64 * i == be) {
+      if (i == slot) {
         a = aff[i];
-        sel[i] = -INFINITY;
+        if (lane == owner) sel[i] = -INFINITY;
       }
-    a = __shfl(a, be & 63, 64);
+    a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), owner));
     if (lane == j) my_aff = a;
     ssum += a;
     if (lane == 0) ids[static_cast<int64_t>(t) * top_k + j] = be;
