@@ -163,6 +163,37 @@ int main(int argc, char** argv) {
   for (int i = 0; i < M; ++i) still += hmask[i];
   check(hacc == 4 && still == M - 4, "unmask accepts ceil(32 / 9) = 4 positions");
 
+  // ---------------------------------------------------------------- both, in one call
+  void* dws3;
+  const size_t ws_f = lmhead_confidence_unmask_ws(1, M, H, V, SPRINT_BF16);
+  HIP_OK(hipMalloc(&dws3, ws_f));
+  HIP_OK(hipMemset(dws3, 0x5a, ws_f));   // the call sets what it needs
+  HIP_OK(hipMemset(dmask, 1, M));
+  HIP_OK(hipMemset(dtok, 0xff, M * 4));
+  HIP_OK(hipMemset(dconf, 0, M * 4));
+  SPRINT_OK_(lmhead_confidence_unmask(dx, 1, M, H, dw, V, SPRINT_BF16, dconf, darg, 0.95f, 9, dmask,
+                                      dtok, dacc, dws3, ws_f, NULL));
+  HIP_OK(hipDeviceSynchronize());
+  int32_t htok[M];
+  HIP_OK(hipMemcpy(hconf, dconf, sizeof(hconf), hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(hmask, dmask, M, hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(htok, dtok, sizeof(htok), hipMemcpyDeviceToHost));
+  HIP_OK(hipMemcpy(&hacc, dacc, 4, hipMemcpyDeviceToHost));
+  bool f_ok = hacc == 4;
+  int accepted = 0;
+  for (int i = 0; i < M; ++i) {
+    f_ok = f_ok && fabsf(hconf[i] - 1.f / V) <= 1e-6f;
+    if (hmask[i] == 0) {
+      ++accepted;
+      f_ok = f_ok && htok[i] == 0;
+    } else {
+      f_ok = f_ok && htok[i] == -1;
+    }
+  }
+  check(f_ok && accepted == 4,
+        "LM head and unmask in one call: confidence 1/V, 4 positions take token 0");
+  HIP_OK(hipFree(dws3));
+
   // ---------------------------------------------------------------- errors
   check(block_attend(dq, nseq, Lq, Hq, dk, dv, dcu, L, L, dkb, dvb, 3, D, 0.1f, SPRINT_BF16, dO,
                      dws, ws_a, NULL) == SPRINT_EINVAL,
