@@ -237,7 +237,7 @@ def cpu_baseline(x, wl, n_steps):
                 "prefix_lm_extrapolated": round(t_prefix_lm, 2), "block": round(block, 2)}}
 
 
-def profile_call(args, blk, n_steps, torch):
+def profile_call(args, blk, wl, n_steps, torch):
     """Launch one call (or a calibration copy) a few times and exit: a short
     program for rocprofv3 counter passes."""
     if args.profile_call == "copy":
@@ -253,6 +253,8 @@ def profile_call(args, blk, n_steps, torch):
                "unmask": lambda: blk.unmask(1),
                "lmhead_unmask": lambda: blk.confidence_and_unmask(1)}
         blk.run_block(n_steps)
+        if args.profile_call == "moe":
+            fns["moe"] = moe_call(args, blk, wl, torch)[0]
         fn = fns[args.profile_call]
         what = args.profile_call
     torch.cuda.synchronize()
@@ -470,12 +472,11 @@ def measure_layers(args, x, n_steps, torch, reps=5):
     return out
 
 
-def measure_moe(args, blk, x_in, wl, n_steps, torch, reps=20):
-    """The MoE FFN on the block's attention outputs (M = 32 tokens), with
+def moe_call(args, blk, wl, torch):
+    """One MoE FFN call on the block's attention outputs (M = 32 tokens), with
     synthetic weights drawn on the GPU (the laws of synth.make_moe_weights,
-    bf16): 20 back-to-back calls captured in a graph, HIP events around the
-    replay.  Algorithmic bytes: every chosen expert's three matrices once,
-    the router, and x, the residual and y."""
+    bf16).  Returns the call, the expert ids it writes, (E, K, I, H, M) and
+    the weights (router, bias, gate, up, down)."""
     from sparse_prefix_kv_amd import sprint as sp
     E, K, I, H = args.moe_experts, 8, 512, wl.H
     g = torch.Generator(device="cuda").manual_seed(0)
@@ -502,6 +503,14 @@ def measure_moe(args, blk, x_in, wl, n_steps, torch, reps=20):
     def call():
         sp.moe_ffn(x, wr, bias, wg, wu, wd, K, residual=x, y=y, expert_ids=ids, gates=gates,
                    ws=ws)
+    return call, ids, (E, K, I, H, M), (wr, bias, wg, wu, wd)
+
+
+def measure_moe(args, blk, x_in, wl, n_steps, torch, reps=20):
+    """The MoE FFN (moe_call): 20 back-to-back calls captured in a graph, HIP
+    events around the replay.  Algorithmic bytes: every chosen expert's three
+    matrices once, the router, and x, the residual and y."""
+    call, ids, (E, K, I, H, M), (wr, bias, wg, wu, wd) = moe_call(args, blk, wl, torch)
     call()
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
@@ -730,7 +739,7 @@ def main():
         f"{blk.total_kept} of {lay.total_L} prefix positions")
 
     if args.profile_call:
-        profile_call(args, blk, n_steps, torch)
+        profile_call(args, blk, wl, n_steps, torch)
         return
 
     # ---------------------------------------------------------------- warmup
